@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Throughput of one verify step on one MI355X.
+
+A step is one spec_verify_run over one batch: RoPE + tree-masked GQA
+attention + W_o + final norm + full-vocabulary LM head + vocab reductions +
+overlaps + acceptance, metadata upload included.  Default workload: 32
+concurrent chains at 27B shape (24/4 heads, d 256, hidden 5120, vocab
+248,320), gamma 7 -> 256 verify rows, ragged bf16 KV prefixes
+U{1024..16384}; synthetic seeded inputs, resident in HBM before timing.
+
+Prints one JSON line (stdout).  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verify rows/s (attn+LM-head+accept) γ=7, 27B shape; step ms; % of roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
+COUNTERS = os.path.join(ROOT, "profiles", "lm_head_counters.json")
+GEMM_SRC = os.path.join(ROOT, "draft_block_verification_verify_amd", "csrc", "k_gemm.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counters_traffic(workload: str):
+    """HBM bytes per LM-head launch from committed rocprofv3 counter runs,
+    if they were taken on this workload with the current kernel source."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = c.get(workload)
+    if not rec or rec.get("source_sha") != kernel_source_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, tree: int = 0) -> dict:
+    """The fp64 oracle, as it stands, on one sequence of the workload."""
+    from oracle import verify_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    rng = np.random.default_rng(99)
+    d = O.inp_dict(inp)
+    d = dict(d)
+    d["draft_ids"] = rng.integers(0, inp.cfg.vocab, inp.st.n_rows).astype(np.int32)
+    t0 = time.perf_counter()
+    O.verify(O.cfg_dict(inp.cfg), d, trees=[tree])
+    dt = time.perf_counter() - t0
+    roots = np.nonzero(inp.st.parent < 0)[0].tolist() + [inp.st.n_rows]
+    rows = int(roots[tree + 1] - roots[tree])
+    L = int(inp.st.root_kv_len[tree])
+    return {"value": rows / dt, "unit": "rows/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"tree {tree} of {inp.st.n_roots} ({rows} rows, {L}-token prefix, full vocabulary); "
+                      f"{dt:.1f} s"}
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 3) -> None:
+    """A plain device copy of known size, for scaling HBM counters."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5],
+                    help="1 chain-tiny, 2 chain-8b, 3 block-27b-b16, 4 tree-specopd, 5 conc32-27b (default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the verify step is not "
+              "sharded across GPUs in this build", file=sys.stderr)
+        return 2
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+
+    from draft_block_verification_verify_amd import accounting as A
+    from draft_block_verification_verify_amd import binding as B
+    from draft_block_verification_verify_amd import workloads as W
+    from draft_block_verification_verify_amd.runner import DeviceCase
+
+    B.lib()                                   # fails loudly without the HIP library
+    cfg = W.CONFIGS[args.workload]
+    log(f"[bench] generating {cfg.name} seed {args.seed}")
+    t0 = time.perf_counter()
+    inp = W.make_inputs(cfg, args.seed)
+    st = inp.st
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s: rows {st.n_rows}, trees {st.n_roots}, "
+        f"kv tokens {st.kv_tokens}")
+    dc = DeviceCase(inp, with_logits=False)
+    torch.cuda.synchronize()
+
+    # draft ids: trees use draws from the drafter; chains get a planted
+    # accepted prefix k ~ U{0..gamma} on the target's greedy tokens (taken from
+    # a first run of this same step)
+    planted = None
+    if cfg.kind == "tree":
+        W.sample_tree_drafts(inp)
+    else:
+        dc.run()
+        g = dc.results()["argmax"]
+        planted = W.plant_chain_drafts(inp, g)
+    dc.refresh()
+
+    log(f"[bench] warmup {args.warmup}")
+    B.spec_verify_profile(dc.ver.h, True)
+    for _ in range(args.warmup):
+        dc.run()
+    torch.cuda.synchronize()
+    # timed region: K steps, per-stage HIP events recorded on the run's stream
+    B.spec_verify_profile(dc.ver.h, True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dc.run()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stages = dict(B.spec_verify_stage_times(dc.ver.h))
+    B.spec_verify_profile(dc.ver.h, False)
+    ms = (t1 - t0) * 1e3 / args.steps
+    # same loop without the stage events, for the event overhead
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        dc.run()
+    torch.cuda.synchronize()
+    ms_plain = (time.perf_counter() - t2) * 1e3 / args.steps
+    out = dc.results()
+    if planted is not None:
+        ok = bool((out["accept_len"] == planted + 1).all())
+    else:
+        ok = None
+
+    n = st.n_rows
+    sb, sf = A.step_bytes(cfg, st), A.step_flops(cfg, st)
+    lm_ms = stages.get("lm_head", float("nan"))
+    lm_bytes = sb["lm_head"]
+    lm_flops = sf["lm_head"]
+    ai = lm_flops / lm_bytes
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai < ridge:
+        achieved = lm_bytes / (lm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    else:
+        achieved = lm_flops / (lm_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / BF16_PEAK_TFLOPS}
+    roof["traffic"] = counters_traffic(cfg.name)
+    roof["kernel"] = "lm_head"
+    roof["kernel_ms"] = lm_ms
+    roof["algorithmic_bytes"] = lm_bytes
+    roof["algorithmic_flops"] = lm_flops
+    roof["mfma_frac"] = lm_flops / (lm_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
+
+    step_s = ms * 1e-3
+    res = {
+        "metric": METRIC,
+        "value": n / step_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; random-init weights of the stated shapes)",
+        "config": {"workload": cfg.name, "rows": n, "trees": st.n_roots, "kv_tokens": int(st.kv_tokens),
+                   "heads_q_kv": [cfg.n_q_heads, cfg.n_kv_heads], "head_dim": cfg.head_dim,
+                   "hidden": cfg.hidden, "vocab": cfg.vocab, "gamma": cfg.gamma, "seed": args.seed},
+        "roofline": roof,
+        "step": {"algorithmic_bytes": sb["total"], "algorithmic_flops": sf["total"],
+                 "device_ms": stages.get("step"), "ms_per_step_without_stage_events": ms_plain,
+                 "hbm_frac_of_step": sb["total"] / step_s / 1e9 / HBM_PEAK_GBS,
+                 "stages_ms": {k: v for k, v in stages.items() if k != "step"},
+                 "planted_accept_ok": ok,
+                 "accept_len_mean": float(out["accept_len"].mean())},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle on one sequence)")
+        res["cpu_baseline"] = cpu_baseline(inp)
+    else:
+        res["cpu_baseline"] = None
+    dc.close()
+    print(json.dumps(res))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

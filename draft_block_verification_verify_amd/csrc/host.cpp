@@ -1,0 +1,558 @@
+// C ABI of the verify step (include/spec_verify.h): handle lifetime, scratch,
+// metadata upload and the launch sequence of one run.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "launch.hpp"
+#include "plan.hpp"
+#include "spec_verify.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+sv_status fail(sv_status st, std::string msg) {
+  g_err = std::move(msg);
+  return st;
+}
+
+constexpr int kRing = 4;          // pinned metadata staging slots
+constexpr int kDChunk = 8192;     // vocabulary chunk of the drafter-stats pass
+constexpr int kOChunk = 8192;     // vocabulary chunk of the overlap pass
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Stage {
+  const char *name;
+  hipEvent_t a, b;
+};
+
+}  // namespace
+
+struct sv_handle {
+  sv_config cfg{};
+  sv::Dims dm{};
+  const void *w_o = nullptr, *w_lm = nullptr;
+  int device = 0, n_cu = 256, target_items = 1024;
+  int elt = 2;
+  // metadata
+  char *d_meta = nullptr;
+  size_t meta_cap = 0;
+  char *h_meta[kRing] = {};
+  hipEvent_t meta_ev[kRing] = {};
+  bool meta_used[kRing] = {};
+  int ring = 0;
+  // scratch
+  void *q_rot = nullptr, *k_rot = nullptr, *o_act = nullptr, *hn = nullptr;
+  float *part_o = nullptr, *part_ml = nullptr, *h_part = nullptr, *logits = nullptr;
+  float *t_max = nullptr, *t_sum = nullptr, *lse_q = nullptr, *opart = nullptr;
+  int32_t *t_arg = nullptr;
+  float2 *dpart = nullptr;
+  int64_t slot_cap = 0;
+  int wo_split_max = 1;
+  int n_tiles_cap = 0, n_dch = 0, n_och = 0;
+  size_t h_part_floats = 0;
+  std::vector<void *> allocs;
+  // completion / profiling
+  hipEvent_t done = nullptr;
+  bool ran = false;
+  bool profile = false;
+  std::vector<Stage> stages;      // every recorded stage of every recorded run
+};
+
+namespace {
+
+sv_status hip_fail(const char *what, hipError_t e) {
+  return fail(SV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+template <class T>
+sv_status dev_alloc(sv_handle *h, T **p, size_t bytes) {
+  void *q = nullptr;
+  if (bytes == 0) bytes = 16;
+  const hipError_t e = hipMalloc(&q, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(SV_ERR_OOM, "hipMalloc of " + std::to_string(bytes) + " bytes failed: " + hipGetErrorString(e));
+  }
+  h->allocs.push_back(q);
+  *p = static_cast<T *>(q);
+  return SV_OK;
+}
+
+void release(sv_handle *h) {
+  for (void *p : h->allocs) (void)hipFree(p);
+  h->allocs.clear();
+  for (int i = 0; i < kRing; ++i) {
+    if (h->h_meta[i]) (void)hipHostFree(h->h_meta[i]);
+    if (h->meta_ev[i]) (void)hipEventDestroy(h->meta_ev[i]);
+  }
+  if (h->done) (void)hipEventDestroy(h->done);
+  for (auto &s : h->stages) {
+    (void)hipEventDestroy(s.a);
+    (void)hipEventDestroy(s.b);
+  }
+  h->stages.clear();
+  delete h;
+}
+
+// Split-K factor of W_o for the skinny launch: enough workgroups to cover the
+// chip twice, K pieces of at least 256.
+int wo_splits(const sv_handle *h, int rows, int *k_split) {
+  const int K = h->dm.Hq * h->dm.d;
+  if (rows > 64) {
+    *k_split = K;
+    return 1;
+  }
+  const int n_tiles = int(ceil_div(h->dm.hidden, 128));
+  int s = int(ceil_div(2 * h->n_cu, n_tiles));
+  s = std::max(1, std::min(s, K / 256));
+  int ks = int(ceil_div(ceil_div(K, s), 64) * 64);
+  s = int(ceil_div(K, ks));
+  *k_split = ks;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *spec_verify_last_error(void) { return g_err.c_str(); }
+
+sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *w_lm, sv_handle **out) {
+  g_err.clear();
+  if (!cfg || !out) return fail(SV_ERR_INVALID_ARG, "cfg and out must be non-null");
+  *out = nullptr;
+  if (!w_o || !w_lm) return fail(SV_ERR_INVALID_ARG, "w_o and w_lm must be non-null device pointers");
+  sv::Dims dm{cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, cfg->hidden, cfg->vocab, cfg->dtype,
+              cfg->max_rows,  cfg->max_roots,  cfg->max_tree_rows, cfg->max_pos};
+  std::string err;
+  const int pc = sv::check_dims(dm, &err);
+  if (pc != sv::P_OK) return fail(sv_status(pc), err);
+  if (!(cfg->rope_base > 1.0f) || !std::isfinite(cfg->rope_base))
+    return fail(SV_ERR_INVALID_ARG, "rope_base must be a finite value > 1");
+  if (!(cfg->norm_eps >= 0.0f) || !std::isfinite(cfg->norm_eps))
+    return fail(SV_ERR_INVALID_ARG, "norm_eps must be finite and >= 0");
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail("hipGetDeviceProperties", e);
+  if (std::strstr(prop.gcnArchName, "gfx950") == nullptr)
+    return fail(SV_ERR_UNSUPPORTED, std::string("device ") + std::to_string(dev) + " is " + prop.gcnArchName +
+                                        "; this library is built for gfx950 (MI355X) only");
+
+  sv_handle *h = new sv_handle();
+  h->cfg = *cfg;
+  h->dm = dm;
+  h->w_o = w_o;
+  h->w_lm = w_lm;
+  h->device = dev;
+  h->n_cu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+  h->target_items = 4 * h->n_cu;
+  h->elt = dm.dtype == SV_BF16 ? 2 : 4;
+
+  const int64_t R = dm.max_rows, Hq = dm.Hq, Hkv = dm.Hkv, D = dm.d, H = dm.hidden, V = dm.vocab;
+  const int64_t E = h->elt;
+  h->slot_cap = sv::slot_capacity(dm);
+  int ks = 0;
+  h->wo_split_max = wo_splits(h, int(std::min<int64_t>(R, 64)), &ks);
+  h->h_part_floats = size_t(std::max<int64_t>(int64_t(h->wo_split_max) * std::min<int64_t>(R, 64), R)) * H;
+  h->n_tiles_cap = int(ceil_div(V, 128));
+  h->n_dch = int(ceil_div(V, kDChunk));
+  h->n_och = int(ceil_div(V, kOChunk));
+  h->meta_cap = sv::meta_capacity(dm, h->target_items);
+
+  sv_status st = SV_OK;
+  auto A = [&](auto **p, size_t bytes) {
+    if (st == SV_OK) st = dev_alloc(h, p, bytes);
+  };
+  A(&h->d_meta, h->meta_cap);
+  A(&h->q_rot, size_t(R * Hq * D * 4));       // bf16: hi + lo planes; fp32: one plane
+  A(&h->k_rot, size_t(R * Hkv * D * E));
+  if (dm.dtype == SV_BF16) {
+    A(&h->part_o, size_t(h->slot_cap * D * 4));
+    A(&h->part_ml, size_t(h->slot_cap * 2 * 4));
+  }
+  A(&h->o_act, size_t(R * Hq * D * 4));       // bf16 hi + lo planes, fp16, or fp32
+  A(&h->h_part, h->h_part_floats * 4);
+  A(&h->hn, size_t(R * H * 4));
+  A(&h->logits, size_t(R * V * 4));
+  A(&h->t_max, size_t(R * h->n_tiles_cap * 4));
+  A(&h->t_sum, size_t(R * h->n_tiles_cap * 4));
+  A(&h->t_arg, size_t(R * h->n_tiles_cap * 4));
+  A(&h->dpart, size_t(R * h->n_dch * 8));
+  A(&h->lse_q, size_t(R * 4));
+  A(&h->opart, size_t(R * h->n_och * 4));
+  if (st != SV_OK) {
+    release(h);
+    return st;
+  }
+  for (int i = 0; i < kRing; ++i) {
+    e = hipHostMalloc(reinterpret_cast<void **>(&h->h_meta[i]), h->meta_cap, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      release(h);
+      return fail(SV_ERR_OOM, std::string("hipHostMalloc: ") + hipGetErrorString(e));
+    }
+    e = hipEventCreateWithFlags(&h->meta_ev[i], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      release(h);
+      return hip_fail("hipEventCreate", e);
+    }
+  }
+  e = hipEventCreateWithFlags(&h->done, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    release(h);
+    return hip_fail("hipEventCreate", e);
+  }
+  *out = h;
+  return SV_OK;
+}
+
+sv_status spec_verify_destroy(sv_handle *h) {
+  g_err.clear();
+  if (!h) return SV_OK;
+  sv_status st = SV_OK;
+  if (h->ran) {
+    const hipError_t e = hipEventSynchronize(h->done);
+    if (e != hipSuccess) st = hip_fail("hipEventSynchronize", e);
+  }
+  release(h);
+  return st;
+}
+
+static void drop_stages(sv_handle *h) {
+  for (auto &s : h->stages) {
+    (void)hipEventDestroy(s.a);
+    (void)hipEventDestroy(s.b);
+  }
+  h->stages.clear();
+}
+
+sv_status spec_verify_profile(sv_handle *h, int32_t on) {
+  g_err.clear();
+  if (!h) return fail(SV_ERR_INVALID_ARG, "null handle");
+  if (h->ran) {
+    const hipError_t e = hipEventSynchronize(h->done);
+    if (e != hipSuccess) return hip_fail("hipEventSynchronize", e);
+  }
+  drop_stages(h);
+  h->profile = on != 0;
+  return SV_OK;
+}
+
+int32_t spec_verify_stage_times(sv_handle *h, const char **names, float *ms, int32_t cap) {
+  g_err.clear();
+  if (!h) return fail(SV_ERR_INVALID_ARG, "null handle");
+  if (h->stages.empty()) return 0;
+  hipError_t e = hipEventSynchronize(h->stages.back().b);
+  if (e != hipSuccess) return hip_fail("hipEventSynchronize", e);
+  // mean per stage name, in order of first appearance
+  std::vector<const char *> order;
+  std::vector<double> sum;
+  std::vector<int> cnt;
+  for (const auto &s : h->stages) {
+    float t = 0.f;
+    e = hipEventElapsedTime(&t, s.a, s.b);
+    if (e != hipSuccess) return hip_fail("hipEventElapsedTime", e);
+    size_t k = 0;
+    while (k < order.size() && std::strcmp(order[k], s.name) != 0) ++k;
+    if (k == order.size()) {
+      order.push_back(s.name);
+      sum.push_back(0.0);
+      cnt.push_back(0);
+    }
+    sum[k] += t;
+    cnt[k] += 1;
+  }
+  const int n = int(std::min<size_t>(order.size(), size_t(std::max(cap, 0))));
+  for (int i = 0; i < n; ++i) {
+    if (names) names[i] = order[i];
+    if (ms) ms[i] = float(sum[i] / cnt[i]);
+  }
+  return int32_t(order.size());
+}
+
+sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *out, void *stream_v) {
+  g_err.clear();
+  if (!h || !in || !out) return fail(SV_ERR_INVALID_ARG, "handle, inputs and outputs must be non-null");
+  const sv::Dims &dm = h->dm;
+  const hipStream_t stream = static_cast<hipStream_t>(stream_v);
+
+  // ---- host-side validation and plan (nothing is enqueued before this passes)
+  sv::HostInputs hi{in->n_rows, in->n_roots, in->parent, in->pos, in->root_kv_off, in->root_kv_len, in->kv_tokens};
+  sv::Plan plan;
+  std::string err;
+  const int pc = sv::build_plan(dm, hi, h->slot_cap, h->target_items, &plan, &err);
+  if (pc != sv::P_OK) return fail(sv_status(pc), err);
+  if (!in->q_rows || !in->k_rows || !in->v_rows || !in->draft_ids)
+    return fail(SV_ERR_INVALID_ARG, "q_rows, k_rows, v_rows and draft_ids must be non-null device pointers");
+  if (plan.n_draft > 0 && !in->drafter_logits)
+    return fail(SV_ERR_INVALID_ARG, "drafter_logits must be non-null when the block has draft rows");
+  if (in->kv_tokens > 0 && (!in->kv_k || !in->kv_v))
+    return fail(SV_ERR_INVALID_ARG, "kv_k and kv_v must be non-null when kv_tokens > 0");
+  if (!out->accept_len || !out->bonus || !out->last_row || !out->surv_sum || !out->argmax || !out->row_max ||
+      !out->row_lse || !out->overlap || !out->survival)
+    return fail(SV_ERR_INVALID_ARG, "every output except logits must be a non-null device pointer");
+  const sv::MetaLayout lay =
+      sv::meta_layout(plan.n, plan.R, plan.n_draft, int(plan.items.size()), plan.R * dm.Hkv * plan.qg_max);
+  if (lay.total > h->meta_cap) return fail(SV_ERR_CAPACITY, "metadata exceeds the handle's staging capacity");
+
+  const int n = plan.n;
+  const int64_t V = dm.vocab, H = dm.hidden, D = dm.d, Hq = dm.Hq, Hkv = dm.Hkv;
+  const bool bf16 = dm.dtype == SV_BF16;
+
+  size_t step_stage = 0;
+  if (h->profile) {
+    Stage s{"step", nullptr, nullptr};
+    (void)hipEventCreate(&s.a);
+    (void)hipEventCreate(&s.b);
+    h->stages.push_back(s);
+    step_stage = h->stages.size() - 1;
+  }
+  // ---- metadata: pinned staging slot -> one async copy
+  const int slot = h->ring;
+  h->ring = (h->ring + 1) % kRing;
+  hipError_t e;
+  if (h->meta_used[slot]) {
+    e = hipEventSynchronize(h->meta_ev[slot]);   // the copy issued kRing runs ago
+    if (e != hipSuccess) return hip_fail("hipEventSynchronize", e);
+  }
+  sv::MetaLayout lay2;
+  sv::pack_plan(plan, dm.Hkv, h->h_meta[slot], &lay2);
+  if (h->profile) (void)hipEventRecord(h->stages[step_stage].a, stream);
+  e = hipMemcpyAsync(h->d_meta, h->h_meta[slot], lay.total, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail("hipMemcpyAsync", e);
+  e = hipEventRecord(h->meta_ev[slot], stream);
+  if (e != hipSuccess) return hip_fail("hipEventRecord", e);
+  h->meta_used[slot] = true;
+
+  const char *m = h->d_meta;
+  const int32_t *row_tree = reinterpret_cast<const int32_t *>(m + lay.row_tree);
+  const int32_t *row_local = reinterpret_cast<const int32_t *>(m + lay.row_local);
+  const int32_t *row_pos = reinterpret_cast<const int32_t *>(m + lay.row_pos);
+  const int32_t *row_parent = reinterpret_cast<const int32_t *>(m + lay.row_parent);
+  const int32_t *row_draft = reinterpret_cast<const int32_t *>(m + lay.row_draft);
+  const uint64_t *row_anc = reinterpret_cast<const uint64_t *>(m + lay.row_anc);
+  const int32_t *draft_row = reinterpret_cast<const int32_t *>(m + lay.draft_row);
+  const int32_t *tree_start = reinterpret_cast<const int32_t *>(m + lay.tree_start);
+  const int32_t *tree_rows = reinterpret_cast<const int32_t *>(m + lay.tree_rows);
+  const int32_t *tree_kv_len = reinterpret_cast<const int32_t *>(m + lay.tree_kv_len);
+  const int64_t *tree_kv_off = reinterpret_cast<const int64_t *>(m + lay.tree_kv_off);
+  const sv::AttnItem *items = reinterpret_cast<const sv::AttnItem *>(m + lay.items);
+  const int32_t *group_first = reinterpret_cast<const int32_t *>(m + lay.group_first);
+  const int32_t *group_count = reinterpret_cast<const int32_t *>(m + lay.group_count);
+
+  // ---- stage bookkeeping for profiling (events on the run's stream)
+  auto begin = [&](const char *name) {
+    if (!h->profile) return;
+    Stage s{name, nullptr, nullptr};
+    (void)hipEventCreate(&s.a);
+    (void)hipEventCreate(&s.b);
+    (void)hipEventRecord(s.a, stream);
+    h->stages.push_back(s);
+  };
+  auto end = [&]() {
+    if (!h->profile) return;
+    (void)hipEventRecord(h->stages.back().b, stream);
+  };
+
+  float *logits = out->logits ? out->logits : h->logits;
+  const int tile_w = bf16 ? sv::lm_tile_width(n) : 256;
+  const int n_tiles = int(ceil_div(V, tile_w));
+
+  sv::VocabArgs va{};
+  va.n = n;
+  va.n_draft = plan.n_draft;
+  va.R = plan.R;
+  va.V = int(V);
+  va.row_parent = row_parent;
+  va.row_draft = row_draft;
+  va.draft_row = draft_row;
+  va.tree_start = tree_start;
+  va.tree_rows = tree_rows;
+  va.draft_ids = in->draft_ids;
+  va.drafter = in->drafter_logits;
+  va.drafter_bf16 = bf16 ? 1 : 0;
+  va.logits = logits;
+  va.t_max = h->t_max;
+  va.t_sum = h->t_sum;
+  va.t_arg = h->t_arg;
+  va.n_tiles = n_tiles;
+  va.dpart = h->dpart;
+  va.n_dch = h->n_dch;
+  va.dchunk = kDChunk;
+  va.lse_q = h->lse_q;
+  va.opart = h->opart;
+  va.n_och = h->n_och;
+  va.ochunk = kOChunk;
+  va.argmax = out->argmax;
+  va.accept_len = out->accept_len;
+  va.bonus = out->bonus;
+  va.last_row = out->last_row;
+  va.row_max = out->row_max;
+  va.row_lse = out->row_lse;
+  va.overlap = out->overlap;
+  va.survival = out->survival;
+  va.surv_sum = out->surv_sum;
+
+  int k_split = 0;
+  const int splits = bf16 ? wo_splits(h, n, &k_split) : 1;
+  // activation format of the projections: bf16 hi + lo planes for the
+  // skinny launch, fp16 for the tiled one
+  const int act_mode = n <= 64 ? sv::ACT_SPLIT : sv::ACT_F16;
+  const int64_t q_lo = int64_t(dm.max_rows) * Hq * D;   // lo planes start one capacity further
+  const int64_t o_lo = int64_t(dm.max_rows) * Hq * D;
+  const int64_t h_lo = int64_t(dm.max_rows) * H;
+
+  if (bf16) {
+    begin("rope");
+    sv::launch_rope_bf16(static_cast<const uint16_t *>(in->q_rows), static_cast<const uint16_t *>(in->k_rows),
+                         static_cast<uint16_t *>(h->q_rot), static_cast<uint16_t *>(h->k_rot), row_pos, n, int(Hq),
+                         int(Hkv), int(D), double(h->cfg.rope_base), q_lo, stream);
+    end();
+    begin("drafter_stats");
+    sv::launch_drafter_partial(va, stream);
+    end();
+    sv::AttnArgs aa{};
+    aa.kv_k = static_cast<const uint16_t *>(in->kv_k);
+    aa.kv_v = static_cast<const uint16_t *>(in->kv_v);
+    aa.k_rot = static_cast<const uint16_t *>(h->k_rot);
+    aa.v_rows = static_cast<const uint16_t *>(in->v_rows);
+    aa.q_rot = static_cast<const uint16_t *>(h->q_rot);
+    aa.q_lo_off = q_lo;
+    aa.items = items;
+    aa.tree_start = tree_start;
+    aa.tree_rows = tree_rows;
+    aa.tree_kv_len = tree_kv_len;
+    aa.tree_kv_off = tree_kv_off;
+    aa.row_anc = row_anc;
+    aa.part_o = h->part_o;
+    aa.part_ml = h->part_ml;
+    aa.Hq = int(Hq);
+    aa.Hkv = int(Hkv);
+    aa.G = int(Hq / Hkv);
+    aa.scale_log2 = float(1.4426950408889634 / std::sqrt(double(D)));
+    int max_nq = 1;
+    for (const auto &it : plan.items) max_nq = std::max(max_nq, int(it.nq));
+    begin("attention");
+    sv::launch_attn_mfma(aa, int(plan.items.size()), int(D), int(ceil_div(max_nq, 16)), stream);
+    end();
+    sv::MergeArgs ma{};
+    ma.part_o = h->part_o;
+    ma.part_ml = h->part_ml;
+    ma.items = items;
+    ma.group_first = group_first;
+    ma.group_count = group_count;
+    ma.row_tree = row_tree;
+    ma.row_local = row_local;
+    ma.Hq = int(Hq);
+    ma.Hkv = int(Hkv);
+    ma.qg_max = plan.qg_max;
+    ma.mode = act_mode;
+    ma.lo_off = o_lo;
+    ma.out = static_cast<uint16_t *>(h->o_act);
+    begin("attn_merge");
+    sv::launch_attn_merge(ma, n, int(D), stream);
+    end();
+    sv::GemmArgs g{};
+    g.act = static_cast<const uint16_t *>(h->o_act);
+    g.act_lo = g.act + o_lo;
+    g.rows = n;
+    g.W = static_cast<const uint16_t *>(h->w_o);
+    g.N = int(H);
+    g.K = int(Hq * D);
+    g.k_split = k_split;
+    g.out = h->h_part;
+    g.ldo = H;
+    g.split_stride = int64_t(n) * H;
+    begin("w_o");
+    sv::launch_gemm_bf16(g, false, splits, stream);
+    end();
+    begin("final_norm");
+    sv::launch_norm(h->h_part, splits, int64_t(n) * H, n, int(H), h->cfg.norm_eps, act_mode, h->hn, h_lo, stream);
+    end();
+    sv::GemmArgs l{};
+    l.act = static_cast<const uint16_t *>(h->hn);
+    l.act_lo = l.act + h_lo;
+    l.rows = n;
+    l.W = static_cast<const uint16_t *>(h->w_lm);
+    l.N = int(V);
+    l.K = int(H);
+    l.k_split = int(H);
+    l.out = logits;
+    l.ldo = V;
+    l.split_stride = 0;
+    l.t_max = h->t_max;
+    l.t_sum = h->t_sum;
+    l.t_arg = h->t_arg;
+    l.n_tiles = n_tiles;
+    begin("lm_head");
+    sv::launch_gemm_bf16(l, true, 1, stream);
+    end();
+  } else {
+    begin("rope");
+    sv::launch_rope_f32(static_cast<const float *>(in->q_rows), static_cast<const float *>(in->k_rows),
+                        static_cast<float *>(h->q_rot), static_cast<float *>(h->k_rot), row_pos, n, int(Hq), int(Hkv),
+                        int(D), double(h->cfg.rope_base), stream);
+    end();
+    begin("drafter_stats");
+    sv::launch_drafter_partial(va, stream);
+    end();
+    sv::AttnF32Args af{};
+    af.kv_k = static_cast<const float *>(in->kv_k);
+    af.kv_v = static_cast<const float *>(in->kv_v);
+    af.k_rot = static_cast<const float *>(h->k_rot);
+    af.v_rows = static_cast<const float *>(in->v_rows);
+    af.q_rot = static_cast<const float *>(h->q_rot);
+    af.row_tree = row_tree;
+    af.tree_start = tree_start;
+    af.tree_rows = tree_rows;
+    af.tree_kv_len = tree_kv_len;
+    af.tree_kv_off = tree_kv_off;
+    af.row_anc = row_anc;
+    af.out = static_cast<float *>(h->o_act);
+    af.Hq = int(Hq);
+    af.Hkv = int(Hkv);
+    af.D = int(D);
+    begin("attention");
+    sv::launch_attn_f32(af, n, stream);
+    end();
+    begin("w_o");
+    sv::launch_gemm_f32(static_cast<const float *>(h->o_act), n, static_cast<const float *>(h->w_o), int(H),
+                        int(Hq * D), h->h_part, stream);
+    end();
+    begin("final_norm");
+    sv::launch_norm(h->h_part, 1, 0, n, int(H), h->cfg.norm_eps, sv::ACT_F32, h->hn, 0, stream);
+    end();
+    begin("lm_head");
+    sv::launch_gemm_f32(static_cast<const float *>(h->hn), n, static_cast<const float *>(h->w_lm), int(V), int(H),
+                        logits, stream);
+    sv::launch_stats_from_logits(logits, n, int(V), 256, h->t_max, h->t_sum, h->t_arg, n_tiles, stream);
+    end();
+  }
+  begin("row_combine");
+  sv::launch_row_combine(va, stream);
+  end();
+  begin("overlap");
+  sv::launch_overlap_partial(va, stream);
+  end();
+  begin("accept");
+  sv::launch_accept(va, stream);
+  end();
+  if (h->profile) (void)hipEventRecord(h->stages[step_stage].b, stream);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail("kernel launch", e);
+  e = hipEventRecord(h->done, stream);
+  if (e != hipSuccess) return hip_fail("hipEventRecord", e);
+  h->ran = true;
+  return SV_OK;
+}
+
+}  // extern "C"

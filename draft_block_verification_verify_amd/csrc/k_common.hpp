@@ -1,0 +1,125 @@
+// Device-side helpers shared by the gfx950 kernels: bf16 bit handling, MFMA
+// wrappers, wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.hpp"
+
+namespace sv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal (streamed data that is read once).
+__device__ __forceinline__ uint4 ld_nt16(const void *p) {
+  const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// fp32 -> fp16 bits, round to nearest even.
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f)); }
+
+// Split x into bf16 hi + lo with hi + lo = x to about 16 significant bits.
+__device__ __forceinline__ void split_bf(float x, uint16_t &hi, uint16_t &lo) {
+  hi = f2bf(x);
+  lo = f2bf(x - bf2f(hi));
+}
+
+// 8 bf16 -> 8 fp16.  Exact for |x| in the fp16 normal range (a bf16
+// significand fits in fp16's); tiny values become fp16 subnormals.
+__device__ __forceinline__ uint4 bf8_to_h8(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xFFFF0000u);
+    o[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// D(32x32) += A(32x16) * B(16x32).  Lane l supplies A[l%32][8*(l/32)+0..7],
+// B[8*(l/32)+0..7][l%32]; acc element j of lane l is
+// D[8*(j/4) + 4*(l/32) + (j%4)][l%32].
+__device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(a), as_bf8(b), c, 0, 0, 0);
+}
+
+// Same layout with fp16 operands.
+__device__ __forceinline__ f32x16 mfma32h(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                0);
+}
+
+// D(16x16) += A(16x32) * B(32x16).  Lane l supplies A[l%16][8*(l/16)+0..7],
+// B[8*(l/16)+0..7][l%16]; acc element i of lane l is D[4*(l/16) + i][l%16].
+__device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), as_bf8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Running (max, sum of exp(x - max), index of the max) of a set of logits.
+// The index is the lowest among equal maxima.
+struct MaxSumArg {
+  float m, s;
+  int i;
+};
+
+__device__ __forceinline__ MaxSumArg msa_empty() { return {-INFINITY, 0.f, 0x7fffffff}; }
+
+__device__ __forceinline__ MaxSumArg msa_merge(MaxSumArg a, MaxSumArg b) {
+  MaxSumArg r;
+  r.m = fmaxf(a.m, b.m);
+  if (r.m == -INFINITY) {
+    r.s = 0.f;
+  } else {
+    r.s = a.s * __expf(a.m - r.m) + b.s * __expf(b.m - r.m);
+  }
+  r.i = (b.m > a.m || (b.m == a.m && b.i < a.i)) ? b.i : a.i;
+  return r;
+}
+
+__device__ __forceinline__ MaxSumArg msa_shfl_xor(MaxSumArg a, int mask) {
+  MaxSumArg b;
+  b.m = __shfl_xor(a.m, mask);
+  b.s = __shfl_xor(a.s, mask);
+  b.i = __shfl_xor(a.i, mask);
+  return msa_merge(a, b);
+}
+
+}  // namespace sv

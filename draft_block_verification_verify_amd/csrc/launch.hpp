@@ -1,0 +1,112 @@
+// Kernel argument blocks and host-side launchers of the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.hpp"
+
+namespace sv {
+
+// Formats of the projections' small (activation) operand.
+enum ActMode : int { ACT_SPLIT = 0, ACT_F16 = 1, ACT_F32 = 2 };
+
+struct AttnArgs {
+  const uint16_t *kv_k, *kv_v;     // [T, Hkv, D] bf16, keys already rotated
+  const uint16_t *k_rot, *v_rows;  // [n, Hkv, D] bf16, row keys rotated
+  const uint16_t *q_rot;           // [n, Hq, D] bf16 hi plane of the rotated queries
+  int64_t q_lo_off;                // elements from the hi plane to the lo plane
+  const AttnItem *items;
+  const int32_t *tree_start, *tree_rows, *tree_kv_len;
+  const int64_t *tree_kv_off;
+  const uint64_t *row_anc;
+  float *part_o, *part_ml;         // [slots, D], [slots, 2]
+  int Hq, Hkv, G;
+  float scale_log2;                // log2(e) / sqrt(D)
+};
+
+struct MergeArgs {
+  const float *part_o, *part_ml;
+  const AttnItem *items;
+  const int32_t *group_first, *group_count, *row_tree, *row_local;
+  int Hq, Hkv, qg_max;
+  int mode;                        // ACT_SPLIT: bf16 hi plane at out, lo at out + lo_off; ACT_F16
+  int64_t lo_off;
+  uint16_t *out;                   // [n, Hq*D]
+};
+
+struct AttnF32Args {
+  const float *kv_k, *kv_v, *k_rot, *v_rows, *q_rot;
+  const int32_t *row_tree, *tree_start, *tree_rows, *tree_kv_len;
+  const int64_t *tree_kv_off;
+  const uint64_t *row_anc;
+  float *out;                      // [n, Hq*D]
+  int Hq, Hkv, D;
+};
+
+// out[rows, N] = act[rows, K] . W[N, K]^T (fp32 accumulation).  rows <= 64:
+// act is a bf16 hi + lo pair (ACT_SPLIT); rows > 64: act is fp16 (ACT_F16).
+// Split-K (grid.y) writes out + split * split_stride.  With stats, each
+// workgroup also writes (max, sum exp(x - max), argmax) of its N tile per row.
+struct GemmArgs {
+  const uint16_t *act;             // skinny: bf16 hi plane; tiled: fp16
+  const uint16_t *act_lo;          // skinny: bf16 lo plane
+
+  int rows;
+  const uint16_t *W;
+  int N, K;
+  int k_split;
+  float *out;
+  int64_t ldo, split_stride;
+  float *t_max, *t_sum;
+  int32_t *t_arg;
+  int n_tiles;
+};
+
+// ---- attention ----
+void launch_rope_bf16(const uint16_t *q, const uint16_t *k, uint16_t *qo, uint16_t *ko, const int32_t *row_pos,
+                      int n, int Hq, int Hkv, int D, double base, int64_t q_lo_off, hipStream_t s);
+void launch_rope_f32(const float *q, const float *k, float *qo, float *ko, const int32_t *row_pos, int n, int Hq,
+                     int Hkv, int D, double base, hipStream_t s);
+void launch_attn_mfma(const AttnArgs &a, int n_items, int D, int max_qblocks, hipStream_t s);
+void launch_attn_merge(const MergeArgs &a, int n_rows, int D, hipStream_t s);
+void launch_attn_f32(const AttnF32Args &a, int n_rows, hipStream_t s);
+
+// ---- projections ----
+// Tile width (N columns per stats record) of the LM-head launch chosen for `rows`.
+int lm_tile_width(int rows);
+void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s);
+void launch_gemm_f32(const float *act, int rows, const float *W, int N, int K, float *out, hipStream_t s);
+void launch_stats_from_logits(const float *logits, int rows, int V, int tile, float *t_max, float *t_sum,
+                              int32_t *t_arg, int n_tiles, hipStream_t s);
+// Writes the normalised rows in `mode` (ACT_SPLIT: bf16 hi plane at out, lo
+// plane at out + lo_off; ACT_F16; ACT_F32).
+void launch_norm(const float *part, int splits, int64_t split_stride, int rows, int hidden, float eps, int mode,
+                 void *out, int64_t lo_off, hipStream_t s);
+
+// ---- vocabulary reductions and acceptance ----
+struct VocabArgs {
+  int n, n_draft, R, V;
+  const int32_t *row_parent, *row_draft, *draft_row, *tree_start, *tree_rows;
+  const int32_t *draft_ids;
+  const void *drafter;          // [n_draft, V] bf16 or f32
+  int drafter_bf16;
+  const float *logits;          // [n, V] fp32
+  const float *t_max, *t_sum;
+  const int32_t *t_arg;
+  int n_tiles;
+  float2 *dpart;                // [n_draft, n_dch]
+  int n_dch, dchunk;
+  float *lse_q;                 // [n_draft]
+  float *opart;                 // [n_draft, n_och]
+  int n_och, ochunk;
+  // outputs
+  int32_t *argmax, *accept_len, *bonus, *last_row;
+  float *row_max, *row_lse, *overlap, *survival, *surv_sum;
+};
+void launch_drafter_partial(const VocabArgs &a, hipStream_t s);
+void launch_row_combine(const VocabArgs &a, hipStream_t s);
+void launch_overlap_partial(const VocabArgs &a, hipStream_t s);
+void launch_accept(const VocabArgs &a, hipStream_t s);
+
+}  // namespace sv

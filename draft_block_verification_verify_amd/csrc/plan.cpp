@@ -1,0 +1,306 @@
+// Host-side planning of one verify step (see plan.hpp).
+#include "plan.hpp"
+
+#include <algorithm>
+#include <cstring>
+#include <sstream>
+
+namespace sv {
+
+namespace {
+
+template <class... A>
+std::string cat(A &&...a) {
+  std::ostringstream s;
+  (s << ... << a);
+  return s.str();
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
+
+}  // namespace
+
+int check_dims(const Dims &dm, std::string *err) {
+  if (dm.Hq < 1 || dm.Hkv < 1 || dm.Hq % dm.Hkv != 0) {
+    *err = cat("n_q_heads (", dm.Hq, ") must be a positive multiple of n_kv_heads (", dm.Hkv, ")");
+    return P_INVALID;
+  }
+  if (dm.d != 64 && dm.d != 128 && dm.d != 256) {
+    *err = cat("head_dim ", dm.d, " unsupported (64, 128 or 256)");
+    return P_UNSUPPORTED;
+  }
+  if (dm.hidden < 64 || dm.hidden % 64 != 0) {
+    *err = cat("hidden ", dm.hidden, " must be a positive multiple of 64");
+    return P_UNSUPPORTED;
+  }
+  if (dm.vocab < 2) {
+    *err = cat("vocab ", dm.vocab, " must be >= 2");
+    return P_INVALID;
+  }
+  if (dm.dtype != 0 && dm.dtype != 1) {
+    *err = cat("dtype ", dm.dtype, " is neither SV_F32 (0) nor SV_BF16 (1)");
+    return P_INVALID;
+  }
+  if (dm.max_rows < 1 || dm.max_roots < 1 || dm.max_pos < 1) {
+    *err = "max_rows, max_roots and max_pos must be >= 1";
+    return P_INVALID;
+  }
+  if (dm.max_tree_rows < 1 || dm.max_tree_rows > kMaxTreeRows) {
+    *err = cat("max_tree_rows ", dm.max_tree_rows, " must be in [1, ", kMaxTreeRows, "]");
+    return P_INVALID;
+  }
+  if (dm.max_roots > dm.max_rows) {
+    *err = "max_roots exceeds max_rows";
+    return P_INVALID;
+  }
+  return P_OK;
+}
+
+int64_t slot_capacity(const Dims &dm) {
+  int64_t s = int64_t(16) * dm.Hq * dm.max_rows;
+  return std::min<int64_t>(196608, std::max<int64_t>(16384, s));
+}
+
+static int qg_max_of(const Dims &dm) {
+  const int G = dm.Hq / dm.Hkv;
+  return int(ceil_div(int64_t(dm.max_tree_rows) * G, kItemQ));
+}
+
+MetaLayout meta_layout(int n, int R, int n_draft, int n_items, int n_groups) {
+  MetaLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align16(o + bytes);
+    return at;
+  };
+  L.row_tree = take(4 * size_t(n));
+  L.row_local = take(4 * size_t(n));
+  L.row_pos = take(4 * size_t(n));
+  L.row_parent = take(4 * size_t(n));
+  L.row_draft = take(4 * size_t(n));
+  L.row_anc = take(8 * size_t(n));
+  L.draft_row = take(4 * size_t(std::max(n_draft, 1)));
+  L.tree_start = take(4 * size_t(R));
+  L.tree_rows = take(4 * size_t(R));
+  L.tree_kv_len = take(4 * size_t(R));
+  L.tree_kv_off = take(8 * size_t(R));
+  L.items = take(sizeof(AttnItem) * size_t(std::max(n_items, 1)));
+  L.group_first = take(4 * size_t(n_groups));
+  L.group_count = take(4 * size_t(n_groups));
+  L.total = o;
+  return L;
+}
+
+size_t meta_capacity(const Dims &dm, int target_items) {
+  const int qg = qg_max_of(dm);
+  const int groups = dm.max_roots * dm.Hkv * qg;
+  const int items = target_items + groups + 64;
+  return meta_layout(dm.max_rows, dm.max_roots, dm.max_rows, items, groups).total;
+}
+
+int build_plan(const Dims &dm, const HostInputs &in, int64_t slot_cap, int target_items,
+               Plan *plan, std::string *err) {
+  Plan &P = *plan;
+  P = Plan{};
+  if (in.n_rows < 1) {
+    *err = cat("n_rows ", in.n_rows, " must be >= 1");
+    return P_INVALID;
+  }
+  if (in.n_rows > dm.max_rows) {
+    *err = cat("n_rows ", in.n_rows, " exceeds max_rows ", dm.max_rows);
+    return P_CAPACITY;
+  }
+  if (in.n_roots < 1) {
+    *err = cat("n_roots ", in.n_roots, " must be >= 1");
+    return P_INVALID;
+  }
+  if (in.n_roots > dm.max_roots) {
+    *err = cat("n_roots ", in.n_roots, " exceeds max_roots ", dm.max_roots);
+    return P_CAPACITY;
+  }
+  if (!in.parent || !in.pos || !in.root_kv_off || !in.root_kv_len) {
+    *err = "parent, pos, root_kv_off and root_kv_len must be non-null host arrays";
+    return P_INVALID;
+  }
+  if (in.kv_tokens < 0) {
+    *err = "kv_tokens must be >= 0";
+    return P_INVALID;
+  }
+  const int n = in.n_rows;
+  P.n = n;
+  P.row_tree.resize(n);
+  P.row_local.resize(n);
+  P.row_pos.resize(n);
+  P.row_parent.resize(n);
+  P.row_draft.resize(n);
+  P.row_anc.resize(n);
+  int tree = -1, start = 0;
+  for (int i = 0; i < n; ++i) {
+    const int p = in.parent[i];
+    if (p == -1) {
+      ++tree;
+      if (tree >= in.n_roots) {
+        *err = cat("row ", i, " starts tree ", tree, " but n_roots is ", in.n_roots);
+        return P_BAD_TREE;
+      }
+      start = i;
+      P.tree_start.push_back(i);
+    } else {
+      if (i == 0) {
+        *err = "row 0 must be a root (parent -1)";
+        return P_BAD_TREE;
+      }
+      if (p < start || p >= i) {
+        *err = cat("row ", i, ": parent ", p, " outside its tree's rows [", start, ", ", i, ")");
+        return P_BAD_TREE;
+      }
+    }
+    const int local = i - start;
+    if (local >= dm.max_tree_rows) {
+      *err = cat("tree ", tree, " has more than max_tree_rows = ", dm.max_tree_rows, " rows");
+      return P_CAPACITY;
+    }
+    if (in.pos[i] < 0 || in.pos[i] >= dm.max_pos) {
+      *err = cat("row ", i, ": position ", in.pos[i], " outside [0, max_pos = ", dm.max_pos, ")");
+      return P_BAD_TREE;
+    }
+    P.row_tree[i] = tree;
+    P.row_local[i] = local;
+    P.row_pos[i] = in.pos[i];
+    P.row_parent[i] = p;
+    P.row_anc[i] = (p == -1 ? 0ull : P.row_anc[p]) | (1ull << local);
+    if (p == -1) {
+      P.row_draft[i] = -1;
+    } else {
+      P.row_draft[i] = int32_t(P.draft_row.size());
+      P.draft_row.push_back(i);
+    }
+  }
+  P.R = tree + 1;
+  if (P.R != in.n_roots) {
+    *err = cat("parent map has ", P.R, " roots but n_roots is ", in.n_roots);
+    return P_BAD_TREE;
+  }
+  P.n_draft = int(P.draft_row.size());
+  P.tree_rows.resize(P.R);
+  P.tree_kv_len.resize(P.R);
+  P.tree_kv_off.resize(P.R);
+  for (int r = 0; r < P.R; ++r) {
+    const int end = (r + 1 < P.R) ? P.tree_start[r + 1] : n;
+    P.tree_rows[r] = end - P.tree_start[r];
+    const int64_t off = in.root_kv_off[r];
+    const int32_t len = in.root_kv_len[r];
+    if (len < 0 || off < 0 || off + len > in.kv_tokens) {
+      *err = cat("tree ", r, ": prefix [", off, ", ", off + int64_t(len), ") outside the ",
+                 in.kv_tokens, " KV tokens");
+      return P_BAD_TREE;
+    }
+    if (int64_t(len) + dm.max_pos > (int64_t(1) << 30)) {
+      *err = cat("tree ", r, ": prefix length ", len, " too large");
+      return P_CAPACITY;
+    }
+    P.tree_kv_len[r] = len;
+    P.tree_kv_off[r] = off;
+  }
+
+  // ---- attention work list -------------------------------------------------
+  const int G = dm.Hq / dm.Hkv;
+  P.qg_max = qg_max_of(dm);
+  int64_t total = 0;
+  int mq_max = 1;
+  for (int r = 0; r < P.R; ++r) {
+    const int64_t mq = int64_t(P.tree_rows[r]) * G;
+    mq_max = int(std::max<int64_t>(mq_max, std::min<int64_t>(mq, kItemQ)));
+    total += int64_t(dm.Hkv) * ceil_div(mq, kItemQ) * (P.tree_kv_len[r] + P.tree_rows[r]);
+  }
+  // Each item writes nq partial records of (d + 2) floats; keep that below a
+  // quarter of the item's KV bytes (chunk >= 8 * nq), and aim for
+  // `target_items` items overall.
+  int64_t chunk = std::max<int64_t>({64, 8 * int64_t(mq_max), ceil_div(total, std::max(target_items, 1))});
+  chunk = ceil_div(chunk, 32) * 32;
+  for (;;) {
+    int64_t slots = 0;
+    for (int r = 0; r < P.R; ++r) {
+      const int64_t K = P.tree_kv_len[r] + P.tree_rows[r];
+      const int64_t splits = ceil_div(K, chunk);
+      slots += int64_t(dm.Hkv) * splits * P.tree_rows[r] * G;
+    }
+    if (slots <= slot_cap) {
+      P.slots = slots;
+      break;
+    }
+    if (chunk > (int64_t(1) << 30)) {
+      *err = "attention partial capacity exhausted";
+      return P_CAPACITY;
+    }
+    chunk *= 2;
+  }
+  P.chunk = int32_t(chunk);
+  const int n_groups = P.R * dm.Hkv * P.qg_max;
+  P.group_first.assign(n_groups, 0);
+  P.group_count.assign(n_groups, 0);
+  int64_t slot = 0;
+  for (int r = 0; r < P.R; ++r) {
+    const int mq = P.tree_rows[r] * G;
+    const int64_t K = P.tree_kv_len[r] + P.tree_rows[r];
+    const int64_t splits = ceil_div(K, chunk);
+    // equal pieces, multiples of 32 keys, the last one ragged
+    const int64_t piece = ceil_div(ceil_div(K, splits), 32) * 32;
+    for (int g = 0; g < dm.Hkv; ++g) {
+      for (int qg = 0; qg * kItemQ < mq; ++qg) {
+        const int m0 = qg * kItemQ;
+        const int nq = std::min(kItemQ, mq - m0);
+        const int gi = (r * dm.Hkv + g) * P.qg_max + qg;
+        P.group_first[gi] = int32_t(P.items.size());
+        for (int64_t k0 = 0; k0 < K; k0 += piece) {
+          AttnItem it{};
+          it.tree = r;
+          it.g = g;
+          it.m0 = m0;
+          it.nq = nq;
+          it.k0 = int32_t(k0);
+          it.k1 = int32_t(std::min(K, k0 + piece));
+          it.slot = int32_t(slot);
+          slot += nq;
+          P.items.push_back(it);
+        }
+        P.group_count[gi] = int32_t(P.items.size()) - P.group_first[gi];
+      }
+    }
+  }
+  P.slots = slot;
+  const size_t cap_items = size_t(target_items) + size_t(dm.max_roots) * dm.Hkv * P.qg_max + 64;
+  if (P.items.size() > cap_items || P.slots > slot_cap) {
+    *err = "attention work list exceeds the handle's capacity";
+    return P_CAPACITY;
+  }
+  return P_OK;
+}
+
+void pack_plan(const Plan &p, int Hkv, void *dst, MetaLayout *lay) {
+  const int n_groups = p.R * Hkv * p.qg_max;
+  MetaLayout L = meta_layout(p.n, p.R, p.n_draft, int(p.items.size()), n_groups);
+  char *b = static_cast<char *>(dst);
+  auto put = [&](size_t off, const void *src, size_t bytes) {
+    if (bytes) std::memcpy(b + off, src, bytes);
+  };
+  put(L.row_tree, p.row_tree.data(), 4 * size_t(p.n));
+  put(L.row_local, p.row_local.data(), 4 * size_t(p.n));
+  put(L.row_pos, p.row_pos.data(), 4 * size_t(p.n));
+  put(L.row_parent, p.row_parent.data(), 4 * size_t(p.n));
+  put(L.row_draft, p.row_draft.data(), 4 * size_t(p.n));
+  put(L.row_anc, p.row_anc.data(), 8 * size_t(p.n));
+  put(L.draft_row, p.draft_row.data(), 4 * size_t(p.n_draft));
+  put(L.tree_start, p.tree_start.data(), 4 * size_t(p.R));
+  put(L.tree_rows, p.tree_rows.data(), 4 * size_t(p.R));
+  put(L.tree_kv_len, p.tree_kv_len.data(), 4 * size_t(p.R));
+  put(L.tree_kv_off, p.tree_kv_off.data(), 8 * size_t(p.R));
+  put(L.items, p.items.data(), sizeof(AttnItem) * p.items.size());
+  put(L.group_first, p.group_first.data(), 4 * size_t(n_groups));
+  put(L.group_count, p.group_count.data(), 4 * size_t(n_groups));
+  *lay = L;
+}
+
+}  // namespace sv

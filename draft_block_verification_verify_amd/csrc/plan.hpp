@@ -1,0 +1,84 @@
+// Host-side planning of one verify step: argument and tree validation, per-row
+// tree metadata and the attention work list.  Pure C++17, no HIP, so it can be
+// compiled and tested on a machine without a GPU.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace sv {
+
+// Query vectors of one attention work item: the (row, head-in-group) pairs of
+// one tree for one KV head, at most kItemQ of them per item.
+constexpr int kItemQ = 128;
+constexpr int kMaxTreeRows = 64;   // ancestor masks are one uint64 per row
+
+struct Dims {
+  int32_t Hq, Hkv, d, hidden, vocab, dtype;
+  int32_t max_rows, max_roots, max_tree_rows, max_pos;
+};
+
+// One attention work item: keys [k0, k1) of the tree's virtual key sequence
+// (prefix tokens 0..len-1, then the tree's rows in row order) against query
+// vectors [m0, m0+nq) of (tree, kv head g); m = local_row * G + head_in_group.
+struct AttnItem {
+  int32_t tree, g, m0, nq, k0, k1, slot, pad;
+};
+static_assert(sizeof(AttnItem) == 32, "AttnItem layout");
+
+struct HostInputs {
+  int32_t n_rows, n_roots;
+  const int32_t *parent, *pos;
+  const int64_t *root_kv_off;
+  const int32_t *root_kv_len;
+  int64_t kv_tokens;
+};
+
+struct Plan {
+  int32_t n = 0, R = 0, n_draft = 0;
+  // per row
+  std::vector<int32_t> row_tree, row_local, row_pos, row_parent, row_draft;
+  std::vector<uint64_t> row_anc;     // ancestor-or-self bits, tree-local
+  // per draft row: its global row
+  std::vector<int32_t> draft_row;
+  // per tree
+  std::vector<int32_t> tree_start, tree_rows, tree_kv_len;
+  std::vector<int64_t> tree_kv_off;
+  // attention
+  std::vector<AttnItem> items;
+  int32_t qg_max = 1;                 // query groups per (tree, g)
+  std::vector<int32_t> group_first, group_count;   // [R * Hkv * qg_max]
+  int32_t chunk = 0;                  // keys per work item (before ragged ends)
+  int64_t slots = 0;                  // partial (m, l, o) records needed
+};
+
+// Validation status codes (same values as sv_status).
+enum PlanStatus { P_OK = 0, P_INVALID = -1, P_BAD_TREE = -2, P_CAPACITY = -3, P_UNSUPPORTED = -4 };
+
+// Check the model description and capacities.
+int check_dims(const Dims &dm, std::string *err);
+
+// Validate the host inputs of one run and build its plan.  `slot_cap` bounds
+// plan->slots; the work split is coarsened until it fits.  `target_items`
+// is the work-item count to aim for (a few per compute unit).
+int build_plan(const Dims &dm, const HostInputs &in, int64_t slot_cap, int target_items,
+               Plan *plan, std::string *err);
+
+// Attention partial records that a handle reserves for the given shape.
+int64_t slot_capacity(const Dims &dm);
+
+// Byte layout of the device copy of a plan (offsets into one buffer).
+struct MetaLayout {
+  size_t row_tree, row_local, row_pos, row_parent, row_draft, row_anc, draft_row;
+  size_t tree_start, tree_rows, tree_kv_len, tree_kv_off;
+  size_t items, group_first, group_count;
+  size_t total;
+};
+MetaLayout meta_layout(int n, int R, int n_draft, int n_items, int n_groups);
+// Upper bound of the meta buffer for a handle's capacities.
+size_t meta_capacity(const Dims &dm, int target_items);
+// Serialise the plan into `dst` (at least meta_layout(...).total bytes).
+void pack_plan(const Plan &p, int Hkv, void *dst, MetaLayout *lay);
+
+}  // namespace sv

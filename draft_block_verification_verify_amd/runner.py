@@ -1,0 +1,82 @@
+"""Device plumbing around the C ABI: upload a generated workload with torch,
+create a handle, run the verify step, read the outputs back.
+
+Nothing here computes any part of the verify step.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import binding as B
+from .workloads import Config, Inputs
+
+
+def sv_config(cfg: Config, *, max_rows: int, max_roots: int, max_tree_rows: int = 64,
+              max_pos: int = 1 << 20) -> B.SvConfig:
+    return B.SvConfig(cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.hidden, cfg.vocab,
+                      B.SV_BF16 if cfg.dtype == "bf16" else B.SV_F32, cfg.rope_base, cfg.norm_eps,
+                      max_rows, max_roots, max_tree_rows, max_pos)
+
+
+def to_device(x: np.ndarray | None, dtype: str, device):
+    import torch
+    if x is None:
+        return None
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16))
+        return t.to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+class DeviceCase:
+    """A workload resident on the GPU plus a handle ready to run it."""
+
+    def __init__(self, inp: Inputs, device="cuda:0", *, with_logits: bool = False, verifier=None,
+                 weights=None, max_rows: int | None = None, max_roots: int | None = None):
+        import torch
+        self.inp = inp
+        cfg, st = inp.cfg, inp.st
+        self.device = torch.device(device)
+        dt = cfg.dtype
+        self.kv_k = to_device(inp.kv_k, dt, device) if st.kv_tokens > 0 else None
+        self.kv_v = to_device(inp.kv_v, dt, device) if st.kv_tokens > 0 else None
+        self.q = to_device(inp.q_rows, dt, device)
+        self.k = to_device(inp.k_rows, dt, device)
+        self.v = to_device(inp.v_rows, dt, device)
+        self.dl = to_device(inp.drafter_logits, dt, device) if inp.drafter_logits.shape[0] else None
+        self.draft_ids = torch.from_numpy(np.ascontiguousarray(inp.draft_ids, np.int32)).to(device)
+        if weights is None:
+            weights = (to_device(inp.w_o, dt, device), to_device(inp.w_lm, dt, device))
+        self.w_o, self.w_lm = weights
+        if verifier is None:
+            verifier = B.Verifier(sv_config(cfg, max_rows=max_rows or st.n_rows,
+                                            max_roots=max_roots or st.n_roots,
+                                            max_pos=int(st.pos.max()) + 1),
+                                  self.w_o, self.w_lm)
+        self.ver = verifier
+        self.outs = verifier.alloc_outputs(st.n_rows, st.n_roots, self.device, with_logits)
+        self.refresh()
+
+    def refresh(self):
+        """Rebuild the C structs (after draft ids or structure change)."""
+        import torch
+        st = self.inp.st
+        self.draft_ids = torch.from_numpy(np.ascontiguousarray(self.inp.draft_ids, np.int32)).to(self.device)
+        self.sv_in, self.sv_out, self._keep = B.Verifier.make_structs(
+            st.parent, st.pos, st.root_kv_off, st.root_kv_len, self.kv_k, self.kv_v, self.q, self.k,
+            self.v, self.draft_ids, self.dl, self.outs)
+        if self.kv_k is None:
+            self.sv_in.kv_tokens = 0
+
+    def run(self, stream=None):
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
+        self.ver.run(self.sv_in, self.sv_out, s)
+
+    def results(self) -> dict:
+        import torch
+        torch.cuda.synchronize(self.device)
+        return {k: (v.cpu().numpy() if v is not None else None) for k, v in self.outs.items()}
+
+    def close(self):
+        self.ver.close()

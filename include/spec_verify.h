@@ -1,0 +1,144 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) verify step for a parallel
+ * draft block.
+ *
+ * One call scores a whole draft block with the target in one forward pass
+ * (sionic.ai "Solar Open2 250B DSpark", section 1: the drafter proposes, the
+ * target checks every candidate in one forward, keeps the agreeing leading
+ * candidates and restarts at the first difference).  A block is either a
+ * chain (the last committed token plus gamma drafts: gamma+1 rows, same
+ * page, section 6) or a proposal tree of B anchors x W branch tokens (onedev.kr
+ * SpecOPD summary, "how it works" / "what differs": parent map, semantic
+ * positions, ancestor-and-self mask).
+ *
+ * Per row the step computes: RoPE of the row query/key at its semantic
+ * position; GQA attention over the tree's KV prefix plus the row's ancestors
+ * and itself; W_o; a unit-gain RMS norm; the LM head over the full vocabulary;
+ * max / logsumexp / greedy token of the target distribution p; for every
+ * non-root row the overlap sum_u min(p_parent(u), q(u)) = 1 - TV(p_parent, q)
+ * against the drafter distribution q (SpecOPD summary, "how it is used";
+ * VESSL "Speculative Decoding Part 2", DSpark section); the prefix-survival
+ * product of overlaps from the root (SpecOPD summary, "how it is used").
+ * Per tree it returns the greedy accept length counting the bonus token
+ * (SpecOPD summary, "premises and limits"), the bonus token and the last
+ * accepted row (VESSL part 2, Blockwise section: keep the longest agreeing
+ * prefix).
+ *
+ * Plain C, no HIP or torch types.  Device pointers are HIP device memory of
+ * the current device; `stream` is a hipStream_t passed as void*.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sv_status {
+  SV_OK = 0,
+  SV_ERR_INVALID_ARG = -1, /* null pointer, bad size or config field      */
+  SV_ERR_BAD_TREE = -2,    /* parent map / positions / KV ranges invalid  */
+  SV_ERR_CAPACITY = -3,    /* run exceeds a capacity fixed at create       */
+  SV_ERR_UNSUPPORTED = -4, /* not a gfx950 device, or unsupported shape    */
+  SV_ERR_HIP = -5,         /* a HIP runtime call failed                    */
+  SV_ERR_OOM = -6          /* device or pinned host allocation failed      */
+} sv_status;
+
+typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* Model shape and capacities, fixed for the handle's lifetime. */
+typedef struct sv_config {
+  int32_t n_q_heads;     /* Hq; a multiple of n_kv_heads                       */
+  int32_t n_kv_heads;    /* Hkv; query head h reads KV head h / (Hq/Hkv)       */
+  int32_t head_dim;      /* d: 64, 128 or 256                                  */
+  int32_t hidden;        /* model width (W_o rows, LM-head columns); % 64 == 0 */
+  int32_t vocab;         /* V >= 2                                             */
+  int32_t dtype;         /* sv_dtype of KV, row q/k/v, weights, drafter logits */
+  float rope_base;       /* RoPE base (10000); NeoX half-split pairs (k,k+d/2)  */
+  float norm_eps;        /* final RMS-norm epsilon (1e-6), unit gain           */
+  int32_t max_rows;      /* most rows in one run                              */
+  int32_t max_roots;     /* most trees in one run                             */
+  int32_t max_tree_rows; /* most rows in one tree, <= 64                      */
+  int32_t max_pos;       /* every semantic position must be < max_pos         */
+} sv_config;
+
+typedef struct sv_handle sv_handle;
+
+/* One verify step.  Trees are contiguous row ranges, each starting with its
+ * root (parent -1); for a non-root row i of the tree starting at s,
+ * s <= parent[i] < i.  Roots are numbered in row order and index the
+ * root_kv_* arrays.  Non-root ("draft") rows are numbered in row order and
+ * index drafter_logits. */
+typedef struct sv_inputs {
+  int32_t n_rows;              /* 1 .. max_rows                                 */
+  int32_t n_roots;             /* number of trees (rows with parent -1)         */
+  const int32_t *parent;       /* HOST   [n_rows]                               */
+  const int32_t *pos;          /* HOST   [n_rows]  semantic positions, 0..max_pos-1 */
+  const int64_t *root_kv_off;  /* HOST   [n_roots] first visible prefix token   */
+  const int32_t *root_kv_len;  /* HOST   [n_roots] visible prefix length (>= 0) */
+  int64_t kv_tokens;           /* tokens in kv_k / kv_v                         */
+  const void *kv_k;            /* DEVICE [kv_tokens, Hkv, d], keys already rotated */
+  const void *kv_v;            /* DEVICE [kv_tokens, Hkv, d]                    */
+  const void *q_rows;          /* DEVICE [n_rows, Hq, d]  queries before RoPE   */
+  const void *k_rows;          /* DEVICE [n_rows, Hkv, d] keys before RoPE      */
+  const void *v_rows;          /* DEVICE [n_rows, Hkv, d]                       */
+  const int32_t *draft_ids;    /* DEVICE [n_rows] token at each row; roots ignored */
+  const void *drafter_logits;  /* DEVICE [n_rows - n_roots, V]                  */
+} sv_inputs;
+
+/* Outputs, all DEVICE memory written by the run.  `logits` may be NULL. */
+typedef struct sv_outputs {
+  int32_t *accept_len;  /* [n_roots] accepted drafts + 1 (bonus), in [1, depth+1] */
+  int32_t *bonus;       /* [n_roots] greedy token of the last accepted row          */
+  int32_t *last_row;    /* [n_roots] last accepted row (global row index)           */
+  float *surv_sum;      /* [n_roots] sum of survival over the tree's non-root rows  */
+  int32_t *argmax;      /* [n_rows] greedy token (lowest id among equal maxima)     */
+  float *row_max;       /* [n_rows] max logit                                       */
+  float *row_lse;       /* [n_rows] log sum exp of the logits                       */
+  float *overlap;       /* [n_rows] sum_u min(p_parent, q); 1 for roots             */
+  float *survival;      /* [n_rows] product of overlaps root..row; 1 for roots      */
+  float *logits;        /* [n_rows, V] fp32 target logits, or NULL                  */
+} sv_outputs;
+
+/* Create a handle on the current device.  w_o is DEVICE [hidden, Hq*d] and
+ * w_lm is DEVICE [vocab, hidden], both row-major in cfg->dtype; they are
+ * borrowed (not copied) for the handle's lifetime.  Allocates the handle's
+ * device scratch (sized from the capacities) and pinned host staging.
+ * Fails with SV_ERR_UNSUPPORTED unless the device is gfx950. */
+sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *w_lm,
+                             sv_handle **out);
+
+/* Enqueue one verify step on `stream` (hipStream_t; NULL = default stream).
+ * Host arrays are read and copied before the call returns; device inputs and
+ * outputs must stay valid until the stream passes the enqueued work.  Never
+ * synchronises the host with the device.  Every argument, tree and capacity
+ * check happens before anything is enqueued: on error nothing was enqueued
+ * and the outputs are untouched.  A handle runs one step at a time: steps on
+ * one handle must be ordered by the caller (same stream, or events). */
+sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *out, void *stream);
+
+/* Wait for the handle's last enqueued step, then free everything it owns.
+ * NULL is accepted. */
+sv_status spec_verify_destroy(sv_handle *h);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *spec_verify_last_error(void);
+
+/* Per-stage device times, for profiling.  spec_verify_profile(h, on != 0)
+ * starts recording: every later run records a HIP event before and after each
+ * of its stages (and around the whole step, stage "step") on the run's stream.
+ * spec_verify_stage_times waits for the last recorded run, then writes up to
+ * `cap` stage names (static strings) and their mean duration in ms over all
+ * runs recorded since profiling was switched on; returns the number of
+ * stages (0 if nothing was recorded), or a negative sv_status.
+ * spec_verify_profile(h, 0) stops recording and drops the records. */
+sv_status spec_verify_profile(sv_handle *h, int32_t on);
+int32_t spec_verify_stage_times(sv_handle *h, const char **names, float *ms, int32_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

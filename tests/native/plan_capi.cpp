@@ -1,0 +1,38 @@
+// Test-only C entry to the host planner (plan.cpp), built with g++ on a
+// machine without a GPU: validation status, error text, per-row ancestor
+// masks and the attention work list.
+#include <cstring>
+#include <string>
+
+#include "plan.hpp"
+
+extern "C" int svp_plan(const int *dims, int n_rows, int n_roots, const int32_t *parent, const int32_t *pos,
+                        const int64_t *off, const int32_t *len, int64_t kv_tokens, int64_t slot_cap,
+                        int target_items, int64_t *stats, char *err, int err_cap, uint64_t *anc_out,
+                        int32_t *items_out, int items_cap) {
+  sv::Dims dm{dims[0], dims[1], dims[2], dims[3], dims[4], dims[5], dims[6], dims[7], dims[8], dims[9]};
+  std::string e;
+  int st = sv::check_dims(dm, &e);
+  sv::Plan p;
+  if (st == sv::P_OK) {
+    sv::HostInputs hi{n_rows, n_roots, parent, pos, off, len, kv_tokens};
+    st = sv::build_plan(dm, hi, slot_cap, target_items, &p, &e);
+  }
+  if (err && err_cap > 0) {
+    std::strncpy(err, e.c_str(), size_t(err_cap - 1));
+    err[err_cap - 1] = 0;
+  }
+  if (st != sv::P_OK) return st;
+  stats[0] = p.R;
+  stats[1] = p.n_draft;
+  stats[2] = int64_t(p.items.size());
+  stats[3] = p.slots;
+  stats[4] = p.chunk;
+  stats[5] = p.qg_max;
+  stats[6] = int64_t(sv::meta_layout(p.n, p.R, p.n_draft, int(p.items.size()), p.R * dm.Hkv * p.qg_max).total);
+  stats[7] = int64_t(sv::meta_capacity(dm, target_items));
+  for (int i = 0; i < p.n; ++i) anc_out[i] = p.row_anc[i];
+  const int ni = int(p.items.size()) < items_cap ? int(p.items.size()) : items_cap;
+  std::memcpy(items_out, p.items.data(), sizeof(sv::AttnItem) * size_t(ni));
+  return 0;
+}

@@ -1,0 +1,199 @@
+"""CPU tests of the boundary: the built library loads and exports every
+symbol include/spec_verify.h declares, create() rejects bad configurations
+before touching a device, and the host planner (validation, ancestor masks,
+attention work list) behaves, via a g++ build of plan.cpp."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from draft_block_verification_verify_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+CSRC = os.path.join(ROOT, "draft_block_verification_verify_amd", "csrc")
+
+
+@pytest.fixture(scope="session")
+def libsv():
+    if not os.path.exists(B.LIB_PATH):
+        from draft_block_verification_verify_amd import build
+        build.build()
+    return B.lib()
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(spec_verify_\w+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol(libsv):
+    names = declared_functions()
+    assert set(names) == set(B.SYMBOLS), names
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert getattr(libsv, n) is not None
+
+
+def good_cfg(**kw):
+    c = dict(n_q_heads=4, n_kv_heads=2, head_dim=64, hidden=256, vocab=4096, dtype=B.SV_F32,
+             rope_base=10000.0, norm_eps=1e-6, max_rows=8, max_roots=1, max_tree_rows=8, max_pos=200)
+    c.update(kw)
+    return B.SvConfig(**c)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), B.SV_ERR_UNSUPPORTED),
+    (dict(n_q_heads=5), B.SV_ERR_INVALID_ARG),
+    (dict(hidden=100), B.SV_ERR_UNSUPPORTED),
+    (dict(vocab=1), B.SV_ERR_INVALID_ARG),
+    (dict(dtype=7), B.SV_ERR_INVALID_ARG),
+    (dict(max_tree_rows=65), B.SV_ERR_INVALID_ARG),
+    (dict(max_rows=0), B.SV_ERR_INVALID_ARG),
+    (dict(rope_base=0.5), B.SV_ERR_INVALID_ARG),
+    (dict(norm_eps=-1.0), B.SV_ERR_INVALID_ARG),
+])
+def test_create_rejects_bad_config_before_device(libsv, kw, status):
+    h = C.c_void_p()
+    st = libsv.spec_verify_create(C.byref(good_cfg(**kw)), C.c_void_p(16), C.c_void_p(16), C.byref(h))
+    assert st == status, B.spec_verify_last_error()
+    assert h.value is None
+    assert B.spec_verify_last_error() != ""
+
+
+def test_create_null_weights_and_null_handle_calls(libsv):
+    h = C.c_void_p()
+    assert libsv.spec_verify_create(C.byref(good_cfg()), None, C.c_void_p(16), C.byref(h)) == B.SV_ERR_INVALID_ARG
+    assert libsv.spec_verify_run(None, None, None, None) == B.SV_ERR_INVALID_ARG
+    assert libsv.spec_verify_destroy(None) == B.SV_OK
+    assert libsv.spec_verify_profile(None, 1) == B.SV_ERR_INVALID_ARG
+
+
+def test_create_without_gpu_fails_loudly(libsv):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    h = C.c_void_p()
+    st = libsv.spec_verify_create(C.byref(good_cfg()), C.c_void_p(16), C.c_void_p(16), C.byref(h))
+    assert st in (B.SV_ERR_HIP, B.SV_ERR_UNSUPPORTED)
+    assert h.value is None
+
+
+# ----------------------------------------------------------------------------
+# host planner (g++ build, no HIP)
+# ----------------------------------------------------------------------------
+
+
+@pytest.fixture(scope="session")
+def plan_lib(tmp_path_factory):
+    d = tmp_path_factory.mktemp("svplan")
+    so = str(d / "libsvplan.so")
+    cmd = ["g++", "-O1", "-std=c++17", "-shared", "-fPIC", "-I", CSRC,
+           os.path.join(CSRC, "plan.cpp"), os.path.join(ROOT, "tests", "native", "plan_capi.cpp"), "-o", so]
+    subprocess.run(cmd, check=True)
+    L = C.CDLL(so)
+    L.svp_plan.restype = C.c_int
+    return L
+
+
+def plan(L, dims, parent, pos, off, lens, kv_tokens, slot_cap=1 << 20, target=1024):
+    parent = np.ascontiguousarray(parent, np.int32)
+    pos = np.ascontiguousarray(pos, np.int32)
+    off = np.ascontiguousarray(off, np.int64)
+    lens = np.ascontiguousarray(lens, np.int32)
+    n = len(parent)
+    dims = np.ascontiguousarray(dims, np.int32)
+    stats = np.zeros(8, np.int64)
+    err = C.create_string_buffer(512)
+    anc = np.zeros(max(n, 1), np.uint64)
+    items = np.zeros((8192, 8), np.int32)
+    st = L.svp_plan(dims.ctypes.data_as(C.c_void_p), n, len(lens), parent.ctypes.data_as(C.c_void_p),
+                    pos.ctypes.data_as(C.c_void_p), off.ctypes.data_as(C.c_void_p),
+                    lens.ctypes.data_as(C.c_void_p), C.c_int64(kv_tokens), C.c_int64(slot_cap), target,
+                    stats.ctypes.data_as(C.c_void_p), err, 512, anc.ctypes.data_as(C.c_void_p),
+                    items.ctypes.data_as(C.c_void_p), 8192)
+    return st, err.value.decode(), stats, anc, items[: stats[2]] if st == 0 else None
+
+
+DIMS = [32, 8, 128, 4096, 151936, 1, 512, 64, 64, 1 << 20]   # Hq Hkv d hidden V dtype rows roots tree pos
+
+
+def test_plan_ancestor_masks_and_items_cover_keys(plan_lib):
+    parent = [-1, 0, 0, 1, 2, 2, 5, -1, 7, 8]
+    lens, off = [300, 0], [5, 0]
+    st, err, stats, anc, items = plan(plan_lib, DIMS, parent, np.arange(10) + 400, off, lens, 305)
+    assert st == 0, err
+    # ancestor-or-self masks by brute force
+    starts = [0, 7]
+    for i, p in enumerate(parent):
+        s = max(x for x in starts if x <= i)
+        bits, j = 0, i
+        while j != -1:
+            bits |= 1 << (j - s)
+            j = parent[j]
+        assert int(anc[i]) == bits, i
+    # items: per (tree, kv head, query group) the key ranges tile [0, len + T)
+    T = [7, 3]
+    G = 4
+    assert stats[0] == 2 and stats[1] == 8
+    slots = []
+    for tree in range(2):
+        for g in range(8):
+            for qg in range((T[tree] * G + 127) // 128):
+                its = [it for it in items if it[0] == tree and it[1] == g and it[2] == qg * 128]
+                its.sort(key=lambda it: it[4])
+                assert its[0][4] == 0 and its[-1][5] == lens[tree] + T[tree]
+                for a, b in zip(its, its[1:]):
+                    assert a[5] == b[4]
+                for it in its:
+                    assert it[3] == min(128, T[tree] * G - qg * 128)
+                    slots.append((it[6], it[6] + it[3]))
+    slots.sort()
+    assert slots[0][0] == 0 and slots[-1][1] == stats[3]
+    for a, b in zip(slots, slots[1:]):
+        assert a[1] == b[0]
+    assert stats[6] <= stats[7]          # fits the handle's metadata capacity
+
+
+def test_plan_coarsens_split_to_fit_slot_capacity(plan_lib):
+    parent = [-1] + list(range(16))
+    st, err, stats, _, items = plan(plan_lib, [24, 4, 256, 5120, 248320, 1, 17, 1, 64, 1 << 20],
+                                    parent, np.arange(17) + 8192, [0], [8192], 8192, slot_cap=24 * 17 * 2)
+    assert st == 0, err
+    assert stats[3] <= 24 * 17 * 2
+    assert stats[2] == 4 * 2          # 2 pieces per KV head
+
+
+@pytest.mark.parametrize("parent,pos,off,lens,kv,code,frag", [
+    ([0, 0], [1, 2], [0], [1], 4, -2, "root"),
+    ([-1, 2, 1], [1, 2, 3], [0], [1], 4, -2, "parent"),
+    ([-1, 0, -1, 0], [1, 2, 3, 4], [0, 0], [1, 1], 4, -2, "parent"),
+    ([-1, 0], [1, 2], [0, 0], [1, 1], 4, -2, "roots"),
+    ([-1, 0], [1, 1 << 20], [0], [1], 4, -2, "position"),
+    ([-1, 0], [1, -1], [0], [1], 4, -2, "position"),
+    ([-1, 0], [1, 2], [3], [2], 4, -2, "prefix"),
+    ([-1, 0], [1, 2], [0], [-1], 4, -2, "prefix"),
+])
+def test_plan_rejects_bad_trees(plan_lib, parent, pos, off, lens, kv, code, frag):
+    st, err, *_ = plan(plan_lib, DIMS, parent, pos, off, lens, kv)
+    assert st == code and frag in err, (st, err)
+
+
+def test_plan_capacities(plan_lib):
+    dims = list(DIMS)
+    dims[6], dims[7] = 4, 1          # max_rows, max_roots
+    st, err, *_ = plan(plan_lib, dims, [-1, 0, 1, 2, 3], range(5), [0], [1], 1)
+    assert st == B.SV_ERR_CAPACITY and "max_rows" in err
+    dims = list(DIMS)
+    dims[8] = 4          # max_tree_rows
+    st, err, *_ = plan(plan_lib, dims, [-1, 0, 1, 2, 3], range(5), [0], [1], 1)
+    assert st == B.SV_ERR_CAPACITY and "max_tree_rows" in err
+    dims = list(DIMS)
+    dims[7] = 1          # max_roots
+    st, err, *_ = plan(plan_lib, dims, [-1, -1], range(2), [0, 0], [1, 1], 1)
+    assert st == B.SV_ERR_CAPACITY and "max_roots" in err
