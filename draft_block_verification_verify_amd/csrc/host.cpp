@@ -36,7 +36,8 @@ struct Stage {
 struct sv_handle {
   sv_config cfg{};
   sv::Dims dm{};
-  const void *w_o = nullptr, *w_lm = nullptr;
+  const void *w_o = nullptr, *w_lm = nullptr;   // weights the kernels read (fp16 copies for bf16)
+  int32_t *d_bad = nullptr;
   int device = 0, n_cu = 256, target_items = 1024;
   int elt = 2;
   // metadata
@@ -53,7 +54,6 @@ struct sv_handle {
   int32_t *t_arg = nullptr;
   float2 *dpart = nullptr;
   int64_t slot_cap = 0;
-  int wo_split_max = 1;
   int n_tiles_cap = 0, n_dch = 0, n_och = 0;
   size_t h_part_floats = 0;
   std::vector<void *> allocs;
@@ -100,23 +100,6 @@ void release(sv_handle *h) {
   delete h;
 }
 
-// Split-K factor of W_o for the skinny launch: enough workgroups to cover the
-// chip twice, K pieces of at least 256.
-int wo_splits(const sv_handle *h, int rows, int *k_split) {
-  const int K = h->dm.Hq * h->dm.d;
-  if (rows > 64) {
-    *k_split = K;
-    return 1;
-  }
-  const int n_tiles = int(ceil_div(h->dm.hidden, 128));
-  int s = int(ceil_div(2 * h->n_cu, n_tiles));
-  s = std::max(1, std::min(s, K / 256));
-  int ks = int(ceil_div(ceil_div(K, s), 64) * 64);
-  s = int(ceil_div(K, ks));
-  *k_split = ks;
-  return s;
-}
-
 }  // namespace
 
 extern "C" {
@@ -161,9 +144,13 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
   const int64_t R = dm.max_rows, Hq = dm.Hq, Hkv = dm.Hkv, D = dm.d, H = dm.hidden, V = dm.vocab;
   const int64_t E = h->elt;
   h->slot_cap = sv::slot_capacity(dm);
-  int ks = 0;
-  h->wo_split_max = wo_splits(h, int(std::min<int64_t>(R, 64)), &ks);
-  h->h_part_floats = size_t(std::max<int64_t>(int64_t(h->wo_split_max) * std::min<int64_t>(R, 64), R)) * H;
+  // W_o split-K partials: the largest splits x rows any run up to max_rows needs
+  int64_t part_rows = R;
+  for (int n = 1; n <= dm.max_rows; ++n) {
+    int ks = 0;
+    part_rows = std::max<int64_t>(part_rows, int64_t(sv::gemm_splits(n, int(H), int(Hq * D), h->n_cu, &ks)) * n);
+  }
+  h->h_part_floats = size_t(part_rows) * H;
   h->n_tiles_cap = int(ceil_div(V, 128));
   h->n_dch = int(ceil_div(V, kDChunk));
   h->n_och = int(ceil_div(V, kOChunk));
@@ -190,6 +177,33 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
   A(&h->dpart, size_t(R * h->n_dch * 8));
   A(&h->lse_q, size_t(R * 4));
   A(&h->opart, size_t(R * h->n_och * 4));
+  if (dm.dtype == SV_BF16) {
+    // the projections run on fp16 MFMA: keep fp16 copies of the weights
+    uint16_t *wo16 = nullptr, *wlm16 = nullptr;
+    A(&wo16, size_t(H * Hq * D * 2));
+    A(&wlm16, size_t(V * H * 2));
+    A(&h->d_bad, 4);
+    if (st == SV_OK) {
+      e = hipMemsetAsync(h->d_bad, 0, 4, nullptr);
+      if (e == hipSuccess) {
+        sv::launch_bf16_to_f16(static_cast<const uint16_t *>(w_o), wo16, H * Hq * D, h->d_bad, nullptr);
+        sv::launch_bf16_to_f16(static_cast<const uint16_t *>(w_lm), wlm16, V * H, h->d_bad, nullptr);
+        e = hipGetLastError();
+      }
+      int32_t bad = 0;
+      if (e == hipSuccess) e = hipMemcpy(&bad, h->d_bad, 4, hipMemcpyDeviceToHost);
+      if (e != hipSuccess) {
+        release(h);
+        return hip_fail("weight conversion", e);
+      }
+      if (bad != 0) {
+        release(h);
+        return fail(SV_ERR_UNSUPPORTED, std::to_string(bad) + " weight values exceed the fp16 range (|w| > 65504)");
+      }
+      h->w_o = wo16;
+      h->w_lm = wlm16;
+    }
+  }
   if (st != SV_OK) {
     release(h);
     return st;
@@ -403,7 +417,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   va.surv_sum = out->surv_sum;
 
   int k_split = 0;
-  const int splits = bf16 ? wo_splits(h, n, &k_split) : 1;
+  const int splits = bf16 ? sv::gemm_splits(n, int(H), int(Hq * D), h->n_cu, &k_split) : 1;
   // activation format of the projections: bf16 hi + lo planes for the
   // skinny launch, fp16 for the tiled one
   const int act_mode = n <= 64 ? sv::ACT_SPLIT : sv::ACT_F16;

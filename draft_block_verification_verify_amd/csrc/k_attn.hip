@@ -311,7 +311,7 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(MergeArgs a) {
   const int64_t idx = int64_t(i) * a.Hq * D + int64_t(h) * D + c;
   if (a.mode == ACT_SPLIT) {
     uint16_t hi, lo;
-    split_bf(val, hi, lo);
+    split_h(val, hi, lo);
     a.out[idx] = hi;
     a.out[a.lo_off + idx] = lo;
   } else {

@@ -43,6 +43,14 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 // fp32 -> fp16 bits, round to nearest even.
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f)); }
 
+__device__ __forceinline__ float h2f(uint16_t b) { return float(__builtin_bit_cast(_Float16, b)); }
+
+// Split x into fp16 hi + lo with hi + lo = x to about 22 significant bits.
+__device__ __forceinline__ void split_h(float x, uint16_t &hi, uint16_t &lo) {
+  hi = f2h(x);
+  lo = f2h(x - h2f(hi));
+}
+
 // Split x into bf16 hi + lo with hi + lo = x to about 16 significant bits.
 __device__ __forceinline__ void split_bf(float x, uint16_t &hi, uint16_t &lo) {
   hi = f2bf(x);

@@ -21,6 +21,9 @@
 // their way into LDS (exact for weights in the fp16 normal range) and the
 // activations arrive in fp16, so the activations keep 11 significant bits
 // at no extra MFMA work.
+#include <algorithm>
+#include <type_traits>
+
 #include "k_common.hpp"
 #include "launch.hpp"
 
@@ -61,8 +64,9 @@ __device__ __forceinline__ void store_tile(const GemmArgs &g, const f32x16 (&acc
 }
 
 // Per-lane (max, sumexp, argmax) over the lane's N values of token block t,
-// merged with the partner lane (l ^ 32) holding the other N rows.
-template <int NV, int NT>
+// merged with the partner lane (l ^ 32) holding the other N rows.  CHECK
+// masks columns n >= N (only the last tile of a launch needs it).
+template <int NV, int NT, bool CHECK = true>
 __device__ __forceinline__ MaxSumArg lane_stats(const GemmArgs &g, const f32x16 (&acc)[NV][NT], const int (&nb)[NV],
                                                 int t, int lane) {
   const int kg = lane >> 5;
@@ -74,7 +78,8 @@ __device__ __forceinline__ MaxSumArg lane_stats(const GemmArgs &g, const f32x16 
     for (int j = 0; j < 16; ++j) {
       const int n = nb[v] + 8 * (j >> 2) + 4 * kg + (j & 3);
       const float x = acc[v][t][j];
-      if (n < g.N && (x > m || (x == m && n < arg))) {
+      // columns grow with (v, j): a strict > keeps the lowest index on ties
+      if ((!CHECK || n < g.N) && x > m) {
         m = x;
         arg = n;
       }
@@ -86,7 +91,7 @@ __device__ __forceinline__ MaxSumArg lane_stats(const GemmArgs &g, const f32x16 
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int n = nb[v] + 8 * (j >> 2) + 4 * kg + (j & 3);
-        if (n < g.N) s += __expf(acc[v][t][j] - m);
+        if (!CHECK || n < g.N) s += __expf(acc[v][t][j] - m);
       }
   }
   MaxSumArg r{m, s, arg};
@@ -94,31 +99,123 @@ __device__ __forceinline__ MaxSumArg lane_stats(const GemmArgs &g, const f32x16 
 }
 
 // ----------------------------------------------------------------------------
-// skinny launch
+// direct global -> LDS copies (gfx950 buffer_load ... lds).  A wavefront
+// writes 64 x 16 B = 1 KB of LDS per instruction, lane l at byte 16 l of the
+// wave's destination; the global address of each lane is free, so a tile is
+// laid out XOR-swizzled in LDS by choosing which 16-B chunk a lane fetches.
+// Rows past the end of a tensor are outside the buffer's range and read 0.
 // ----------------------------------------------------------------------------
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor: base, no stride, `bytes` in range (raw-buffer bounds
+// check on the per-lane offset), default data format.
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = int(uint32_t(a));
+  r.y = int(uint32_t(a >> 32) & 0xFFFFu);
+  r.z = int(bytes);
+  r.w = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return uint32_t(reinterpret_cast<uintptr_t>(p));
+}
+
+// 16 B per lane from base(rsrc) + soff + voff into LDS at m0 + 16 * lane.
+// Issued through inline asm so that the compiler does not add its own
+// whole-queue waits; completion is tracked with wait_and_barrier.
+__device__ __forceinline__ i32x4 uniform(i32x4 r) {
+  r.x = __builtin_amdgcn_readfirstlane(r.x);
+  r.y = __builtin_amdgcn_readfirstlane(r.y);
+  r.z = __builtin_amdgcn_readfirstlane(r.z);
+  r.w = __builtin_amdgcn_readfirstlane(r.w);
+  return r;
+}
+
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_wave_dst, int voff, int soff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_wave_dst);
+  const i32x4 rs = uniform(rsrc);
+  const int so = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(rs), "s"(so)
+               : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are pending,
+// then a workgroup barrier (no other memory fence).
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint4 lds16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// ----------------------------------------------------------------------------
+// skinny launch (rows <= 64): 4 wavefronts, each WV x 32 weight rows against
+// all rows (TB blocks of 32).  K steps of 64 (128 B per weight row) land in a
+// 3-stage LDS ring by DMA: weights [NR rows][128 B] and the activation hi and
+// lo planes [TB*32 rows][128 B], row-XOR-swizzled (16-B chunk c of row R at
+// slot c ^ (R & 7)).  Two fp16 MFMAs per product (activation hi + lo).
+// ----------------------------------------------------------------------------
+
+constexpr int kSkST = 3;
+
+template <int TB, int WV>
+constexpr int skinny_stage_bytes() {
+  return 4 * WV * 32 * 128 + 2 * TB * 32 * 128;
+}
 
 template <int TB, int WV, bool STATS>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
+  constexpr int NR = 4 * WV * 32;            // weight rows per workgroup
+  constexpr int WST = NR * 128;              // weight bytes per stage
+  constexpr int AST = TB * 32 * 128;         // activation bytes per plane per stage
+  constexpr int SST = WST + 2 * AST;
+  constexpr int WI = NR / 8 / 4;             // weight DMA instructions per wave per stage
+  constexpr int AI = 2 * TB * 32 / 8 / 4;    // activation DMA instructions per wave per stage
+  constexpr int PER = WI + AI;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r32 = lane & 31, kg = lane >> 5;
-  constexpr int WG_N = 4 * WV * 32;
-  const int n_wave = blockIdx.x * WG_N + w * WV * 32;
+  const int n0 = blockIdx.x * NR;
   const int ks = blockIdx.y * g.k_split;
-  const int ke = min(g.K, ks + g.k_split);
+  const int nk = (min(g.K, ks + g.k_split) - ks) / 64;
+  const int Kb = g.K * 2;
+  const i32x4 rw = make_rsrc(g.W + int64_t(n0) * g.K, uint32_t(min(NR, g.N - n0)) * Kb);
+  const i32x4 rah = make_rsrc(g.act, uint32_t(g.rows) * Kb);
+  const i32x4 ral = make_rsrc(g.act_lo, uint32_t(g.rows) * Kb);
+  const uint32_t lds0 = lds_addr(smem);
+  const int c8 = lane & 7;
+  int woff[WI], aoff[AI];
+#pragma unroll
+  for (int i = 0; i < WI; ++i) {
+    const int R = (w * WI + i) * 8 + (lane >> 3);
+    woff[i] = R * Kb + ((c8 ^ (R & 7)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int ia = w * AI + i;                        // over [0, 2 * TB * 4)
+    const int R = (ia % (TB * 4)) * 8 + (lane >> 3);
+    aoff[i] = R * Kb + ((c8 ^ (R & 7)) << 4);
+  }
+  auto issue = [&](int s) {
+    const uint32_t base = lds0 + (s % kSkST) * SST;
+    const int soff = (ks + s * 64) * 2;
+#pragma unroll
+    for (int i = 0; i < WI; ++i) dma16(rw, base + (w * WI + i) * 1024, woff[i], soff);
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      const int ia = w * AI + i;
+      const int plane = ia / (TB * 4);
+      dma16(plane ? ral : rah, base + WST + plane * AST + (ia % (TB * 4)) * 1024, aoff[i], soff);
+    }
+  };
 
-  const uint16_t *wp[WV];
-#pragma unroll
-  for (int v = 0; v < WV; ++v) {
-    const int n = min(n_wave + v * 32 + r32, g.N - 1);
-    wp[v] = g.W + int64_t(n) * g.K + kg * 32;
-  }
-  const uint16_t *ap[TB];
-#pragma unroll
-  for (int t = 0; t < TB; ++t) {
-    const int row = min(t * 32 + r32, g.rows - 1);
-    ap[t] = g.act + int64_t(row) * g.K + kg * 32;
-  }
-  const int64_t lo_off = g.act_lo - g.act;
   f32x16 acc[WV][TB];
 #pragma unroll
   for (int v = 0; v < WV; ++v)
@@ -127,46 +224,46 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[v][t][j] = 0.f;
 
-  uint4 wa[WV][4], wb[WV][4];
-  auto load_w = [&](uint4 (&dst)[WV][4], int k) {
+  auto compute = [&](int s) {
+    const uint8_t *base = smem + (s % kSkST) * SST;
 #pragma unroll
-    for (int v = 0; v < WV; ++v)
+    for (int j = 0; j < 4; ++j) {
+      const int q = j * 2 + kg;
+      uint4 af[WV], bh[TB], bl[TB];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dst[v][j] = ld_nt16(wp[v] + k + 8 * j);
-  };
-  auto compute = [&](const uint4 (&src)[WV][4], int k) {
-    uint4 bh[TB][4], bl[TB][4];
-#pragma unroll
-    for (int t = 0; t < TB; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bh[t][j] = reinterpret_cast<const uint4 *>(ap[t] + k)[j];
-        bl[t][j] = reinterpret_cast<const uint4 *>(ap[t] + lo_off + k)[j];
+      for (int v = 0; v < WV; ++v) {
+        const int R = w * WV * 32 + v * 32 + r32;
+        af[v] = lds16(base + R * 128 + ((q ^ (R & 7)) << 4));
       }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int t = 0; t < TB; ++t) {
+        const int R = t * 32 + r32;
+        bh[t] = lds16(base + WST + R * 128 + ((q ^ (R & 7)) << 4));
+        bl[t] = lds16(base + WST + AST + R * 128 + ((q ^ (R & 7)) << 4));
+      }
 #pragma unroll
       for (int v = 0; v < WV; ++v)
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
-          acc[v][t] = mfma32(src[v][j], bh[t][j], acc[v][t]);
-          acc[v][t] = mfma32(src[v][j], bl[t][j], acc[v][t]);
+          acc[v][t] = mfma32h(af[v], bh[t], acc[v][t]);
+          acc[v][t] = mfma32h(af[v], bl[t], acc[v][t]);
         }
+    }
   };
 
-  if (ks < ke) load_w(wa, ks);
-  for (int k = ks; k < ke; k += 128) {
-    if (k + 64 < ke) load_w(wb, k + 64);
-    compute(wa, k);
-    if (k + 64 < ke) {
-      if (k + 128 < ke) load_w(wa, k + 128);
-      compute(wb, k + 64);
-    }
+#pragma unroll
+  for (int p = 0; p < kSkST - 1; ++p)
+    if (p < nk) issue(p);
+  for (int s = 0; s < nk; ++s) {
+    // stage s landed (this wave's part, then everyone's); stage s-1's buffer is free
+    if (s + 1 < nk) wait_and_barrier<PER>(); else wait_and_barrier<0>();
+    if (s + kSkST - 1 < nk) issue(s + kSkST - 1);
+    compute(s);
   }
 
   int nb[WV], tb[TB];
 #pragma unroll
-  for (int v = 0; v < WV; ++v) nb[v] = n_wave + v * 32;
+  for (int v = 0; v < WV; ++v) nb[v] = n0 + w * WV * 32 + v * 32;
 #pragma unroll
   for (int t = 0; t < TB; ++t) tb[t] = t * 32;
   GemmArgs go = g;
@@ -174,17 +271,18 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
   store_tile<WV, TB>(go, acc, nb, tb, lane);
 
   if constexpr (STATS) {
-    __shared__ MaxSumArg red[4][TB * 32];
+    __syncthreads();
+    MaxSumArg *red = reinterpret_cast<MaxSumArg *>(smem);   // [4][TB * 32]
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
       const MaxSumArg r = lane_stats<WV, TB>(g, acc, nb, t, lane);
-      if (kg == 0) red[w][t * 32 + r32] = r;
+      if (kg == 0) red[w * TB * 32 + t * 32 + r32] = r;
     }
     __syncthreads();
     if (tid < TB * 32 && tid < g.rows) {
-      MaxSumArg r = red[0][tid];
+      MaxSumArg r = red[tid];
 #pragma unroll
-      for (int ww = 1; ww < 4; ++ww) r = msa_merge(r, red[ww][tid]);
+      for (int ww = 1; ww < 4; ++ww) r = msa_merge(r, red[ww * TB * 32 + tid]);
       const int64_t o = int64_t(tid) * g.n_tiles + blockIdx.x;
       g.t_max[o] = r.m;
       g.t_sum[o] = r.s;
@@ -194,138 +292,249 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 }
 
 // ----------------------------------------------------------------------------
-// tiled launch: 256 (N) x 256 (rows) per workgroup, 8 wavefronts as 2 x 4,
-// each 128 (N) x 64 (rows) = 4 x 2 MFMA blocks.
+// tiled launch (rows > 64), persistent: each workgroup walks output tiles of
+// 256 (N) x 256 (rows).  8 wavefronts as 2 x 4, each 128 (N) x 64 (rows) =
+// 4 x 2 fp16 32x32x16 MFMA blocks.  K steps of 32 (64 B per row) land in a
+// 4-stage LDS ring by DMA (weights 256 rows, then activations 256 rows; 16-B
+// chunk c of row R at slot c ^ ((R >> 2) & 3)), three steps ahead of the
+// MFMAs.  When a tile's K loop ends, the epilogue (per-row max / sumexp /
+// argmax of the tile, logit stores) is issued and the first stages of the
+// workgroup's next tile follow at once, so the stores drain while those
+// loads are in flight.  Tile order: tiles i and i+8 share the weight
+// tile (with two row tiles) and are taken at the same time by workgroups on
+// the same XCD, so one of the two weight reads hits that XCD's L2.
 // ----------------------------------------------------------------------------
 
-constexpr int kTBN = 256, kTBT = 256, kTKS = 64, kTROW = kTKS + 8;
+constexpr int kTBN = 256, kTBT = 256, kTST = 4, kTSST = (kTBN + kTBT) * 64;
+constexpr size_t kTiledLds = size_t(kTST) * kTSST;
 
 template <bool STATS>
 __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  uint16_t *w_lds = lds;                         // [2][kTBN * kTROW]
-  uint16_t *a_lds = lds + 2 * kTBN * kTROW;      // [2][kTBT * kTROW]
+  constexpr int PER = 4;     // DMA instructions per wave per stage (2 weight + 2 activation)
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r32 = lane & 31, kg = lane >> 5;
   const int wn = w & 1, wt = w >> 1;
-  const int n0 = blockIdx.x * kTBN;
-  const int t0 = blockIdx.y * kTBT;
-  const int K = g.K;
-
-  // global -> register staging: 4 W chunks + 4 act chunks of 16 B per thread
-  const uint16_t *wsrc[4];
-  const uint16_t *asrc[4];
-  int ldst[4];
+  const int n_ttiles = (g.rows + kTBT - 1) / kTBT;
+  const int n_ntiles = (g.N + kTBN - 1) / kTBN;
+  const int n_tiles_all = ((n_ntiles + 7) / 8) * 8 * n_ttiles;
+  const int ks = blockIdx.y * g.k_split;
+  const int nk = (min(g.K, ks + g.k_split) - ks) / 32;
+  const int Kb = g.K * 2;
+  const uint32_t lds0 = lds_addr(smem);
+  const int c4 = lane & 3;
+  int off[2];     // 2 instructions of 16 rows: rows w*32 + 16 i + lane/4 (weights and activations alike)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = tid + 512 * j;
-    const int row = c >> 3, col = c & 7;
-    wsrc[j] = g.W + int64_t(min(n0 + row, g.N - 1)) * K + col * 8;
-    asrc[j] = g.act + int64_t(min(t0 + row, g.rows - 1)) * K + col * 8;
-    ldst[j] = row * kTROW + col * 8;
+  for (int i = 0; i < 2; ++i) {
+    const int R = w * 32 + i * 16 + (lane >> 2);
+    off[i] = R * Kb + ((c4 ^ ((R >> 2) & 3)) << 4);
   }
-  uint4 wr[4], ar[4];
-  auto load = [&](int k) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      wr[j] = ld_nt16(wsrc[j] + k);
-      ar[j] = *reinterpret_cast<const uint4 *>(asrc[j] + k);
-    }
+  // tile i -> (weight tile, row tile); i and i+8 share the weight tile
+  auto tile_of = [&](int i, int &n_tile, int &t_tile) {
+    const int grp = i / (8 * n_ttiles), rem = i % (8 * n_ttiles);
+    n_tile = grp * 8 + rem % 8;
+    t_tile = rem / 8;
   };
-  auto store = [&](int b) {
+  struct Src {
+    i32x4 rw, ra;
+  };
+  auto src_of = [&](int n_tile, int t_tile) {
+    const int n0 = n_tile * kTBN, t0 = t_tile * kTBT;
+    Src r;
+    r.rw = make_rsrc(g.W + int64_t(n0) * g.K, uint32_t(min(kTBN, g.N - n0)) * Kb);
+    r.ra = make_rsrc(g.act + int64_t(t0) * g.K, uint32_t(min(kTBT, g.rows - t0)) * Kb);
+    return r;
+  };
+  auto issue = [&](const Src &sr, int s) {
+    const uint32_t base = lds0 + (s % kTST) * kTSST;
+    const int soff = (ks + s * 32) * 2;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<uint4 *>(w_lds + b * kTBN * kTROW + ldst[j]) = bf8_to_h8(wr[j]);
-      *reinterpret_cast<uint4 *>(a_lds + b * kTBT * kTROW + ldst[j]) = ar[j];
-    }
+    for (int i = 0; i < 2; ++i) dma16(sr.rw, base + (w * 32 + i * 16) * 64, off[i], soff);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(sr.ra, base + kTBN * 64 + (w * 32 + i * 16) * 64, off[i], soff);
   };
 
-  f32x16 acc[4][2];
+  int tile = blockIdx.x;
+  // skip tiles past the weight rows (grid rounding)
+  auto valid = [&](int i) {
+    if (i >= n_tiles_all) return false;
+    int a, b;
+    tile_of(i, a, b);
+    return a < n_ntiles;
+  };
+  while (tile < n_tiles_all && !valid(tile)) tile += gridDim.x;
+  if (tile >= n_tiles_all) return;      // whole workgroup, before any barrier
+  int n_tile, t_tile;
+  tile_of(tile, n_tile, t_tile);
+  Src cur = src_of(n_tile, t_tile);
 #pragma unroll
-  for (int v = 0; v < 4; ++v)
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[v][t][j] = 0.f;
+  for (int p = 0; p < kTST - 1; ++p)
+    if (p < nk) issue(cur, p);
 
-  const int nk = K / kTKS;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int s = 0; s < nk; ++s) {
-    const int b = s & 1;
-    if (s + 1 < nk) load((s + 1) * kTKS);
-    const uint16_t *wl = w_lds + b * kTBN * kTROW + (wn * 128 + r32) * kTROW + kg * 8;
-    const uint16_t *al = a_lds + b * kTBT * kTROW + (wt * 64 + r32) * kTROW + kg * 8;
+  for (;;) {
+    f32x16 acc[4][2];
 #pragma unroll
-    for (int kk = 0; kk < kTKS / 16; ++kk) {
-      uint4 af[4], bf[2];
+    for (int v = 0; v < 4; ++v)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) af[v] = *reinterpret_cast<const uint4 *>(wl + v * 32 * kTROW + kk * 16);
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) bf[t] = *reinterpret_cast<const uint4 *>(al + t * 32 * kTROW + kk * 16);
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) acc[v][t] = mfma32h(af[v], bf[t], acc[v][t]);
-    }
-    if (s + 1 < nk) store(b ^ 1);
-    __syncthreads();
-  }
+        for (int j = 0; j < 16; ++j) acc[v][t][j] = 0.f;
 
-  int nb[4], tb[2];
+    for (int s = 0; s < nk; ++s) {
+      const int younger = min(kTST - 2, nk - 1 - s);
+      if (younger >= 2)
+        wait_and_barrier<2 * PER>();
+      else if (younger == 1)
+        wait_and_barrier<PER>();
+      else
+        wait_and_barrier<0>();
+      if (s + kTST - 1 < nk) issue(cur, s + kTST - 1);
+      const uint8_t *base = smem + (s % kTST) * kTSST;
+      uint4 af[2][4], bf[2][2];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) nb[v] = n0 + wn * 128 + v * 32;
+      for (int j = 0; j < 2; ++j) {
+        const int q = j * 2 + kg;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) tb[t] = t0 + wt * 64 + t * 32;
-  store_tile<4, 2>(g, acc, nb, tb, lane);
+        for (int v = 0; v < 4; ++v) {
+          const int R = wn * 128 + v * 32 + r32;
+          af[j][v] = lds16(base + R * 64 + ((q ^ ((R >> 2) & 3)) << 4));
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int R = wt * 64 + t * 32 + r32;
+          bf[j][t] = lds16(base + kTBN * 64 + R * 64 + ((q ^ ((R >> 2) & 3)) << 4));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) acc[v][t] = mfma32h(af[j][v], bf[j][t], acc[v][t]);
+    }
 
-  if constexpr (STATS) {
-    MaxSumArg *red = reinterpret_cast<MaxSumArg *>(lds);   // [2][kTBT]; LDS free after the loop
+    // epilogue of this tile (vector-memory waits count stores too, so the
+    // next tile's loads are issued only after the stores)
+    asm volatile("s_barrier" ::: "memory");   // every wave is done reading the ring
+    const int n0 = n_tile * kTBN, t0 = t_tile * kTBT;
+    int nb[4], tb[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const MaxSumArg r = lane_stats<4, 2>(g, acc, nb, t, lane);
-      if (kg == 0) red[wn * kTBT + wt * 64 + t * 32 + r32] = r;
+    for (int v = 0; v < 4; ++v) nb[v] = n0 + wn * 128 + v * 32;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) tb[t] = t0 + wt * 64 + t * 32;
+    GemmArgs go = g;
+    go.out = g.out + int64_t(blockIdx.y) * g.split_stride;
+    if constexpr (STATS) {
+      // (max, sumexp, argmax) per row over this wave's 128 N, then across
+      // the two N halves through a small static LDS array
+      __shared__ MaxSumArg red[2][kTBT];
+      if (n0 + kTBN > g.N) {
+        // last tile: columns past N (zero weights) must not take part
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              if (nb[v] + 8 * (j >> 2) + 4 * kg + (j & 3) >= g.N) acc[v][t][j] = -INFINITY;
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const MaxSumArg r = lane_stats<4, 2, false>(g, acc, nb, t, lane);
+        if (kg == 0) red[wn][wt * 64 + t * 32 + r32] = r;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (tid < kTBT && t0 + tid < g.rows) {
+        const MaxSumArg r = msa_merge(red[0][tid], red[1][tid]);
+        const int64_t o = int64_t(t0 + tid) * g.n_tiles + n_tile;
+        g.t_max[o] = r.m;
+        g.t_sum[o] = r.s;
+        g.t_arg[o] = r.i;
+      }
     }
-    __syncthreads();
-    if (tid < kTBT && t0 + tid < g.rows) {
-      const MaxSumArg r = msa_merge(red[tid], red[kTBT + tid]);
-      const int64_t o = int64_t(t0 + tid) * g.n_tiles + blockIdx.x;
-      g.t_max[o] = r.m;
-      g.t_sum[o] = r.s;
-      g.t_arg[o] = r.i;
+    store_tile<4, 2>(go, acc, nb, tb, lane);
+
+    int next = tile + gridDim.x;
+    while (next < n_tiles_all && !valid(next)) next += gridDim.x;
+    const bool more = next < n_tiles_all;
+    int nn_tile = 0, nt_tile = 0;
+    Src nsrc = cur;
+    if (more) {
+      tile_of(next, nn_tile, nt_tile);
+      nsrc = src_of(nn_tile, nt_tile);
+#pragma unroll
+      for (int p = 0; p < kTST - 1; ++p)
+        if (p < nk) issue(nsrc, p);
     }
+    if (!more) break;
+    tile = next;
+    n_tile = nn_tile;
+    t_tile = nt_tile;
+    cur = nsrc;
   }
 }
 
-constexpr size_t kTiledLds = size_t(2) * (kTBN + kTBT) * kTROW * sizeof(uint16_t);
-
 int lm_tile_width(int rows) { return rows <= 64 ? 4 * 2 * 32 : kTBN; }
+
+// Split-K factor of a projection with `rows` rows: enough workgroups to
+// cover the chip, K pieces of at least 256.
+int gemm_splits(int rows, int N, int K, int n_cu, int *k_split) {
+  int tiles;
+  if (rows <= 64)
+    tiles = (N + 127) / 128;
+  else
+    tiles = ((N + kTBN - 1) / kTBN) * ((rows + kTBT - 1) / kTBT);
+  int s = (2 * n_cu + tiles - 1) / tiles;
+  if (rows > 64) s = (n_cu + tiles - 1) / tiles;
+  s = max(1, min(s, K / 256));
+  const int ks = ((K + s - 1) / s + 63) / 64 * 64;
+  *k_split = ks;
+  return (K + ks - 1) / ks;
+}
+
+template <int TB, int WV, bool ST>
+static void launch_skinny(const GemmArgs &g, int splits, hipStream_t s) {
+  constexpr size_t lds = size_t(kSkST) * skinny_stage_bytes<TB, WV>();
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_skinny_kernel<TB, WV, ST>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    attr = true;
+  }
+  const dim3 grid((g.N + 4 * WV * 32 - 1) / (4 * WV * 32), splits);
+  hipLaunchKernelGGL((gemm_skinny_kernel<TB, WV, ST>), grid, dim3(256), lds, s, g);
+}
 
 void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s) {
   if (g.rows <= 64) {
-    // WV = 2 for the LM head (256 N rows per workgroup), 1 for split-K W_o
-    const int wv = stats ? 2 : 1;
-    const dim3 grid((g.N + 4 * wv * 32 - 1) / (4 * wv * 32), splits);
-#define SV_SK(TB, WV, ST) hipLaunchKernelGGL((gemm_skinny_kernel<TB, WV, ST>), grid, dim3(256), 0, s, g)
+    // WV = 2 for the LM head (256 weight rows per workgroup), 1 for split-K W_o
     if (g.rows <= 32) {
-      if (stats) SV_SK(1, 2, true); else SV_SK(1, 1, false);
+      if (stats) launch_skinny<1, 2, true>(g, splits, s); else launch_skinny<1, 1, false>(g, splits, s);
     } else {
-      if (stats) SV_SK(2, 2, true); else SV_SK(2, 1, false);
+      if (stats) launch_skinny<2, 2, true>(g, splits, s); else launch_skinny<2, 1, false>(g, splits, s);
     }
-#undef SV_SK
     return;
   }
   static bool attr_set = false;
+  static int n_cu = 256;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_tiled_kernel<true>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, int(kTiledLds));
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_tiled_kernel<false>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, int(kTiledLds));
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess) {
+      int cu = 0;
+      if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cu > 0) n_cu = cu;
+    }
     attr_set = true;
   }
-  const dim3 grid((g.N + kTBN - 1) / kTBN, (g.rows + kTBT - 1) / kTBT);
-  // split-K is not used with the tiled launch
+  // one workgroup per CU (LDS), a multiple of 16 so that tiles i and i+8 go
+  // to co-resident workgroups of one XCD
+  const int n_ntiles = (g.N + kTBN - 1) / kTBN, n_ttiles = (g.rows + kTBT - 1) / kTBT;
+  const int tiles = ((n_ntiles + 7) / 8) * 8 * n_ttiles;
+  const int grid_x = std::min(tiles, std::max(16, n_cu / 16 * 16));
+  const dim3 grid(grid_x, splits);
   if (stats)
     hipLaunchKernelGGL(gemm_tiled_kernel<true>, grid, dim3(512), kTiledLds, s, g);
   else
@@ -382,30 +591,49 @@ void launch_stats_from_logits(const float *logits, int rows, int V, int tile, fl
 // final RMS norm (unit gain) over the summed split-K partials of W_o
 // ----------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void norm_kernel(const float *part, int splits, int64_t split_stride, int hidden,
-                                                   float eps, int mode, void *out, int64_t lo_off) {
+// One workgroup of 1024 threads per row: each thread sums the split-K
+// partials of 4 columns (16-B loads, splits unrolled by 4), keeps h in LDS,
+// then scales.
+__global__ __launch_bounds__(1024) void norm_kernel(const float *part, int splits, int64_t split_stride, int hidden,
+                                                    float eps, int mode, void *out, int64_t lo_off) {
+  extern __shared__ float hrow[];     // [hidden]
   const int row = blockIdx.x, tid = threadIdx.x;
   const float *p = part + int64_t(row) * hidden;
   float ss = 0.f;
-  for (int c = tid; c < hidden; c += 256) {
-    float h = 0.f;
-    for (int s = 0; s < splits; ++s) h += p[s * split_stride + c];
-    ss = fmaf(h, h, ss);
+  for (int c = tid * 4; c < hidden; c += 1024 * 4) {
+    f32x4 h4 = {0.f, 0.f, 0.f, 0.f};
+    int s = 0;
+    for (; s + 4 <= splits; s += 4) {
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(p + (s + 0) * split_stride + c);
+      const f32x4 b = *reinterpret_cast<const f32x4 *>(p + (s + 1) * split_stride + c);
+      const f32x4 d = *reinterpret_cast<const f32x4 *>(p + (s + 2) * split_stride + c);
+      const f32x4 e = *reinterpret_cast<const f32x4 *>(p + (s + 3) * split_stride + c);
+      h4 = h4 + a;
+      h4 = h4 + b;
+      h4 = h4 + d;
+      h4 = h4 + e;
+    }
+    for (; s < splits; ++s) h4 = h4 + *reinterpret_cast<const f32x4 *>(p + s * split_stride + c);
+    *reinterpret_cast<f32x4 *>(hrow + c) = h4;
+    ss = fmaf(h4[0], h4[0], ss);
+    ss = fmaf(h4[1], h4[1], ss);
+    ss = fmaf(h4[2], h4[2], ss);
+    ss = fmaf(h4[3], h4[3], ss);
   }
   ss = wave_sum(ss);
-  __shared__ float red[4];
+  __shared__ float red[16];
   if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
-  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) tot += red[i];
   const float inv = 1.0f / sqrtf(tot / float(hidden) + eps);
-  for (int c = tid; c < hidden; c += 256) {
-    float h = 0.f;
-    for (int s = 0; s < splits; ++s) h += p[s * split_stride + c];
-    const float y = h * inv;
+  for (int c = tid; c < hidden; c += 1024) {
+    const float y = hrow[c] * inv;
     const int64_t idx = int64_t(row) * hidden + c;
     if (mode == ACT_SPLIT) {
       uint16_t hi, lo;
-      split_bf(y, hi, lo);
+      split_h(y, hi, lo);
       static_cast<uint16_t *>(out)[idx] = hi;
       static_cast<uint16_t *>(out)[lo_off + idx] = lo;
     } else if (mode == ACT_F16) {
@@ -418,8 +646,38 @@ __global__ __launch_bounds__(256) void norm_kernel(const float *part, int splits
 
 void launch_norm(const float *part, int splits, int64_t split_stride, int rows, int hidden, float eps, int mode,
                  void *out, int64_t lo_off, hipStream_t s) {
-  hipLaunchKernelGGL(norm_kernel, dim3(rows), dim3(256), 0, s, part, splits, split_stride, hidden, eps, mode, out,
-                     lo_off);
+  hipLaunchKernelGGL(norm_kernel, dim3(rows), dim3(1024), size_t(hidden) * 4, s, part, splits, split_stride, hidden,
+                     eps, mode, out, lo_off);
+}
+
+
+// ----------------------------------------------------------------------------
+// weight preparation (once, at handle creation): bf16 -> fp16.  Exact for
+// values in the fp16 normal range; tiny values become fp16 subnormals.
+// Counts values outside the fp16 range (they would become infinities).
+// ----------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint16_t *__restrict__ src, uint16_t *__restrict__ dst,
+                                                         int64_t n8, int32_t *__restrict__ bad) {
+  int local_bad = 0;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n8; i += int64_t(gridDim.x) * 256) {
+    const uint4 v = reinterpret_cast<const uint4 *>(src)[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float lo = __uint_as_float(w[k] << 16), hi = __uint_as_float(w[k] & 0xFFFF0000u);
+      local_bad += (fabsf(lo) > 65504.f) + (fabsf(hi) > 65504.f);
+    }
+    reinterpret_cast<uint4 *>(dst)[i] = bf8_to_h8(v);
+  }
+  if (local_bad) atomicAdd(bad, local_bad);
+}
+
+void launch_bf16_to_f16(const uint16_t *src, uint16_t *dst, int64_t n, int32_t *bad, hipStream_t s) {
+  const int64_t n8 = n / 8;
+  const int64_t blocks = std::min<int64_t>((n8 + 255) / 256, 8192);
+  hipLaunchKernelGGL(bf16_to_f16_kernel, dim3(unsigned(std::max<int64_t>(blocks, 1))), dim3(256), 0, s, src, dst, n8,
+                     bad);
 }
 
 }  // namespace sv

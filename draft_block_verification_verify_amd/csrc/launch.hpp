@@ -8,7 +8,8 @@
 
 namespace sv {
 
-// Formats of the projections' small (activation) operand.
+// Formats of the projections' small (activation) operand: ACT_SPLIT = fp16
+// hi plane + fp16 lo plane (hi + lo = value to ~22 bits), ACT_F16, ACT_F32.
 enum ActMode : int { ACT_SPLIT = 0, ACT_F16 = 1, ACT_F32 = 2 };
 
 struct AttnArgs {
@@ -44,13 +45,13 @@ struct AttnF32Args {
   int Hq, Hkv, D;
 };
 
-// out[rows, N] = act[rows, K] . W[N, K]^T (fp32 accumulation).  rows <= 64:
-// act is a bf16 hi + lo pair (ACT_SPLIT); rows > 64: act is fp16 (ACT_F16).
+// out[rows, N] = act[rows, K] . W[N, K]^T, W in fp16, fp32 accumulation.
+// rows <= 64: act is an fp16 hi + lo pair (ACT_SPLIT); rows > 64: fp16.
 // Split-K (grid.y) writes out + split * split_stride.  With stats, each
 // workgroup also writes (max, sum exp(x - max), argmax) of its N tile per row.
 struct GemmArgs {
-  const uint16_t *act;             // skinny: bf16 hi plane; tiled: fp16
-  const uint16_t *act_lo;          // skinny: bf16 lo plane
+  const uint16_t *act;             // skinny: fp16 hi plane; tiled: fp16
+  const uint16_t *act_lo;          // skinny: fp16 lo plane
 
   int rows;
   const uint16_t *W;
@@ -75,6 +76,8 @@ void launch_attn_f32(const AttnF32Args &a, int n_rows, hipStream_t s);
 // ---- projections ----
 // Tile width (N columns per stats record) of the LM-head launch chosen for `rows`.
 int lm_tile_width(int rows);
+// Split-K factor (and K per split, a multiple of 64) of a projection launch.
+int gemm_splits(int rows, int N, int K, int n_cu, int *k_split);
 void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s);
 void launch_gemm_f32(const float *act, int rows, const float *W, int N, int K, float *out, hipStream_t s);
 void launch_stats_from_logits(const float *logits, int rows, int V, int tile, float *t_max, float *t_sum,
@@ -83,6 +86,10 @@ void launch_stats_from_logits(const float *logits, int rows, int V, int tile, fl
 // plane at out + lo_off; ACT_F16; ACT_F32).
 void launch_norm(const float *part, int splits, int64_t split_stride, int rows, int hidden, float eps, int mode,
                  void *out, int64_t lo_off, hipStream_t s);
+
+// bf16 -> fp16 copy of n values (n % 8 == 0); adds the count of values
+// outside the fp16 range to *bad (device int).
+void launch_bf16_to_f16(const uint16_t *src, uint16_t *dst, int64_t n, int32_t *bad, hipStream_t s);
 
 // ---- vocabulary reductions and acceptance ----
 struct VocabArgs {

@@ -103,10 +103,14 @@ typedef struct sv_outputs {
 } sv_outputs;
 
 /* Create a handle on the current device.  w_o is DEVICE [hidden, Hq*d] and
- * w_lm is DEVICE [vocab, hidden], both row-major in cfg->dtype; they are
- * borrowed (not copied) for the handle's lifetime.  Allocates the handle's
- * device scratch (sized from the capacities) and pinned host staging.
- * Fails with SV_ERR_UNSUPPORTED unless the device is gfx950. */
+ * w_lm is DEVICE [vocab, hidden], both row-major in cfg->dtype.  For SV_BF16
+ * the handle converts them once into fp16 copies it owns (exact for bf16
+ * values of magnitude up to 65504; larger weights fail with
+ * SV_ERR_UNSUPPORTED) and the caller's buffers are not used afterwards; for
+ * SV_F32 they are borrowed for the handle's lifetime.  Allocates the handle's
+ * device scratch (sized from the capacities) and pinned host staging;
+ * synchronises the device.  Fails with SV_ERR_UNSUPPORTED unless the device
+ * is gfx950. */
 sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *w_lm,
                              sv_handle **out);
 
