@@ -138,7 +138,7 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
   h->w_lm = w_lm;
   h->device = dev;
   h->n_cu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
-  h->target_items = 4 * h->n_cu;
+  h->target_items = 8 * h->n_cu;
   h->elt = dm.dtype == SV_BF16 ? 2 : 4;
 
   const int64_t R = dm.max_rows, Hq = dm.Hq, Hkv = dm.Hkv, D = dm.d, H = dm.hidden, V = dm.vocab;

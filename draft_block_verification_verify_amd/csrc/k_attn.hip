@@ -7,9 +7,9 @@
 // bf16 path: split-KV flash-decode.  A work item is (tree, KV head, query
 // group, key range); its query vectors are the tree's (row, head-in-group)
 // pairs, so one K/V tile streamed from HBM serves every row and every query
-// head of the GQA group.  K/V tiles of 32 keys are staged through LDS (V
-// transposed on the way in), S^T = K.Q^T and O^T += V^T.P^T run on
-// 16x16x32 bf16 MFMA, the online softmax is per wavefront in fp32 (log2
+// head of the GQA group.  K/V tiles reach LDS by DMA in their natural layout,
+// V^T fragments come from transposing LDS reads, S^T = K.Q^T and
+// O^T += V^T.P^T run on 16x16x32 bf16 MFMA, the online softmax is per wavefront in fp32 (log2
 // domain).  The rotated queries and the probabilities are each carried as a
 // bf16 pair hi + lo (two MFMAs per product), so the only bf16 rounding left
 // in the scores is the one of the cached keys themselves.  Each item leaves
@@ -18,6 +18,7 @@
 //
 // fp32 path: one workgroup per (row, query head), plain fp32 arithmetic.
 #include "k_common.hpp"
+#include "k_dma.hpp"
 #include "launch.hpp"
 
 namespace sv {
@@ -88,22 +89,73 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(const T *__restrict__ q,
 
 // ----------------------------------------------------------------------------
 // bf16 split-KV attention on MFMA
+//
+// A work item walks tiles of KT = 8192 / D keys (16 KB of K plus 16 KB of V)
+// through a 4-stage LDS ring filled by direct global -> LDS DMA, three tiles
+// ahead of the one being used.  A tile holds its keys in natural [key][d]
+// layout; 16-B chunk c of tile row r sits at chunk c ^ swz(r), which keeps
+// both the K fragment reads (16 rows, one chunk) and the transposing V reads
+// (4 rows x 32 B per 16 lanes) free of bank conflicts.  Wavefront w owns
+// query block w (16 query vectors); every wavefront issues its share of the
+// DMA.  Prefix tiles come from the KV cache, row tiles from the rotated row
+// keys and the row values; each DMA is range-checked against the tree's own
+// keys, so padding rows read as zeros and are masked.
 // ----------------------------------------------------------------------------
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
-  constexpr int NT = 64 * NW;     // threads
-  constexpr int KT = 32;          // keys per LDS tile
-  constexpr int KROW = D + 8;     // bf16 per LDS K row (16 B pad: conflict-free b128 reads)
-  constexpr int VROW = KT + 4;    // bf16 per LDS V^T row (72 B)
-  constexpr int DS = D / 32;      // 32-wide d steps of S = K.Q^T
+template <int D>
+struct AttnTile {
+  static constexpr int KT = attn_key_tile(D);   // keys per tile
+  static constexpr int ROWB = D * 2;            // bytes per key row
+  static constexpr int TILEB = KT * ROWB;       // 16 KB
+  static constexpr int CH = D / 8;              // 16-B chunks per row
+  static constexpr int RPI = 1024 / ROWB;       // rows per wave DMA instruction
+  static constexpr int NI = TILEB / 1024;       // DMA instructions per K (or V) tile
+};
+template <int D, int STG>
+constexpr size_t attn_lds_bytes() { return size_t(STG) * 2 * AttnTile<D>::TILEB; }
+
+// LDS chunk slot of logical 16-B chunk c in tile row r.  D >= 128: any 16
+// aligned consecutive rows get 16 distinct slots (and any 8 rows distinct
+// slots mod 8), any 8 aligned rows get 8 distinct chunk pairs; D = 64 (8
+// chunks per row): 8 rows distinct, 4 aligned rows distinct pairs.
+template <int D>
+__device__ __forceinline__ int swz_chunk(int r, int c) {
+  if constexpr (D >= 128)
+    return c ^ (((r & 7) << 1) | (((r >> 2) ^ (r >> 3)) & 1));
+  else
+    return c ^ (((r & 3) << 1) | ((r >> 2) & 1));
+}
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane j receives 16-bit element (j & 3) of the 8-byte rows addressed by
+// lanes 4k + (j >> 2), k = 0..3, in that order.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint8_t *p) {
+  typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+  const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4 *)((__attribute__((address_space(3))) uint8_t *)(p)));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// STG: ring stages (tiles in flight = STG - 1); OCC: wavefronts per SIMD the
+// launch is built for (registers per wavefront <= 512 / OCC).
+template <int D, int NW, int STG, int OCC>
+__global__ __launch_bounds__(64 * NW, OCC) void attn_mfma_kernel(AttnArgs a) {
+  using TL = AttnTile<D>;
+  constexpr int KT = TL::KT, ROWB = TL::ROWB, TILEB = TL::TILEB, CH = TL::CH, RPI = TL::RPI;
+  constexpr int DS = D / 32;      // 32-wide d steps of S^T = K.Q^T
   constexpr int DB = D / 16;      // 16-wide d blocks of O^T
-  constexpr int KUN = KT * D / 8;                      // 16-B K chunks per tile
-  constexpr int KCH = (KUN + NT - 1) / NT;
-  constexpr int VUN = (KT / 2) * (D / 8);              // (key pair, 16-B column) units
-  constexpr int VCH = (VUN + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KT * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VROW];
+  constexpr int KB = KT / 16;     // 16-key blocks of S^T
+  constexpr int KP = KT / 32;     // 32-key steps of O^T += V^T.P^T
+  constexpr int PER = 2 * TL::NI / NW;   // DMA instructions per wave per stage
+  // fragments read ahead per group: all of a tile's with one wavefront per
+  // SIMD, half with more
+  constexpr int KSPLIT = OCC > 1 ? 2 : 1;
+  constexpr int VSPLIT = OCC > 1 ? 2 : 1;
+  static_assert(STG >= 2 && STG <= 4, "ring depth");
+  static_assert(PER * NW == 2 * TL::NI && PER % 2 == 0 && 2 * PER < 64, "DMA split");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // [stage][K tile | V tile]
 
   const AttnItem it = a.items[blockIdx.x];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -112,8 +164,9 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
   const int s0 = a.tree_start[r], T = a.tree_rows[r], klen = a.tree_kv_len[r];
   const int64_t koff = a.tree_kv_off[r];
   const int g = it.g, G = a.G, Hkv = a.Hkv, Hq = a.Hq;
-  const int nkeys = klen + T;
-  const int QB = (it.nq + 15) / 16;   // <= NW
+  const int np = (klen + KT - 1) / KT;          // prefix tiles of the tree
+  const int t0 = it.k0 / KT, nt = (it.k1 - it.k0) / KT;
+  const int QB = (it.nq + 15) / 16;             // <= NW
   const bool wave_on = w < QB;
 
   // ---- this wave's query fragments (B operand of S^T = K.Q^T), hi and lo
@@ -135,140 +188,199 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
     }
     anc = a.row_anc[row];
   }
+  // Complete these loads here: the compiler does not see the DMA below, and
+  // would otherwise re-wait for them (with every DMA in flight) in the loop.
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) {
+    asm volatile("" : "+v"(qh[ds].x), "+v"(qh[ds].y), "+v"(qh[ds].z), "+v"(qh[ds].w));
+    asm volatile("" : "+v"(ql[ds].x), "+v"(ql[ds].y), "+v"(ql[ds].z), "+v"(ql[ds].w));
+  }
+  asm volatile("" : "+v"(anc));
+
+  // ---- DMA sources: the tree's prefix of KV head g, and its rows
+  const int64_t key_stride = int64_t(Hkv) * ROWB;            // bytes between keys
+  const int64_t head0 = int64_t(g) * D;
+  const uint32_t pre_bytes = klen > 0 ? uint32_t(int64_t(klen - 1) * key_stride + ROWB) : 0u;
+  const uint32_t row_bytes = uint32_t(int64_t(T - 1) * key_stride + ROWB);
+  const uint16_t *pk = a.kv_k + koff * Hkv * D + head0, *pv = a.kv_v + koff * Hkv * D + head0;
+  const uint16_t *rk = a.k_rot + int64_t(s0) * Hkv * D + head0, *rv = a.v_rows + int64_t(s0) * Hkv * D + head0;
+  // DMA instruction i of this wave covers tile block w + NW * (i % HPER) of
+  // K (i < HPER) or V (i >= HPER); voff_lane is the lane's byte offset from
+  // the tile's first key (tile row, swizzled source chunk)
+  constexpr int HPER = PER / 2;
+  int voff_lane[HPER];
+#pragma unroll
+  for (int i = 0; i < HPER; ++i) {
+    const int row = (w + NW * i) * RPI + lane / CH;
+    voff_lane[i] = int(row * key_stride + 16 * swz_chunk<D>(row, lane % CH));
+  }
+  const uint32_t lds0 = lds_addr(smem);
+  auto issue = [&](int s) {                   // DMA tile t0 + s into stage s % STG
+    const int t = t0 + s;
+    const bool pre = t < np;
+    const int vbase = int(int64_t((pre ? t : t - np) * KT) * key_stride);
+    const i32x4 rsk = make_rsrc(pre ? pk : rk, pre ? pre_bytes : row_bytes);
+    const i32x4 rsv = make_rsrc(pre ? pv : rv, pre ? pre_bytes : row_bytes);
+    const uint32_t sbase = lds0 + uint32_t((s % STG) * 2 * TILEB) + uint32_t(w * 1024);
+#pragma unroll
+    for (int i = 0; i < HPER; ++i) dma16(rsk, sbase + uint32_t(NW * i * 1024), vbase + voff_lane[i], 0);
+#pragma unroll
+    for (int i = 0; i < HPER; ++i) dma16(rsv, sbase + uint32_t(TILEB + NW * i * 1024), vbase + voff_lane[i], 0);
+  };
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- staging registers for one tile
-  uint4 kreg[KCH];
-  uint4 vreg[VCH][2];
-  auto key_src = [&](int v, const uint16_t *pre, const uint16_t *rows) -> const uint16_t * {
-    if (v < klen) return pre + ((koff + v) * Hkv + g) * int64_t(D);
-    if (v < nkeys) return rows + (int64_t(s0 + v - klen) * Hkv + g) * D;
-    return nullptr;
-  };
-  auto load_tile = [&](int kt) {
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int c = tid + NT * j;
-      const int kk = c / (D / 8), col = c % (D / 8);
-      const uint16_t *p = (c < KUN) ? key_src(kt + kk, a.kv_k, a.k_rot) : nullptr;
-      kreg[j] = p ? *reinterpret_cast<const uint4 *>(p + col * 8) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < VCH; ++j) {
-      const int u = tid + NT * j;
-      const int pr = u % (KT / 2), col = u / (KT / 2);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const uint16_t *p = (u < VUN) ? key_src(kt + 2 * pr + e, a.kv_v, a.v_rows) : nullptr;
-        vreg[j][e] = p ? *reinterpret_cast<const uint4 *>(p + col * 8) : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_tile = [&](int b) {
-#pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int c = tid + NT * j;
-      if (c < KUN) {
-        const int kk = c / (D / 8), col = c % (D / 8);
-        *reinterpret_cast<uint4 *>(&k_lds[b][kk * KROW + col * 8]) = kreg[j];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < VCH; ++j) {
-      const int u = tid + NT * j;
-      if (u < VUN) {
-        const int pr = u % (KT / 2), col = u / (KT / 2);
-        const uint32_t *w0 = reinterpret_cast<const uint32_t *>(&vreg[j][0]);
-        const uint32_t *w1 = reinterpret_cast<const uint32_t *>(&vreg[j][1]);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const uint32_t lo = (w0[t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
-          const uint32_t hi = (w1[t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
-          *reinterpret_cast<uint32_t *>(&v_lds[b][(col * 8 + t) * VROW + 2 * pr]) = lo | (hi << 16);
-        }
-      }
-    }
-  };
+  for (int s = 0; s < STG - 1; ++s)
+    if (s < nt) issue(s);
 
-  const int nsub = (it.k1 - it.k0 + KT - 1) / KT;
-  load_tile(it.k0);
-  store_tile(0);
-  __syncthreads();
-  for (int stp = 0; stp < nsub; ++stp) {
-    const int b = stp & 1;
-    const int kt = it.k0 + stp * KT;
-    if (stp + 1 < nsub) load_tile(kt + KT);
-    if (wave_on) {
-      // S^T = K.(Q_hi + Q_lo)^T for two 16-key blocks
-      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  for (int s = 0; s < nt; ++s) {
+    const int ahead = min(STG - 2, nt - 1 - s);   // tiles in flight behind this one
+    if (ahead >= 2)
+      wait_and_barrier<2 * PER>();
+    else if (ahead == 1)
+      wait_and_barrier<PER>();
+    else
+      wait_and_barrier<0>();
+    if (s + STG - 1 < nt) issue(s + STG - 1);
+    if (!wave_on) continue;
+    const int t = t0 + s;
+    const uint8_t *kt_lds = smem + (s % STG) * 2 * TILEB;
+    const uint8_t *vt_lds = kt_lds + TILEB;
+
+    // S^T = K.(Q_hi + Q_lo)^T, KB blocks of 16 keys.  With one wavefront per
+    // SIMD, every K and V^T fragment of the tile is read up front (their LDS
+    // latency then overlaps the MFMAs and the softmax); with two, K and V^T
+    // are read in halves.
+    const int sl = lane & 15;
+    const int ra0 = 4 * kg + (sl >> 2);       // V^T source row within a 32-key step
+    auto read_k = [&](int ds, int kb) {
+      const int row = 16 * kb + n16;
+      return *reinterpret_cast<const uint4 *>(kt_lds + row * ROWB + 16 * swz_chunk<D>(row, ds * 4 + kg));
+    };
+    auto read_v = [&](int kp, int db) {
+      const int ra = 32 * kp + ra0, rb = ra + 16;
+      const int c = 2 * db + ((sl & 3) >> 1);
+      const uint2 lo = lds_read_tr16(vt_lds + ra * ROWB + 8 * (sl & 1) + 16 * swz_chunk<D>(ra, c));
+      const uint2 hi = lds_read_tr16(vt_lds + rb * ROWB + 8 * (sl & 1) + 16 * swz_chunk<D>(rb, c));
+      return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    };
+    f32x4 sacc[KB];
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
+    for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint4 vf[KP][DB / VSPLIT];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const uint4 kf = *reinterpret_cast<const uint4 *>(&k_lds[b][(16 * kb + n16) * KROW + ds * 32 + kg * 8]);
-          sacc[kb] = mfma16(kf, qh[ds], sacc[kb]);
-          sacc[kb] = mfma16(kf, ql[ds], sacc[kb]);
-        }
+    for (int part = 0; part < KSPLIT; ++part) {
+      uint4 kf[DS / KSPLIT][KB];
+#pragma unroll
+      for (int dd = 0; dd < DS / KSPLIT; ++dd)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) kf[dd][kb] = read_k(part * (DS / KSPLIT) + dd, kb);
+      if (part == 0) {
+#pragma unroll
+        for (int kp = 0; kp < KP; ++kp)
+#pragma unroll
+          for (int dd = 0; dd < DB / VSPLIT; ++dd) vf[kp][dd] = read_v(kp, dd);
       }
-      // masked online softmax (log2 domain) for the lane's query
-      float x[2][4];
-      float tmax = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int dd = 0; dd < DS / KSPLIT; ++dd)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int v = kt + 16 * kb + 4 * kg + i;
-          const bool ok = qok && v < it.k1 && (v < klen || ((anc >> (v - klen)) & 1ull));
-          x[kb][i] = ok ? sacc[kb][i] * a.scale_log2 : -INFINITY;
-          tmax = fmaxf(tmax, x[kb][i]);
+        for (int kb = 0; kb < KB; ++kb) {
+          const int ds = part * (DS / KSPLIT) + dd;
+          sacc[kb] = mfma16(kf[dd][kb], qh[ds], sacc[kb]);
+          sacc[kb] = mfma16(kf[dd][kb], ql[ds], sacc[kb]);
         }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);
-      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_ref);
-      float p[2][4];
-      float rs = 0.f;
+      // order: the K reads, then the S^T MFMAs with the V^T reads (two per
+      // fragment) slotted one per MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, (DS / KSPLIT) * KB, 0);
+      if (part == 0) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[kb][i] = exp2f(x[kb][i] - m_ref);
-          rs += p[kb][i];
+        for (int m = 0; m < 2 * (DS / KSPLIT) * KB; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (m < 2 * KP * (DB / VSPLIT)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-      rs += __shfl_xor(rs, 16);
-      rs += __shfl_xor(rs, 32);
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-      // P as hi + lo bf16 pairs; key slot 8*kg + t <-> key 4*kg + t (t < 4),
-      // 16 + 4*kg + t - 4 (t >= 4), the same order the V^T fragments use
-      uint16_t ph[2][4], pl[2][4];
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * (DS / KSPLIT) * KB, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // visibility of the lane's 4 keys per block, as nibbles: a prefix tile
+    // shows its first klen - key0 keys, a row tile the ancestor-or-self rows
+    const bool pre = t < np;
+    const int key0 = (pre ? t : t - np) * KT;
+    const int lim = pre ? klen - key0 : 0;
+    const uint64_t rbits = (!pre && key0 < 64) ? (anc >> key0) : 0ull;
+    const uint32_t rlo = uint32_t(rbits), rhi = uint32_t(rbits >> 32);
+    float x[KB][4];
+    float tmax = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb) {
+      const int vb = 16 * kb + 4 * kg;
+      const uint32_t nib_pre = (1u << min(max(lim - vb, 0), 4)) - 1u;
+      uint32_t nib_row = 0;
+      if (16 * kb < 64) nib_row = ((kb < 2 ? rlo : rhi) >> ((16 * kb & 31) + 4 * kg)) & 15u;
+      const uint32_t nib = qok ? (pre ? nib_pre : nib_row) : 0u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) split_bf(p[kb][i], ph[kb][i], pl[kb][i]);
-      const uint4 pfh = make_uint4(ph[0][0] | (uint32_t(ph[0][1]) << 16), ph[0][2] | (uint32_t(ph[0][3]) << 16),
-                                   ph[1][0] | (uint32_t(ph[1][1]) << 16), ph[1][2] | (uint32_t(ph[1][3]) << 16));
-      const uint4 pfl = make_uint4(pl[0][0] | (uint32_t(pl[0][1]) << 16), pl[0][2] | (uint32_t(pl[0][3]) << 16),
-                                   pl[1][0] | (uint32_t(pl[1][1]) << 16), pl[1][2] | (uint32_t(pl[1][3]) << 16));
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint16_t *vrow = &v_lds[b][(db * 16 + n16) * VROW];
-        const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + 4 * kg);
-        const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 16 + 4 * kg);
-        const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        o[db] = o[db] * alpha;
-        o[db] = mfma16(vf, pfh, o[db]);
-        o[db] = mfma16(vf, pfl, o[db]);
+      for (int i = 0; i < 4; ++i) {
+        x[kb][i] = ((nib >> i) & 1u) ? sacc[kb][i] * a.scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, x[kb][i]);
       }
     }
-    if (stp + 1 < nsub) store_tile(b ^ 1);
-    __syncthreads();
+    // Online softmax (log2 domain) with a lazy reference: the reference m_run
+    // moves only when the tile max exceeds it by more than 8, so p <= 2^8 and
+    // the rescale of O is usually skipped.  l_run is the lane's own share.
+    tmax = rows4_max(tmax);
+    const bool up = tmax > m_run + 8.f;
+    const float alpha = up ? exp2f(m_run - tmax) : 1.f;
+    m_run = up ? tmax : m_run;
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[kb][i] = exp2f(x[kb][i] - m_use);
+        ls += x[kb][i];
+      }
+    l_run = l_run * alpha + ls;
+    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = o[db] * alpha;
+    }
+    // O^T += V^T.(P_hi + P_lo)^T per 32 keys.  Operand slot 8*kg + t holds
+    // key 4*kg + t (t < 4) or 16 + 4*kg + t - 4 (t >= 4) of the 32, on both
+    // operands.  V^T fragments come from transposing reads: source lane s of
+    // the 16-lane group addresses tile row r0 + (s >> 2), columns
+    // 16*db + 4*(s & 3) .. +3.
+#pragma unroll
+    for (int kp = 0; kp < KP; ++kp) {
+      uint16_t ph[8], pl[8];
+#pragma unroll
+      for (int t8 = 0; t8 < 8; ++t8) split_bf(x[2 * kp + (t8 >> 2)][t8 & 3], ph[t8], pl[t8]);
+      const uint4 pfh = make_uint4(ph[0] | (uint32_t(ph[1]) << 16), ph[2] | (uint32_t(ph[3]) << 16),
+                                   ph[4] | (uint32_t(ph[5]) << 16), ph[6] | (uint32_t(ph[7]) << 16));
+      const uint4 pfl = make_uint4(pl[0] | (uint32_t(pl[1]) << 16), pl[2] | (uint32_t(pl[3]) << 16),
+                                   pl[4] | (uint32_t(pl[5]) << 16), pl[6] | (uint32_t(pl[7]) << 16));
+#pragma unroll
+      for (int part = 0; part < VSPLIT; ++part) {
+        if (part > 0) {
+#pragma unroll
+          for (int dd = 0; dd < DB / VSPLIT; ++dd) vf[kp][dd] = read_v(kp, part * (DB / VSPLIT) + dd);
+        }
+#pragma unroll
+        for (int dd = 0; dd < DB / VSPLIT; ++dd) {
+          const int db = part * (DB / VSPLIT) + dd;
+          o[db] = mfma16(vf[kp][dd], pfh, o[db]);
+          o[db] = mfma16(vf[kp][dd], pfl, o[db]);
+        }
+      }
+    }
   }
+  l_run = rows4_sum(l_run);
 
   // ---- partial results
   if (qok) {
@@ -408,20 +520,22 @@ void launch_rope_f32(const float *q, const float *k, float *qo, float *ko, const
                      int64_t(0));
 }
 
+template <int D, int NW, int STG, int OCC>
+static void launch_attn_dd(const AttnArgs &a, int n_items, hipStream_t s) {
+  constexpr size_t lds = attn_lds_bytes<D, STG>();
+  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(attn_mfma_kernel<D, NW, STG, OCC>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  hipLaunchKernelGGL((attn_mfma_kernel<D, NW, STG, OCC>), dim3(n_items), dim3(64 * NW), lds, s, a);
+}
+
+// Four wavefronts (up to 64 query vectors): a 2-stage ring (64 KB of LDS)
+// so that two workgroups share a compute unit and hide each other's
+// latencies.  Eight wavefronts: a 4-stage ring, one workgroup per unit.
 void launch_attn_mfma(const AttnArgs &a, int n_items, int D, int max_qblocks, hipStream_t s) {
   const bool eight = max_qblocks > 4;
-#define SV_ATTN(DD)                                                                              \
-  if (D == DD) {                                                                                 \
-    if (eight)                                                                                   \
-      hipLaunchKernelGGL((attn_mfma_kernel<DD, 8>), dim3(n_items), dim3(512), 0, s, a);          \
-    else                                                                                         \
-      hipLaunchKernelGGL((attn_mfma_kernel<DD, 4>), dim3(n_items), dim3(256), 0, s, a);          \
-    return;                                                                                      \
-  }
-  SV_ATTN(64)
-  SV_ATTN(128)
-  SV_ATTN(256)
-#undef SV_ATTN
+  if (D == 64) eight ? launch_attn_dd<64, 8, 4, 2>(a, n_items, s) : launch_attn_dd<64, 4, 2, 2>(a, n_items, s);
+  if (D == 128) eight ? launch_attn_dd<128, 8, 4, 2>(a, n_items, s) : launch_attn_dd<128, 4, 2, 2>(a, n_items, s);
+  if (D == 256) eight ? launch_attn_dd<256, 8, 4, 2>(a, n_items, s) : launch_attn_dd<256, 4, 2, 2>(a, n_items, s);
 }
 
 void launch_attn_merge(const MergeArgs &a, int n_rows, int D, hipStream_t s) {

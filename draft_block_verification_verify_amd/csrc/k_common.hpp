@@ -101,6 +101,27 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Reductions over the four lanes l, l^16, l^32, l^48 (one per 16-lane row)
+// with the gfx950 row swaps: v_permlane16_swap exchanges the odd rows of its
+// first operand with the even rows of its second, v_permlane32_swap the upper
+// half of the first with the lower half of the second; with both operands
+// equal, the two results of a swap hold every lane's partner of that step.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float rows4_max(float v) {
+  u32x2 r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r.x), __uint_as_float(r.y));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r.x), __uint_as_float(r.y));
+}
+
+__device__ __forceinline__ float rows4_sum(float v) {
+  u32x2 r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r.x) + __uint_as_float(r.y);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r.x) + __uint_as_float(r.y);
+}
+
 // Running (max, sum of exp(x - max), index of the max) of a set of logits.
 // The index is the lowest among equal maxima.
 struct MaxSumArg {

@@ -58,8 +58,8 @@ int check_dims(const Dims &dm, std::string *err) {
 }
 
 int64_t slot_capacity(const Dims &dm) {
-  int64_t s = int64_t(16) * dm.Hq * dm.max_rows;
-  return std::min<int64_t>(196608, std::max<int64_t>(16384, s));
+  int64_t s = int64_t(24) * dm.Hq * dm.max_rows;
+  return std::min<int64_t>(393216, std::max<int64_t>(16384, s));
 }
 
 static int qg_max_of(const Dims &dm) {
@@ -207,61 +207,62 @@ int build_plan(const Dims &dm, const HostInputs &in, int64_t slot_cap, int targe
 
   // ---- attention work list -------------------------------------------------
   const int G = dm.Hq / dm.Hkv;
+  const int KT = attn_key_tile(dm.d);
   P.qg_max = qg_max_of(dm);
+  std::vector<int64_t> tiles(P.R);
   int64_t total = 0;
   int mq_max = 1;
   for (int r = 0; r < P.R; ++r) {
+    const int64_t len = P.tree_kv_len[r];
+    // per-lane byte offsets into one tree's prefix stay below 2^31
+    if (dm.dtype == 1 && (len + KT) * dm.Hkv * dm.d * 2 >= (int64_t(1) << 31)) {
+      *err = cat("tree ", r, ": prefix length ", len, " too large for 32-bit KV offsets");
+      return P_UNSUPPORTED;
+    }
+    tiles[r] = ceil_div(len, KT) + ceil_div(P.tree_rows[r], KT);
     const int64_t mq = int64_t(P.tree_rows[r]) * G;
     mq_max = int(std::max<int64_t>(mq_max, std::min<int64_t>(mq, kItemQ)));
-    total += int64_t(dm.Hkv) * ceil_div(mq, kItemQ) * (P.tree_kv_len[r] + P.tree_rows[r]);
+    total += int64_t(dm.Hkv) * ceil_div(mq, kItemQ) * tiles[r];
   }
-  // Each item writes nq partial records of (d + 2) floats; keep that below a
-  // quarter of the item's KV bytes (chunk >= 8 * nq), and aim for
+  // Each item writes nq partial records of (d + 2) floats; keep that below
+  // half of the item's K + V bytes (chunk >= 4 * nq keys), and aim for
   // `target_items` items overall.
-  int64_t chunk = std::max<int64_t>({64, 8 * int64_t(mq_max), ceil_div(total, std::max(target_items, 1))});
-  chunk = ceil_div(chunk, 32) * 32;
+  int64_t chunk = std::max<int64_t>({ceil_div(64, KT), ceil_div(4 * int64_t(mq_max), KT),
+                                     ceil_div(total, std::max(target_items, 1))});   // in tiles
   for (;;) {
     int64_t slots = 0;
-    for (int r = 0; r < P.R; ++r) {
-      const int64_t K = P.tree_kv_len[r] + P.tree_rows[r];
-      const int64_t splits = ceil_div(K, chunk);
-      slots += int64_t(dm.Hkv) * splits * P.tree_rows[r] * G;
-    }
-    if (slots <= slot_cap) {
-      P.slots = slots;
-      break;
-    }
-    if (chunk > (int64_t(1) << 30)) {
+    for (int r = 0; r < P.R; ++r)
+      slots += int64_t(dm.Hkv) * ceil_div(tiles[r], chunk) * P.tree_rows[r] * G;
+    if (slots <= slot_cap) break;
+    if (chunk > (int64_t(1) << 30) / KT) {
       *err = "attention partial capacity exhausted";
       return P_CAPACITY;
     }
     chunk *= 2;
   }
-  P.chunk = int32_t(chunk);
+  P.chunk = int32_t(chunk * KT);
   const int n_groups = P.R * dm.Hkv * P.qg_max;
   P.group_first.assign(n_groups, 0);
   P.group_count.assign(n_groups, 0);
   int64_t slot = 0;
   for (int r = 0; r < P.R; ++r) {
     const int mq = P.tree_rows[r] * G;
-    const int64_t K = P.tree_kv_len[r] + P.tree_rows[r];
-    const int64_t splits = ceil_div(K, chunk);
-    // equal pieces, multiples of 32 keys, the last one ragged
-    const int64_t piece = ceil_div(ceil_div(K, splits), 32) * 32;
+    const int64_t splits = ceil_div(tiles[r], chunk);
+    const int64_t piece = ceil_div(tiles[r], splits);   // equal pieces, the last one ragged
     for (int g = 0; g < dm.Hkv; ++g) {
       for (int qg = 0; qg * kItemQ < mq; ++qg) {
         const int m0 = qg * kItemQ;
         const int nq = std::min(kItemQ, mq - m0);
         const int gi = (r * dm.Hkv + g) * P.qg_max + qg;
         P.group_first[gi] = int32_t(P.items.size());
-        for (int64_t k0 = 0; k0 < K; k0 += piece) {
+        for (int64_t t0 = 0; t0 < tiles[r]; t0 += piece) {
           AttnItem it{};
           it.tree = r;
           it.g = g;
           it.m0 = m0;
           it.nq = nq;
-          it.k0 = int32_t(k0);
-          it.k1 = int32_t(std::min(K, k0 + piece));
+          it.k0 = int32_t(t0 * KT);
+          it.k1 = int32_t(std::min(tiles[r], t0 + piece) * KT);
           it.slot = int32_t(slot);
           slot += nq;
           P.items.push_back(it);

@@ -19,9 +19,18 @@ struct Dims {
   int32_t max_rows, max_roots, max_tree_rows, max_pos;
 };
 
-// One attention work item: keys [k0, k1) of the tree's virtual key sequence
-// (prefix tokens 0..len-1, then the tree's rows in row order) against query
-// vectors [m0, m0+nq) of (tree, kv head g); m = local_row * G + head_in_group.
+// Keys per attention tile for head dimension d: one tile of K (or V) is
+// 16 KB of bf16.
+constexpr int attn_key_tile(int d) { return 8192 / d; }
+
+// Virtual key sequence of a tree, in tiles of KT = attn_key_tile(d) keys:
+// prefix tiles [0, ceil(len / KT)) hold prefix tokens 0..len-1 (the last tile
+// padded), then ceil(T / KT) row tiles hold the tree's T rows in row order.
+// A tile never mixes the prefix with the rows.
+//
+// One attention work item: tiles [k0 / KT, k1 / KT) of that sequence (k0, k1
+// in keys, multiples of KT) against query vectors [m0, m0+nq) of
+// (tree, kv head g); m = local_row * G + head_in_group.
 struct AttnItem {
   int32_t tree, g, m0, nq, k0, k1, slot, pad;
 };

@@ -137,9 +137,12 @@ def test_plan_ancestor_masks_and_items_cover_keys(plan_lib):
             bits |= 1 << (j - s)
             j = parent[j]
         assert int(anc[i]) == bits, i
-    # items: per (tree, kv head, query group) the key ranges tile [0, len + T)
+    # items: per (tree, kv head, query group) the tile-aligned key ranges cover
+    # the tree's key sequence: ceil(len / KT) prefix tiles, then ceil(T / KT)
+    # row tiles (KT = 8192 / d = 64 keys)
     T = [7, 3]
     G = 4
+    KT = 8192 // DIMS[2]
     assert stats[0] == 2 and stats[1] == 8
     slots = []
     for tree in range(2):
@@ -147,9 +150,11 @@ def test_plan_ancestor_masks_and_items_cover_keys(plan_lib):
             for qg in range((T[tree] * G + 127) // 128):
                 its = [it for it in items if it[0] == tree and it[1] == g and it[2] == qg * 128]
                 its.sort(key=lambda it: it[4])
-                assert its[0][4] == 0 and its[-1][5] == lens[tree] + T[tree]
+                span = (-(-lens[tree] // KT) - (-T[tree] // KT)) * KT
+                assert its[0][4] == 0 and its[-1][5] == span
                 for a, b in zip(its, its[1:]):
                     assert a[5] == b[4]
+                assert all(it[4] % KT == 0 and it[5] % KT == 0 and it[5] > it[4] for it in its)
                 for it in its:
                     assert it[3] == min(128, T[tree] * G - qg * 128)
                     slots.append((it[6], it[6] + it[3]))
