@@ -106,8 +106,9 @@ def spec_verify_destroy(h) -> None:
     _check(lib().spec_verify_destroy(h))
 
 
-def spec_verify_profile(h, on: bool) -> None:
-    _check(lib().spec_verify_profile(h, 1 if on else 0))
+def spec_verify_profile(h, mode) -> None:
+    """mode: 0/False off, 1/True every stage, 2 the LM-head stage only."""
+    _check(lib().spec_verify_profile(h, int(mode)))
 
 
 def spec_verify_stage_times(h) -> list[tuple[str, float]]:

@@ -60,7 +60,7 @@ struct sv_handle {
   // completion / profiling
   hipEvent_t done = nullptr;
   bool ran = false;
-  bool profile = false;
+  int profile = 0;                 // 0 off, 1 every stage, 2 the LM head only
   std::vector<Stage> stages;      // every recorded stage of every recorded run
 };
 
@@ -167,7 +167,7 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
     A(&h->part_o, size_t(h->slot_cap * D * 4));
     A(&h->part_ml, size_t(h->slot_cap * 2 * 4));
   }
-  A(&h->o_act, size_t(R * Hq * D * 4));       // bf16 hi + lo planes, fp16, or fp32
+  A(&h->o_act, size_t(R * Hq * D * 4));       // fp16 hi + lo planes, fp16, or fp32
   A(&h->h_part, h->h_part_floats * 4);
   A(&h->hn, size_t(R * H * 4));
   A(&h->logits, size_t(R * V * 4));
@@ -249,15 +249,16 @@ static void drop_stages(sv_handle *h) {
   h->stages.clear();
 }
 
-sv_status spec_verify_profile(sv_handle *h, int32_t on) {
+sv_status spec_verify_profile(sv_handle *h, int32_t on) {  // on: profiling mode
   g_err.clear();
   if (!h) return fail(SV_ERR_INVALID_ARG, "null handle");
   if (h->ran) {
     const hipError_t e = hipEventSynchronize(h->done);
     if (e != hipSuccess) return hip_fail("hipEventSynchronize", e);
   }
+  if (on < 0 || on > 2) return fail(SV_ERR_INVALID_ARG, "profile mode must be 0, 1 or 2");
   drop_stages(h);
-  h->profile = on != 0;
+  h->profile = on;
   return SV_OK;
 }
 
@@ -323,7 +324,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   const bool bf16 = dm.dtype == SV_BF16;
 
   size_t step_stage = 0;
-  if (h->profile) {
+  if (h->profile == 1) {
     Stage s{"step", nullptr, nullptr};
     (void)hipEventCreate(&s.a);
     (void)hipEventCreate(&s.b);
@@ -340,7 +341,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   }
   sv::MetaLayout lay2;
   sv::pack_plan(plan, dm.Hkv, h->h_meta[slot], &lay2);
-  if (h->profile) (void)hipEventRecord(h->stages[step_stage].a, stream);
+  if (h->profile == 1) (void)hipEventRecord(h->stages[step_stage].a, stream);
   e = hipMemcpyAsync(h->d_meta, h->h_meta[slot], lay.total, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return hip_fail("hipMemcpyAsync", e);
   e = hipEventRecord(h->meta_ev[slot], stream);
@@ -364,8 +365,10 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   const int32_t *group_count = reinterpret_cast<const int32_t *>(m + lay.group_count);
 
   // ---- stage bookkeeping for profiling (events on the run's stream)
+  bool recording = false;
   auto begin = [&](const char *name) {
-    if (!h->profile) return;
+    recording = h->profile == 1 || (h->profile == 2 && std::strcmp(name, "lm_head") == 0);
+    if (!recording) return;
     Stage s{name, nullptr, nullptr};
     (void)hipEventCreate(&s.a);
     (void)hipEventCreate(&s.b);
@@ -373,8 +376,9 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     h->stages.push_back(s);
   };
   auto end = [&]() {
-    if (!h->profile) return;
+    if (!recording) return;
     (void)hipEventRecord(h->stages.back().b, stream);
+    recording = false;
   };
 
   float *logits = out->logits ? out->logits : h->logits;
@@ -418,7 +422,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
 
   int k_split = 0;
   const int splits = bf16 ? sv::gemm_splits(n, int(H), int(Hq * D), h->n_cu, &k_split) : 1;
-  // activation format of the projections: bf16 hi + lo planes for the
+  // activation format of the projections: fp16 hi + lo planes for the
   // skinny launch, fp16 for the tiled one
   const int act_mode = n <= 64 ? sv::ACT_SPLIT : sv::ACT_F16;
   const int64_t q_lo = int64_t(dm.max_rows) * Hq * D;   // lo planes start one capacity further
@@ -560,7 +564,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   begin("accept");
   sv::launch_accept(va, stream);
   end();
-  if (h->profile) (void)hipEventRecord(h->stages[step_stage].b, stream);
+  if (h->profile == 1) (void)hipEventRecord(h->stages[step_stage].b, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail("kernel launch", e);
   e = hipEventRecord(h->done, stream);

@@ -7,20 +7,18 @@
 // Part 2", MTP section), so its epilogue also reduces every N tile to
 // (max, sum exp, argmax) per row, ready for the vocab-wide softmax.
 //
-// Skinny launch (rows <= 64, HBM-bound): no LDS.  Each wavefront owns WV x 32
-// weight rows and streams them straight into MFMA A-operand registers, 64
-// contiguous bytes per lane per 64-wide K block; the activation fragments
-// come from L2.  The K index inside a 64-block is permuted identically on
-// both operands so that every lane reads contiguous memory.  The activations
-// are a bf16 pair hi + lo (two bf16 MFMAs against the exact bf16 weights),
-// which costs MFMA time this launch has to spare.
+// The weights are the handle's fp16 copies (converted once from bf16 at
+// handle creation, exact for the weights accepted there); both operands of
+// every MFMA are fp16 with fp32 accumulation.
 //
-// Tiled launch (rows > 64, near the compute ridge): 256 x 256 output tiles,
-// 8 wavefronts, K steps of 64 double-buffered through LDS, 32x32x16 fp16
-// MFMA with fp32 accumulation.  Weight tiles are converted bf16 -> fp16 on
-// their way into LDS (exact for weights in the fp16 normal range) and the
-// activations arrive in fp16, so the activations keep 11 significant bits
-// at no extra MFMA work.
+// Skinny launch (rows <= 64, HBM-bound): weight rows and the activation
+// stream into a 3-stage LDS ring by direct global -> LDS loads; the
+// activation is an fp16 pair hi + lo (two MFMAs per product, MFMA time this
+// launch has to spare), so it keeps about 22 significant bits.
+//
+// Tiled launch (rows > 64, near the compute ridge): persistent, 256 x 256
+// output tiles, a 4-stage DMA ring, 32x32x16 fp16 MFMA; the activation is
+// plain fp16 (11 significant bits).
 #include <algorithm>
 #include <type_traits>
 

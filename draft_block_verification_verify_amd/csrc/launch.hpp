@@ -31,7 +31,7 @@ struct MergeArgs {
   const AttnItem *items;
   const int32_t *group_first, *group_count, *row_tree, *row_local;
   int Hq, Hkv, qg_max;
-  int mode;                        // ACT_SPLIT: bf16 hi plane at out, lo at out + lo_off; ACT_F16
+  int mode;                        // ACT_SPLIT: fp16 hi plane at out, lo at out + lo_off; ACT_F16
   int64_t lo_off;
   uint16_t *out;                   // [n, Hq*D]
 };
@@ -82,7 +82,7 @@ void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s);
 void launch_gemm_f32(const float *act, int rows, const float *W, int N, int K, float *out, hipStream_t s);
 void launch_stats_from_logits(const float *logits, int rows, int V, int tile, float *t_max, float *t_sum,
                               int32_t *t_arg, int n_tiles, hipStream_t s);
-// Writes the normalised rows in `mode` (ACT_SPLIT: bf16 hi plane at out, lo
+// Writes the normalised rows in `mode` (ACT_SPLIT: fp16 hi plane at out, lo
 // plane at out + lo_off; ACT_F16; ACT_F32).
 void launch_norm(const float *part, int splits, int64_t split_stride, int rows, int hidden, float eps, int mode,
                  void *out, int64_t lo_off, hipStream_t s);

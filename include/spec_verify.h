@@ -130,15 +130,17 @@ sv_status spec_verify_destroy(sv_handle *h);
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *spec_verify_last_error(void);
 
-/* Per-stage device times, for profiling.  spec_verify_profile(h, on != 0)
- * starts recording: every later run records a HIP event before and after each
- * of its stages (and around the whole step, stage "step") on the run's stream.
- * spec_verify_stage_times waits for the last recorded run, then writes up to
- * `cap` stage names (static strings) and their mean duration in ms over all
- * runs recorded since profiling was switched on; returns the number of
- * stages (0 if nothing was recorded), or a negative sv_status.
- * spec_verify_profile(h, 0) stops recording and drops the records. */
-sv_status spec_verify_profile(sv_handle *h, int32_t on);
+/* Per-stage device times, for profiling.  spec_verify_profile(h, mode)
+ * drops earlier records and sets what later runs record on their stream:
+ * mode 1, a HIP event before and after each stage and around the whole step
+ * (stage "step"); mode 2, events around the LM-head stage only (the step's
+ * dominant kernel, at the cost of two events per run); mode 0, nothing.
+ * Other modes fail with SV_ERR_INVALID_ARG.  spec_verify_stage_times waits
+ * for the last recorded run, then writes up to `cap` stage names (static
+ * strings) and their mean duration in ms over all runs recorded since the
+ * mode was set; returns the number of stages (0 if nothing was recorded), or
+ * a negative sv_status. */
+sv_status spec_verify_profile(sv_handle *h, int32_t mode);
 int32_t spec_verify_stage_times(sv_handle *h, const char **names, float *ms, int32_t cap);
 
 #ifdef __cplusplus
