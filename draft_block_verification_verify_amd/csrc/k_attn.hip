@@ -58,10 +58,16 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(const T *__restrict__ q,
                                                         T *__restrict__ q_out, T *__restrict__ k_out,
                                                         const int32_t *__restrict__ row_pos, int Hq,
                                                         int Hkv, int D, double base, int64_t q_lo_off) {
+  __shared__ double cs[128], sn[128];   // cos, sin of pos * theta_k, k < D/2 <= 128
   const int i = blockIdx.x;
   const int half = D / 2;
   const int heads = Hq + Hkv;
   const double pos = double(row_pos[i]);
+  for (int kk = threadIdx.x; kk < half; kk += blockDim.x) {
+    const double theta = pow(base, -2.0 * double(kk) / double(D));
+    sincos(pos * theta, &sn[kk], &cs[kk]);
+  }
+  __syncthreads();
   for (int p = threadIdx.x; p < heads * half; p += blockDim.x) {
     const int hh = p / half, kk = p % half;
     const T *src;
@@ -73,9 +79,7 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(const T *__restrict__ q,
       src = k + (int64_t(i) * Hkv + (hh - Hq)) * D;
       dst = k_out + (int64_t(i) * Hkv + (hh - Hq)) * D;
     }
-    const double theta = pow(base, -2.0 * double(kk) / double(D));
-    double s, c;
-    sincos(pos * theta, &s, &c);
+    const double c = cs[kk], s = sn[kk];
     const double a = ld(src + kk), b = ld(src + kk + half);
     if (hh < Hq) {
       st_q(dst + kk, q_lo_off, a * c - b * s);
@@ -395,31 +399,56 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_mfma_kernel(AttnArgs a) {
   }
 }
 
-// Combine the split-KV partials of one (row, query head) and write o (bf16).
+// Combine the split-KV partials of one (row, query head) and write o in the
+// projection's activation format.  The first wave reads the (max, sum)
+// records of all splits at once and leaves each split's weight
+// exp2(m_t - M) in LDS; then every thread sums its column over the splits,
+// four independent loads at a time.
 template <int D>
 __global__ __launch_bounds__(D) void attn_merge_kernel(MergeArgs a) {
+  __shared__ float wgt[kMaxSplits];
+  __shared__ int64_t slot_of[kMaxSplits];
+  __shared__ float tot_l;
   const int i = blockIdx.x / a.Hq, h = blockIdx.x % a.Hq;
   const int G = a.Hq / a.Hkv;
   const int r = a.row_tree[i], loc = a.row_local[i];
   const int g = h / G, m = loc * G + h % G;
   const int qg = m / kItemQ, mi = m % kItemQ;
   const int gi = (r * a.Hkv + g) * a.qg_max + qg;
-  const int first = a.group_first[gi], cnt = a.group_count[gi];
-  float M = -INFINITY;
-  for (int t = 0; t < cnt; ++t) {
-    const int64_t slot = int64_t(a.items[first + t].slot) + mi;
-    M = fmaxf(M, a.part_ml[2 * slot]);
-  }
-  float L = 0.f, acc = 0.f;
+  const int first = a.group_first[gi], cnt = min(a.group_count[gi], kMaxSplits);   // the plan keeps it <= kMaxSplits
   const int c = threadIdx.x;
-  for (int t = 0; t < cnt; ++t) {
-    const int64_t slot = int64_t(a.items[first + t].slot) + mi;
-    const float mt = a.part_ml[2 * slot];
-    const float wgt = (mt == -INFINITY) ? 0.f : exp2f(mt - M);
-    L += wgt * a.part_ml[2 * slot + 1];
-    acc += wgt * a.part_o[slot * D + c];
+  if (c < 64) {
+    float M = -INFINITY;
+    for (int t = c; t < cnt; t += 64) {
+      const int64_t slot = int64_t(a.items[first + t].slot) + mi;
+      slot_of[t] = slot;
+      M = fmaxf(M, a.part_ml[2 * slot]);
+    }
+    M = wave_max(M);
+    float L = 0.f;
+    for (int t = c; t < cnt; t += 64) {
+      const int64_t slot = slot_of[t];
+      const float mt = a.part_ml[2 * slot];
+      const float w = (mt == -INFINITY) ? 0.f : exp2f(mt - M);
+      wgt[t] = w;
+      L += w * a.part_ml[2 * slot + 1];
+    }
+    L = wave_sum(L);
+    if (c == 0) tot_l = L;
   }
-  const float val = acc / L;
+  __syncthreads();
+  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+  int t = 0;
+  for (; t + 4 <= cnt; t += 4) {
+    const float o0 = a.part_o[slot_of[t] * D + c], o1 = a.part_o[slot_of[t + 1] * D + c];
+    const float o2 = a.part_o[slot_of[t + 2] * D + c], o3 = a.part_o[slot_of[t + 3] * D + c];
+    acc0 += wgt[t] * o0;
+    acc1 += wgt[t + 1] * o1;
+    acc2 += wgt[t + 2] * o2;
+    acc3 += wgt[t + 3] * o3;
+  }
+  for (; t < cnt; ++t) acc0 += wgt[t] * a.part_o[slot_of[t] * D + c];
+  const float val = ((acc0 + acc1) + (acc2 + acc3)) / tot_l;
   const int64_t idx = int64_t(i) * a.Hq * D + int64_t(h) * D + c;
   if (a.mode == ACT_SPLIT) {
     uint16_t hi, lo;

@@ -240,7 +240,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 // 256 (N) x 256 (rows).  8 wavefronts as 2 x 4, each 128 (N) x 64 (rows) =
 // 4 x 2 fp16 32x32x16 MFMA blocks.  K steps of 32 (64 B per row) land in a
 // 4-stage LDS ring by DMA (weights 256 rows, then activations 256 rows; 16-B
-// chunk c of row R at slot c ^ ((R >> 2) & 3)), three steps ahead of the
+// chunk c of row R at slot c ^ ((R >> 1) & 3), so that any 8 consecutive
+// rows of one chunk fall in 8 distinct bank groups), three steps ahead of the
 // MFMAs.  When a tile's K loop ends, the epilogue (per-row max / sumexp /
 // argmax of the tile, logit stores) is issued and the first stages of the
 // workgroup's next tile follow at once, so the stores drain while those
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int R = w * 32 + i * 16 + (lane >> 2);
-    off[i] = R * Kb + ((c4 ^ ((R >> 2) & 3)) << 4);
+    off[i] = R * Kb + ((c4 ^ ((R >> 1) & 3)) << 4);
   }
   // tile i -> (weight tile, row tile); i and i+8 share the weight tile
   auto tile_of = [&](int i, int &n_tile, int &t_tile) {
@@ -341,12 +342,12 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int R = wn * 128 + v * 32 + r32;
-          af[j][v] = lds16(base + R * 64 + ((q ^ ((R >> 2) & 3)) << 4));
+          af[j][v] = lds16(base + R * 64 + ((q ^ ((R >> 1) & 3)) << 4));
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int R = wt * 64 + t * 32 + r32;
-          bf[j][t] = lds16(base + kTBN * 64 + R * 64 + ((q ^ ((R >> 2) & 3)) << 4));
+          bf[j][t] = lds16(base + kTBN * 64 + R * 64 + ((q ^ ((R >> 1) & 3)) << 4));
         }
       }
 #pragma unroll

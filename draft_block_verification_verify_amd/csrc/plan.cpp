@@ -227,8 +227,11 @@ int build_plan(const Dims &dm, const HostInputs &in, int64_t slot_cap, int targe
   // Each item writes nq partial records of (d + 2) floats; keep that below
   // half of the item's K + V bytes (chunk >= 4 * nq keys), and aim for
   // `target_items` items overall.
+  int64_t max_tiles = 1;
+  for (int r = 0; r < P.R; ++r) max_tiles = std::max(max_tiles, tiles[r]);
   int64_t chunk = std::max<int64_t>({ceil_div(64, KT), ceil_div(4 * int64_t(mq_max), KT),
-                                     ceil_div(total, std::max(target_items, 1))});   // in tiles
+                                     ceil_div(total, std::max(target_items, 1)),
+                                     ceil_div(max_tiles, kMaxSplits)});   // in tiles
   for (;;) {
     int64_t slots = 0;
     for (int r = 0; r < P.R; ++r)

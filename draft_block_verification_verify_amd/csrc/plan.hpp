@@ -13,6 +13,7 @@ namespace sv {
 // one tree for one KV head, at most kItemQ of them per item.
 constexpr int kItemQ = 128;
 constexpr int kMaxTreeRows = 64;   // ancestor masks are one uint64 per row
+constexpr int kMaxSplits = 1024;   // most key-range items per (tree, KV head, query group)
 
 struct Dims {
   int32_t Hq, Hkv, d, hidden, vocab, dtype;

@@ -174,6 +174,18 @@ def test_plan_coarsens_split_to_fit_slot_capacity(plan_lib):
     assert stats[2] == 4 * 2          # 2 pieces per KV head
 
 
+def test_plan_caps_splits_per_group(plan_lib):
+    # one long prefix and a huge work-item target: the split count per
+    # (tree, KV head, query group) stays within what the merge handles
+    st, err, stats, _, items = plan(plan_lib, DIMS, [-1, 0], [500000, 500001], [0], [500000], 500000,
+                                    target=100000)
+    assert st == 0, err
+    per_head = {}
+    for it in items:
+        per_head[it[1]] = per_head.get(it[1], 0) + 1
+    assert max(per_head.values()) <= 1024
+
+
 @pytest.mark.parametrize("parent,pos,off,lens,kv,code,frag", [
     ([0, 0], [1, 2], [0], [1], 4, -2, "root"),
     ([-1, 2, 1], [1, 2, 3], [0], [1], 4, -2, "parent"),
