@@ -83,7 +83,7 @@ CONFIGS: dict[int, Config] = {
 
 # tensor tags for independent random streams
 _TAG = {"kv_k": 1, "kv_v": 2, "q": 3, "k": 4, "v": 5, "w_o": 6, "w_lm": 7,
-        "drafter": 8, "struct": 9, "plant": 10, "sample": 11}
+        "drafter": 8, "struct": 9, "plant": 10, "sample": 11, "uniform": 12}
 
 
 def _rng(cfg_id: int, seed: int, tag: str, sub: int = 0) -> np.random.Generator:
@@ -317,3 +317,15 @@ def sample_tree_drafts(inp: Inputs) -> np.ndarray:
         ids[i] = int(np.argmax(b + g))
     inp.draft_ids = ids
     return ids
+
+
+def make_uniforms(inp: Inputs):
+    """Uniforms in [0, 1) for the T = 1 verification rule: one accept test
+    per non-root row (u_accept[n], roots 0) and one bonus draw per tree
+    (u_bonus[R]), fp32 so that both sides read the same values."""
+    st = inp.st
+    r = _rng(inp.cfg.cfg_id, inp.seed, "uniform")
+    u_accept = r.random(st.n_rows, dtype=np.float32)
+    u_accept[np.asarray(st.parent) < 0] = 0.0
+    u_bonus = r.random(st.n_roots, dtype=np.float32)
+    return u_accept, u_bonus

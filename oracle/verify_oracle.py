@@ -40,6 +40,18 @@ from their fp32 / bf16 bits):
    probabilities of the earlier positions); surv_sum = sum over non-root rows
    of the tree (the expected accepted length a scheduler obtains by
    multiplying probabilities, VESSL part 2, DSpark section).
+9. T = 1 stochastic verification of chains (mode 1).  The pages evaluate
+   sampling at T = 1 (DSpine page, temperature section; SpecOPD summary,
+   "premises and limits") and give the per-position acceptance probability
+   as alpha = 1 - D_TV (VESSL part 2, DSpark section) without writing the
+   rule out; the plainest rule with exactly that acceptance is the standard
+   one taken here: at row cur with child c carrying draft d, accept when
+   u_accept[c] * q_c(d) < p_cur(d) (probability min(1, p/q)); on the first
+   rejection the bonus token is drawn from max(0, p_cur - q_c), and when the
+   walk reaches a leaf it is drawn from p_cur, both by the inverse CDF at
+   u_bonus (the smallest token whose running weight exceeds u_bonus times
+   the total).  The uniforms are inputs.  Trees with branching nodes are not
+   taken in this mode.
 """
 from __future__ import annotations
 
@@ -213,6 +225,53 @@ def survival(forest: Forest, overlaps):
 
 
 # ----------------------------------------------------------------------------
+# 9. T = 1 stochastic verification (chains)
+# ----------------------------------------------------------------------------
+
+
+def sample_inverse_cdf(weights: np.ndarray, u: float):
+    """Smallest token t whose running weight sum exceeds u * (total weight),
+    for non-negative weights with a positive total and u in [0, 1).  Also
+    returns the distance from u * total to the nearest running sum (relative
+    to the total), which says how close the draw is to a neighbouring token."""
+    c = np.cumsum(np.asarray(weights, dtype=np.float64))
+    z = float(c[-1])
+    target = u * z
+    t = int(np.searchsorted(c, target, side="right"))
+    lo = float(c[t - 1]) if t > 0 else 0.0
+    margin = min(target - lo, float(c[t]) - target) / z
+    return t, margin
+
+
+def stochastic_walk(forest: Forest, root: int, p_of, q_of, draft_ids, u_accept, u_bonus: float):
+    """T = 1 walk of one chain from `root` (step 9).  p_of(row) is the
+    target distribution at a row, q_of(row) the drafter distribution of a
+    non-root row.  Returns (accept_len, bonus, last_row, margin) where margin
+    is the smallest relative distance of any accept test, or of the bonus
+    draw, from its decision boundary."""
+    cur, acc = root, 0
+    margin = float("inf")
+    while True:
+        ch = forest.children(cur)
+        if len(ch) > 1:
+            raise ValueError(f"row {cur} has {len(ch)} children: stochastic verification takes chains")
+        p = p_of(cur)
+        if not ch:
+            t, m = sample_inverse_cdf(p, u_bonus)
+            return acc + 1, t, cur, min(margin, m)
+        c = ch[0]
+        d = int(draft_ids[c])
+        q = q_of(c)
+        lhs, rhs = float(u_accept[c]) * float(q[d]), float(p[d])
+        margin = min(margin, abs(lhs - rhs) / max(float(p[d]), float(q[d]), 1e-300))
+        if lhs < rhs:
+            cur, acc = c, acc + 1
+            continue
+        t, m = sample_inverse_cdf(np.maximum(p - q, 0.0), u_bonus)
+        return acc + 1, t, cur, min(margin, m)
+
+
+# ----------------------------------------------------------------------------
 # the whole step
 # ----------------------------------------------------------------------------
 
@@ -277,8 +336,10 @@ def verify(cfg, inp, trees=None, keep_logits: bool = False) -> dict:
 
     Rows outside the listed trees get NaN / -1 in the outputs.
     Returns a dict of numpy arrays: argmax, row_max, row_lse, gap, overlap,
-    survival per row; accept_len, bonus, last_row, surv_sum per tree;
-    optionally logits [n, V] (NaN for rows not computed)."""
+    survival per row; accept_len, bonus, last_row, surv_sum per tree (with
+    inp["mode"] == 1, the T = 1 walk of step 9 on inp["u_accept"] and
+    inp["u_bonus"], and walk_margin, its closest decision); optionally
+    logits [n, V] (NaN for rows not computed)."""
     forest = Forest(inp["parent"])
     n, R = forest.n, len(forest.roots)
     if trees is None:
@@ -311,10 +372,22 @@ def verify(cfg, inp, trees=None, keep_logits: bool = False) -> dict:
     for k in ("accept_len", "bonus", "last_row"):
         res[k] = np.full(R, -1, np.int64)
     res["surv_sum"] = np.full(R, np.nan)
+    res["walk_margin"] = np.full(R, np.inf)
     for t in trees:
         for i in forest.tree_rows[t]:
             res["survival"][i] = surv_all[i]
-        acc, bonus, last = accept_walk(forest, forest.roots[t], res["argmax"], inp["draft_ids"])
+        if int(inp.get("mode", 0)) == 1:
+            def p_of(i):
+                return softmax(logits[where[i]])
+
+            def q_of(i):
+                return softmax(decode(dl[forest.draft_index[i]], cfg["dtype"]))
+
+            acc, bonus, last, mg = stochastic_walk(forest, forest.roots[t], p_of, q_of, inp["draft_ids"],
+                                                   inp["u_accept"], float(inp["u_bonus"][t]))
+            res["walk_margin"][t] = mg
+        else:
+            acc, bonus, last = accept_walk(forest, forest.roots[t], res["argmax"], inp["draft_ids"])
         res["accept_len"][t], res["bonus"][t], res["last_row"][t] = acc, bonus, last
         res["surv_sum"][t] = sum(surv_all[i] for i in forest.tree_rows[t] if forest.parent[i] != -1)
     if keep_logits:

@@ -197,3 +197,37 @@ def test_random_forests_mask_matches_sdpa(choices, plen, seed):
             q[None, :, None], keys.permute(1, 0, 2).repeat_interleave(2, 0)[None],
             vals.permute(1, 0, 2).repeat_interleave(2, 0)[None], attn_mask=mask[None, None, None])
         np.testing.assert_allclose(att[i], o[0, :, 0].numpy(), atol=1e-12)
+
+
+def test_stochastic_mode_with_certain_accepts_draws_bonus_from_last_row():
+    # u_accept = 0 accepts every draft with p(d) > 0 (all of them under a
+    # softmax), so the walk reaches the leaf and draws from its distribution
+    inp = W.make_inputs(1, 0)
+    W.sample_tree_drafts(inp)
+    u_acc, u_bonus = W.make_uniforms(inp)
+    d = dict(O.inp_dict(inp))
+    d["mode"], d["u_accept"], d["u_bonus"] = 1, np.zeros_like(u_acc), u_bonus
+    res = O.verify(O.cfg_dict(inp.cfg), d, keep_logits=True)
+    n = inp.st.n_rows
+    assert res["accept_len"][0] == n and res["last_row"][0] == n - 1
+    t, _ = O.sample_inverse_cdf(O.softmax(res["logits"][n - 1]), float(u_bonus[0]))
+    assert res["bonus"][0] == t
+    # greedy outputs of the other steps are unchanged by the mode
+    g = O.verify(O.cfg_dict(inp.cfg), O.inp_dict(inp))
+    np.testing.assert_array_equal(res["argmax"], g["argmax"])
+    np.testing.assert_allclose(res["overlap"], g["overlap"])
+
+
+def test_stochastic_mode_on_a_chain_batch_matches_per_tree_walks():
+    inp = W.make_inputs(1, 1)
+    W.sample_tree_drafts(inp)
+    u_acc, u_bonus = W.make_uniforms(inp)
+    d = dict(O.inp_dict(inp))
+    d["mode"], d["u_accept"], d["u_bonus"] = 1, u_acc, u_bonus
+    res = O.verify(O.cfg_dict(inp.cfg), d, keep_logits=True)
+    f = O.Forest(inp.st.parent)
+    lg = res["logits"]
+    dl = O.decode(inp.drafter_logits, "f32")
+    acc, bonus, last, _ = O.stochastic_walk(f, 0, lambda i: O.softmax(lg[i]), lambda i: O.softmax(dl[f.draft_index[i]]),
+                                            inp.draft_ids, u_acc, float(u_bonus[0]))
+    assert (res["accept_len"][0], res["bonus"][0], res["last_row"][0]) == (acc, bonus, last)
