@@ -108,6 +108,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5],
                     help="1 chain-tiny, 2 chain-8b, 3 block-27b-b16, 4 tree-specopd, 5 conc32-27b (default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sample", action="store_true",
+                    help="T = 1 stochastic verification (drafts drawn from the drafter, seeded uniforms)")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -139,12 +141,14 @@ def main() -> int:
     # accepted prefix k ~ U{0..gamma} on the target's greedy tokens (taken from
     # a first run of this same step)
     planted = None
-    if cfg.kind == "tree":
+    if cfg.kind == "tree" or args.sample:
         W.sample_tree_drafts(inp)
     else:
         dc.run()
         g = dc.results()["argmax"]
         planted = W.plant_chain_drafts(inp, g)
+    if args.sample:
+        dc.set_uniforms(W.make_uniforms(inp))
     dc.refresh()
 
     log(f"[bench] warmup {args.warmup}")
@@ -219,7 +223,8 @@ def main() -> int:
         "data": "synthetic (seeded; random-init weights of the stated shapes)",
         "config": {"workload": cfg.name, "rows": n, "trees": st.n_roots, "kv_tokens": int(st.kv_tokens),
                    "heads_q_kv": [cfg.n_q_heads, cfg.n_kv_heads], "head_dim": cfg.head_dim,
-                   "hidden": cfg.hidden, "vocab": cfg.vocab, "gamma": cfg.gamma, "seed": args.seed},
+                   "hidden": cfg.hidden, "vocab": cfg.vocab, "gamma": cfg.gamma, "seed": args.seed,
+                   "acceptance": "T=1 sampling" if args.sample else "greedy"},
         "roofline": roof,
         "step": {"algorithmic_bytes": sb["total"], "algorithmic_flops": sf["total"],
                  "device_ms_staged": stages.get("step"), "ms_per_step_staged": ms_staged,

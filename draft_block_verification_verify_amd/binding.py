@@ -36,7 +36,11 @@ class SvInputs(C.Structure):
                 ("kv_tokens", C.c_int64),
                 ("kv_k", C.c_void_p), ("kv_v", C.c_void_p),
                 ("q_rows", C.c_void_p), ("k_rows", C.c_void_p), ("v_rows", C.c_void_p),
-                ("draft_ids", C.c_void_p), ("drafter_logits", C.c_void_p)]
+                ("draft_ids", C.c_void_p), ("drafter_logits", C.c_void_p),
+                ("mode", C.c_int32), ("u_accept", C.c_void_p), ("u_bonus", C.c_void_p)]
+
+
+SV_MODE_GREEDY, SV_MODE_SAMPLE = 0, 1
 
 
 class SvOutputs(C.Structure):
@@ -174,7 +178,8 @@ class Verifier:
 
     @staticmethod
     def make_structs(parent, pos, root_kv_off, root_kv_len, kv_k, kv_v, q_rows, k_rows, v_rows,
-                     draft_ids, drafter_logits, outs: dict):
+                     draft_ids, drafter_logits, outs: dict, mode: int = SV_MODE_GREEDY, u_accept=None,
+                     u_bonus=None):
         """Build (SvInputs, SvOutputs, keepalive) from host arrays and device tensors."""
         parent, pos = host_i32(parent), host_i32(pos)
         root_kv_off, root_kv_len = host_i64(root_kv_off), host_i32(root_kv_len)
@@ -186,7 +191,7 @@ class Verifier:
                        root_kv_off.ctypes.data_as(C.POINTER(C.c_int64)),
                        root_kv_len.ctypes.data_as(C.POINTER(C.c_int32)), kv_tokens,
                        _ptr(kv_k), _ptr(kv_v), _ptr(q_rows), _ptr(k_rows), _ptr(v_rows),
-                       _ptr(draft_ids), _ptr(drafter_logits))
+                       _ptr(draft_ids), _ptr(drafter_logits), int(mode), _ptr(u_accept), _ptr(u_bonus))
         o = SvOutputs(*[_ptr(outs.get(k)) for k, _ in SvOutputs._fields_])
         keep = (parent, pos, root_kv_off, root_kv_len)
         return inp, o, keep

@@ -22,7 +22,7 @@ sv_status fail(sv_status st, std::string msg) {
 
 constexpr int kRing = 4;          // pinned metadata staging slots
 constexpr int kDChunk = 8192;     // vocabulary chunk of the drafter-stats pass
-constexpr int kOChunk = 8192;     // vocabulary chunk of the overlap pass
+constexpr int kOChunk = 8192;     // vocabulary chunk of the overlap pass and of the T = 1 draw
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -55,6 +55,8 @@ struct sv_handle {
   float2 *dpart = nullptr;
   int64_t slot_cap = 0;
   int n_tiles_cap = 0, n_dch = 0, n_och = 0;
+  int32_t *rej_child = nullptr;    // T = 1 mode: per tree
+  float *rpart = nullptr;          // T = 1 mode: [max_roots, n_och]
   size_t h_part_floats = 0;
   std::vector<void *> allocs;
   // completion / profiling
@@ -177,6 +179,8 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
   A(&h->dpart, size_t(R * h->n_dch * 8));
   A(&h->lse_q, size_t(R * 4));
   A(&h->opart, size_t(R * h->n_och * 4));
+  A(&h->rej_child, size_t(dm.max_roots) * 4);
+  A(&h->rpart, size_t(dm.max_roots) * h->n_och * 4);
   if (dm.dtype == SV_BF16) {
     // the projections run on fp16 MFMA: keep fp16 copies of the weights
     uint16_t *wo16 = nullptr, *wlm16 = nullptr;
@@ -310,6 +314,16 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     return fail(SV_ERR_INVALID_ARG, "q_rows, k_rows, v_rows and draft_ids must be non-null device pointers");
   if (plan.n_draft > 0 && !in->drafter_logits)
     return fail(SV_ERR_INVALID_ARG, "drafter_logits must be non-null when the block has draft rows");
+  if (in->mode != SV_MODE_GREEDY && in->mode != SV_MODE_SAMPLE)
+    return fail(SV_ERR_INVALID_ARG, "mode must be SV_MODE_GREEDY or SV_MODE_SAMPLE");
+  if (in->mode == SV_MODE_SAMPLE) {
+    if (!in->u_accept || !in->u_bonus)
+      return fail(SV_ERR_INVALID_ARG, "SV_MODE_SAMPLE needs u_accept and u_bonus");
+    if (!plan.chains_only)
+      return fail(SV_ERR_UNSUPPORTED, "SV_MODE_SAMPLE takes chains: a row has more than one child");
+    if (h->n_och > 1024)
+      return fail(SV_ERR_UNSUPPORTED, "SV_MODE_SAMPLE supports vocabularies up to 8388608 tokens");
+  }
   if (in->kv_tokens > 0 && (!in->kv_k || !in->kv_v))
     return fail(SV_ERR_INVALID_ARG, "kv_k and kv_v must be non-null when kv_tokens > 0");
   if (!out->accept_len || !out->bonus || !out->last_row || !out->surv_sum || !out->argmax || !out->row_max ||
@@ -355,6 +369,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   const int32_t *row_parent = reinterpret_cast<const int32_t *>(m + lay.row_parent);
   const int32_t *row_draft = reinterpret_cast<const int32_t *>(m + lay.row_draft);
   const uint64_t *row_anc = reinterpret_cast<const uint64_t *>(m + lay.row_anc);
+  const int32_t *row_child = reinterpret_cast<const int32_t *>(m + lay.row_child);
   const int32_t *draft_row = reinterpret_cast<const int32_t *>(m + lay.draft_row);
   const int32_t *tree_start = reinterpret_cast<const int32_t *>(m + lay.tree_start);
   const int32_t *tree_rows = reinterpret_cast<const int32_t *>(m + lay.tree_rows);
@@ -564,6 +579,17 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   begin("accept");
   sv::launch_accept(va, stream);
   end();
+  if (in->mode == SV_MODE_SAMPLE) {
+    sv::SampleArgs sa{};
+    sa.row_child = row_child;
+    sa.u_accept = in->u_accept;
+    sa.u_bonus = in->u_bonus;
+    sa.rej_child = h->rej_child;
+    sa.rpart = h->rpart;
+    begin("sample");
+    sv::launch_sample(va, sa, stream);
+    end();
+  }
   if (h->profile == 1) (void)hipEventRecord(h->stages[step_stage].b, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail("kernel launch", e);

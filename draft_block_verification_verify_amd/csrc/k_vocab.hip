@@ -215,6 +215,237 @@ __global__ __launch_bounds__(64) void accept_kernel(VocabArgs a) {
   }
 }
 
+// ----------------------------------------------------------------------------
+// T = 1 stochastic verification of chains.  One thread walks each chain (at
+// most 64 rows): the draft d of child c of row cur is accepted when
+// u_accept[c] * q_c(d) < p_cur(d).  The bonus weights of the stop row are
+// max(0, p_cur - q_c) after a rejection of child c, or p_cur after a leaf.
+// The draw sums them per 8192-token chunk (coalesced, fixed order), then
+// selects by prefix sums: the chunk, the 32-token segment inside it and the
+// token inside that, each the first with weight whose running total passes
+// the remaining target (u_bonus times the total weight).  Where rounding puts
+// the target past every prefix, the last entry with weight is taken.  All
+// orders are fixed, so repeated runs draw the same token.
+// ----------------------------------------------------------------------------
+
+constexpr int kSampChunk = 8192;   // tokens per chunk
+
+__device__ __forceinline__ float drafter_at(const VocabArgs &a, int draft, int u) {
+  return load1(a.drafter, a.drafter_bf16, int64_t(draft) * a.V + u);
+}
+
+__global__ __launch_bounds__(64) void swalk_kernel(VocabArgs a, SampleArgs sa) {
+  const int r = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  int cur = a.tree_start[r], acc = 0;
+  int c;
+  while ((c = sa.row_child[cur]) >= 0) {
+    const int d = a.draft_ids[c];
+    const float pd = __expf(a.logits[int64_t(cur) * a.V + d] - a.row_lse[cur]);
+    const int dr = a.row_draft[c];
+    const float qd = __expf(drafter_at(a, dr, d) - a.lse_q[dr]);
+    if (!(sa.u_accept[c] * qd < pd)) break;
+    cur = c;
+    ++acc;
+  }
+  a.accept_len[r] = acc + 1;
+  a.last_row[r] = cur;
+  sa.rej_child[r] = sa.row_child[cur];
+}
+
+// Bonus weights of one stop row: p_stop(u), or max(0, p_stop(u) - q_c(u))
+// after the rejection of child c (rej = c; -1 after a leaf).
+struct BonusRow {
+  const float *lp;      // logits of the stop row
+  const void *lq;       // drafter logits of the rejected child (resid only)
+  float lse_p, lse_q;
+  bool resid;
+};
+
+__device__ __forceinline__ BonusRow bonus_row(const VocabArgs &a, int stop, int rej) {
+  BonusRow b;
+  b.lp = a.logits + int64_t(stop) * a.V;
+  b.lse_p = a.row_lse[stop];
+  b.resid = rej >= 0;
+  const int dr = b.resid ? a.row_draft[rej] : 0;
+  b.lq = a.drafter_bf16 ? static_cast<const void *>(static_cast<const uint16_t *>(a.drafter) + int64_t(dr) * a.V)
+                        : static_cast<const void *>(static_cast<const float *>(a.drafter) + int64_t(dr) * a.V);
+  b.lse_q = b.resid ? a.lse_q[dr] : 0.f;
+  return b;
+}
+
+constexpr int kSampPer = kSampChunk / 256;   // tokens per thread in a chunk
+
+// weights of tokens base + tid + 256 j, j < kSampPer (0 past the vocabulary);
+// every load is issued before the arithmetic
+__device__ __forceinline__ void chunk_weights(const VocabArgs &a, const BonusRow &b, int base,
+                                              float (&w)[kSampPer]) {
+  float lg[kSampPer];
+#pragma unroll
+  for (int j = 0; j < kSampPer; ++j) {
+    const int u = base + int(threadIdx.x) + 256 * j;
+    lg[j] = u < a.V ? b.lp[u] : -INFINITY;
+  }
+  if (b.resid) {
+    float lq[kSampPer];
+#pragma unroll
+    for (int j = 0; j < kSampPer; ++j) {
+      const int u = min(base + int(threadIdx.x) + 256 * j, a.V - 1);
+      lq[j] = load1(b.lq, a.drafter_bf16, u);
+    }
+#pragma unroll
+    for (int j = 0; j < kSampPer; ++j)
+      w[j] = fmaxf(__expf(lg[j] - b.lse_p) - __expf(lq[j] - b.lse_q), 0.f);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kSampPer; ++j) w[j] = __expf(lg[j] - b.lse_p);
+  }
+}
+
+// chunk sum: thread t adds its weights in j order, then the block adds the
+// thread sums in a fixed tree (sum_block256)
+__device__ __forceinline__ float chunk_sum(const VocabArgs &a, const BonusRow &b, int k) {
+  float w[kSampPer];
+  chunk_weights(a, b, k * kSampChunk, w);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kSampPer; ++j) s += w[j];
+  return sum_block256(s);
+}
+
+__global__ __launch_bounds__(256) void residual_partial_kernel(VocabArgs a, SampleArgs sa) {
+  const int k = blockIdx.x, r = blockIdx.y;
+  const float s = chunk_sum(a, bonus_row(a, a.last_row[r], sa.rej_child[r]), k);
+  if (threadIdx.x == 0) sa.rpart[int64_t(r) * a.n_och + k] = s;
+}
+
+// inclusive prefix sum over the 64 lanes of a wave (Kogge-Stone order)
+__device__ __forceinline__ float wave_incl_scan(float v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int first_lane(uint64_t m) { return __builtin_ctzll(m); }
+__device__ __forceinline__ int last_lane(uint64_t m) { return 63 - __builtin_clzll(m); }
+
+// Select among n weights w[0..n) (LDS, n <= 64 * passes) by one wave: the
+// first index with positive weight whose inclusive prefix exceeds `target`,
+// else the last index with positive weight, else -1.  Writes the chosen
+// index and the target less the prefix before it (clamped to the index's
+// weight) through lane 0.
+__device__ __forceinline__ void wave_select(const float *w, int n, float target, int *sel, float *rest) {
+  const int lane = threadIdx.x & 63;
+  float carry = 0.f;
+  int found = -1, last = -1;
+  float excl = 0.f;
+  for (int b = 0; b < n && found < 0; b += 64) {
+    const int i = b + lane;
+    const float x = i < n ? w[i] : 0.f;
+    const float S = carry + wave_incl_scan(x);
+    const uint64_t hit = __ballot(x > 0.f && S > target);
+    const uint64_t pos = __ballot(x > 0.f);
+    if (hit) {
+      const int f = first_lane(hit);
+      found = b + f;
+      excl = __shfl(S - x, f, 64);
+    } else if (pos) {
+      last = b + last_lane(pos);
+    }
+    carry = __shfl(S, 63, 64);
+  }
+  if (lane == 0) {
+    if (found >= 0) {
+      *sel = found;
+      *rest = fminf(fmaxf(target - excl, 0.f), w[found]);
+    } else {
+      *sel = last;
+      *rest = last >= 0 ? w[last] : 0.f;
+    }
+  }
+}
+
+// Draw: one workgroup per tree.  With zero residual mass the weights fall
+// back to p of the stop row (chunk sums then recomputed here).
+__global__ __launch_bounds__(256) void sample_kernel(VocabArgs a, SampleArgs sa) {
+  __shared__ float w_lds[kSampChunk];
+  __shared__ float part[256];
+  __shared__ float zc[1024];
+  __shared__ int sh_sel, sh_tok;
+  __shared__ float sh_rest, sh_rest2;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int stop = a.last_row[r];
+  const int rej0 = sa.rej_child[r];
+  const float *rp = sa.rpart + int64_t(r) * a.n_och;
+  float zl = 0.f;
+  for (int k = tid; k < a.n_och; k += 256) {
+    const float x = rp[k];
+    zc[k] = x;
+    zl += x;
+  }
+  float Z = sum_block256(zl);
+  const int rej = Z > 0.f ? rej0 : -1;
+  const BonusRow br = bonus_row(a, stop, rej);
+  if (rej != rej0) {   // zero residual mass: weights p of the stop row
+    for (int k = 0; k < a.n_och; ++k) {
+      const float x = chunk_sum(a, br, k);
+      if (tid == 0) zc[k] = x;
+    }
+    __syncthreads();
+    zl = 0.f;
+    for (int k = tid; k < a.n_och; k += 256) zl += zc[k];
+    Z = sum_block256(zl);
+  }
+  __syncthreads();
+  if (tid < 64) wave_select(zc, a.n_och, sa.u_bonus[r] * Z, &sh_sel, &sh_rest);
+  __syncthreads();
+  const int chunk = max(sh_sel, 0);
+  const float target = sh_rest;
+  const int base = chunk * kSampChunk;
+  {
+    float w[kSampPer];
+    chunk_weights(a, br, base, w);
+#pragma unroll
+    for (int j = 0; j < kSampPer; ++j) w_lds[tid + 256 * j] = w[j];
+  }
+  __syncthreads();
+  {   // token-order segments of 32
+    const float4 *w4 = reinterpret_cast<const float4 *>(w_lds + tid * 32);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float4 x = w4[j];
+      s += x.x;
+      s += x.y;
+      s += x.z;
+      s += x.w;
+    }
+    part[tid] = s;
+  }
+  __syncthreads();
+  if (tid < 64) wave_select(part, 256, target, &sh_sel, &sh_rest);
+  __syncthreads();
+  if (tid < 64) {
+    const int seg = sh_sel;
+    if (seg < 0) {   // no weight in the chunk (only with no mass at all)
+      if (tid == 0) a.bonus[r] = min(base, a.V - 1);
+      return;
+    }
+    wave_select(w_lds + seg * 32, 32, sh_rest, &sh_tok, &sh_rest2);
+    if (tid == 0) a.bonus[r] = base + seg * 32 + max(sh_tok, 0);
+  }
+}
+
+void launch_sample(const VocabArgs &a, const SampleArgs &sa, hipStream_t s) {
+  hipLaunchKernelGGL(swalk_kernel, dim3(a.R), dim3(64), 0, s, a, sa);
+  hipLaunchKernelGGL(residual_partial_kernel, dim3(a.n_och, a.R), dim3(256), 0, s, a, sa);
+  hipLaunchKernelGGL(sample_kernel, dim3(a.R), dim3(256), 0, s, a, sa);
+}
+
 void launch_drafter_partial(const VocabArgs &a, hipStream_t s) {
   if (a.n_draft == 0) return;
   hipLaunchKernelGGL(drafter_partial_kernel, dim3(a.n_dch, a.n_draft), dim3(256), 0, s, a);

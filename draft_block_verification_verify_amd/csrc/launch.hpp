@@ -111,6 +111,16 @@ struct VocabArgs {
   int32_t *argmax, *accept_len, *bonus, *last_row;
   float *row_max, *row_lse, *overlap, *survival, *surv_sum;
 };
+// T = 1 stochastic verification of chains (see sv_mode in spec_verify.h).
+struct SampleArgs {
+  const int32_t *row_child;     // [n] the row's child or -1
+  const float *u_accept;        // [n]
+  const float *u_bonus;         // [R]
+  int32_t *rej_child;           // [R] rejected child of the stop row, -1 after a leaf
+  float *rpart;                 // [R, n_och] canonical chunk sums of the bonus weights
+};
+void launch_sample(const VocabArgs &a, const SampleArgs &sa, hipStream_t s);
+
 void launch_drafter_partial(const VocabArgs &a, hipStream_t s);
 void launch_row_combine(const VocabArgs &a, hipStream_t s);
 void launch_overlap_partial(const VocabArgs &a, hipStream_t s);

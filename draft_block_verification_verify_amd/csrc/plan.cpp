@@ -81,6 +81,7 @@ MetaLayout meta_layout(int n, int R, int n_draft, int n_items, int n_groups) {
   L.row_parent = take(4 * size_t(n));
   L.row_draft = take(4 * size_t(n));
   L.row_anc = take(8 * size_t(n));
+  L.row_child = take(4 * size_t(n));
   L.draft_row = take(4 * size_t(std::max(n_draft, 1)));
   L.tree_start = take(4 * size_t(R));
   L.tree_rows = take(4 * size_t(R));
@@ -176,6 +177,14 @@ int build_plan(const Dims &dm, const HostInputs &in, int64_t slot_cap, int targe
     } else {
       P.row_draft[i] = int32_t(P.draft_row.size());
       P.draft_row.push_back(i);
+    }
+  }
+  P.row_child.assign(n, -1);
+  for (int i = 0; i < n; ++i) {
+    const int p = P.row_parent[i];
+    if (p >= 0) {
+      if (P.row_child[p] >= 0) P.chains_only = false;
+      P.row_child[p] = i;
     }
   }
   P.R = tree + 1;
@@ -296,6 +305,7 @@ void pack_plan(const Plan &p, int Hkv, void *dst, MetaLayout *lay) {
   put(L.row_parent, p.row_parent.data(), 4 * size_t(p.n));
   put(L.row_draft, p.row_draft.data(), 4 * size_t(p.n));
   put(L.row_anc, p.row_anc.data(), 8 * size_t(p.n));
+  put(L.row_child, p.row_child.data(), 4 * size_t(p.n));
   put(L.draft_row, p.draft_row.data(), 4 * size_t(p.n_draft));
   put(L.tree_start, p.tree_start.data(), 4 * size_t(p.R));
   put(L.tree_rows, p.tree_rows.data(), 4 * size_t(p.R));

@@ -50,6 +50,8 @@ struct Plan {
   // per row
   std::vector<int32_t> row_tree, row_local, row_pos, row_parent, row_draft;
   std::vector<uint64_t> row_anc;     // ancestor-or-self bits, tree-local
+  std::vector<int32_t> row_child;    // the row's child, -1 if none (last one if several)
+  bool chains_only = true;           // no row has more than one child
   // per draft row: its global row
   std::vector<int32_t> draft_row;
   // per tree
@@ -80,7 +82,7 @@ int64_t slot_capacity(const Dims &dm);
 
 // Byte layout of the device copy of a plan (offsets into one buffer).
 struct MetaLayout {
-  size_t row_tree, row_local, row_pos, row_parent, row_draft, row_anc, draft_row;
+  size_t row_tree, row_local, row_pos, row_parent, row_draft, row_anc, row_child, draft_row;
   size_t tree_start, tree_rows, tree_kv_len, tree_kv_off;
   size_t items, group_first, group_count;
   size_t total;

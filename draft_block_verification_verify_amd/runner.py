@@ -32,7 +32,8 @@ class DeviceCase:
     """A workload resident on the GPU plus a handle ready to run it."""
 
     def __init__(self, inp: Inputs, device="cuda:0", *, with_logits: bool = False, verifier=None,
-                 weights=None, max_rows: int | None = None, max_roots: int | None = None):
+                 weights=None, max_rows: int | None = None, max_roots: int | None = None,
+                 uniforms=None):
         import torch
         self.inp = inp
         cfg, st = inp.cfg, inp.st
@@ -55,6 +56,17 @@ class DeviceCase:
                                   self.w_o, self.w_lm)
         self.ver = verifier
         self.outs = verifier.alloc_outputs(st.n_rows, st.n_roots, self.device, with_logits)
+        self.set_uniforms(uniforms)
+
+    def set_uniforms(self, uniforms):
+        """(u_accept, u_bonus) host arrays switch the runs to T = 1 stochastic
+        verification; None switches back to greedy."""
+        import torch
+        if uniforms is None:
+            self.u_accept = self.u_bonus = None
+        else:
+            self.u_accept = torch.from_numpy(np.ascontiguousarray(uniforms[0], np.float32)).to(self.device)
+            self.u_bonus = torch.from_numpy(np.ascontiguousarray(uniforms[1], np.float32)).to(self.device)
         self.refresh()
 
     def refresh(self):
@@ -64,7 +76,8 @@ class DeviceCase:
         self.draft_ids = torch.from_numpy(np.ascontiguousarray(self.inp.draft_ids, np.int32)).to(self.device)
         self.sv_in, self.sv_out, self._keep = B.Verifier.make_structs(
             st.parent, st.pos, st.root_kv_off, st.root_kv_len, self.kv_k, self.kv_v, self.q, self.k,
-            self.v, self.draft_ids, self.dl, self.outs)
+            self.v, self.draft_ids, self.dl, self.outs,
+            B.SV_MODE_SAMPLE if self.u_accept is not None else B.SV_MODE_GREEDY, self.u_accept, self.u_bonus)
         if self.kv_k is None:
             self.sv_in.kv_tokens = 0
 

@@ -48,6 +48,20 @@ typedef enum sv_status {
 
 typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 
+/* Acceptance rule of a run.  SV_MODE_GREEDY: a draft is accepted when it
+ * equals the target's greedy token at its parent.  SV_MODE_SAMPLE: T = 1
+ * stochastic verification of chains (every row has at most one child): the
+ * draft d of row c with parent cur is accepted when u_accept[c] * q_c(d) <
+ * p_cur(d), p and q the target and drafter softmaxes; the walk stops at the
+ * first rejection and draws the bonus token from max(0, p_cur - q_c), or,
+ * after a leaf, from p_cur, by inverse CDF at u_bonus (the smallest token
+ * whose running weight exceeds u_bonus times the total weight; from p_cur
+ * if the residual has no mass).  The pages evaluate T = 1 sampling
+ * (Dev.to/aiwithghost DSpine page, temperature section; SpecOPD summary,
+ * "premises and limits") and state its per-position acceptance probability
+ * alpha = 1 - D_TV (VESSL part 2, DSpark section), which this rule has. */
+typedef enum sv_mode { SV_MODE_GREEDY = 0, SV_MODE_SAMPLE = 1 } sv_mode;
+
 /* Model shape and capacities, fixed for the handle's lifetime. */
 typedef struct sv_config {
   int32_t n_q_heads;     /* Hq; a multiple of n_kv_heads                       */
@@ -86,12 +100,16 @@ typedef struct sv_inputs {
   const void *v_rows;          /* DEVICE [n_rows, Hkv, d]                       */
   const int32_t *draft_ids;    /* DEVICE [n_rows] token at each row; roots ignored */
   const void *drafter_logits;  /* DEVICE [n_rows - n_roots, V]                  */
+  int32_t mode;                /* sv_mode; 0 (greedy) when zero-initialised     */
+  const float *u_accept;       /* DEVICE [n_rows] uniforms in [0, 1), SV_MODE_SAMPLE only; roots ignored */
+  const float *u_bonus;        /* DEVICE [n_roots] uniforms in [0, 1), SV_MODE_SAMPLE only */
 } sv_inputs;
 
 /* Outputs, all DEVICE memory written by the run.  `logits` may be NULL. */
 typedef struct sv_outputs {
   int32_t *accept_len;  /* [n_roots] accepted drafts + 1 (bonus), in [1, depth+1] */
-  int32_t *bonus;       /* [n_roots] greedy token of the last accepted row          */
+  int32_t *bonus;       /* [n_roots] bonus token: greedy token of the last accepted
+                           row, or (SV_MODE_SAMPLE) the draw described at sv_mode */
   int32_t *last_row;    /* [n_roots] last accepted row (global row index)           */
   float *surv_sum;      /* [n_roots] sum of survival over the tree's non-root rows  */
   int32_t *argmax;      /* [n_rows] greedy token (lowest id among equal maxima)     */
@@ -115,6 +133,9 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
                              sv_handle **out);
 
 /* Enqueue one verify step on `stream` (hipStream_t; NULL = default stream).
+ * in->mode selects the acceptance rule (sv_mode); SV_MODE_SAMPLE needs
+ * u_accept and u_bonus and fails with SV_ERR_UNSUPPORTED when a row has
+ * more than one child.
  * Host arrays are read and copied before the call returns; device inputs and
  * outputs must stay valid until the stream passes the enqueued work.  Never
  * synchronises the host with the device.  Every argument, tree and capacity

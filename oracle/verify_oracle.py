@@ -50,8 +50,8 @@ from their fp32 / bf16 bits):
    rejection the bonus token is drawn from max(0, p_cur - q_c), and when the
    walk reaches a leaf it is drawn from p_cur, both by the inverse CDF at
    u_bonus (the smallest token whose running weight exceeds u_bonus times
-   the total).  The uniforms are inputs.  Trees with branching nodes are not
-   taken in this mode.
+   the total; a residual without mass falls back to p_cur).  The uniforms
+   are inputs.  Trees with branching nodes are not taken in this mode.
 """
 from __future__ import annotations
 
@@ -267,7 +267,8 @@ def stochastic_walk(forest: Forest, root: int, p_of, q_of, draft_ids, u_accept, 
         if lhs < rhs:
             cur, acc = c, acc + 1
             continue
-        t, m = sample_inverse_cdf(np.maximum(p - q, 0.0), u_bonus)
+        resid = np.maximum(p - q, 0.0)
+        t, m = sample_inverse_cdf(resid if resid.sum() > 0 else p, u_bonus)
         return acc + 1, t, cur, min(margin, m)
 
 

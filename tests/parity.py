@@ -38,8 +38,9 @@ def tree_ranges(parent):
     return list(zip(roots, roots[1:] + [len(parent)]))
 
 
-def check_self_consistency(parent, drafts, gpu):
-    """Properties that hold at any size, from the GPU outputs alone."""
+def check_self_consistency(parent, drafts, gpu, greedy=True):
+    """Properties that hold at any size, from the GPU outputs alone (the
+    greedy walk only when `greedy`)."""
     parent = np.asarray(parent)
     n = len(parent)
     ov, sv = gpu["overlap"], gpu["survival"]
@@ -53,8 +54,9 @@ def check_self_consistency(parent, drafts, gpu):
             surv[i - s] = surv[parent[i] - s] * np.float64(ov[i])
         np.testing.assert_allclose(sv[s:e], surv, rtol=1e-5, atol=1e-7)
         assert abs(gpu["surv_sum"][t] - surv[1:].sum()) <= 1e-5 * max(1.0, surv[1:].sum()) + 1e-6
-        acc, bonus, last = walk(parent, s, e, gpu["argmax"], drafts)
-        assert (gpu["accept_len"][t], gpu["bonus"][t], gpu["last_row"][t]) == (acc, bonus, last), t
+        if greedy:
+            acc, bonus, last = walk(parent, s, e, gpu["argmax"], drafts)
+            assert (gpu["accept_len"][t], gpu["bonus"][t], gpu["last_row"][t]) == (acc, bonus, last), t
         depth = 0
         for i in range(s + 1, e):
             d, j = 0, i
@@ -65,9 +67,10 @@ def check_self_consistency(parent, drafts, gpu):
     assert n == len(gpu["argmax"])
 
 
-def compare(ref, gpu, parent, drafts, rows=None, logits_ref=None, logits_gpu=None, report=None):
+def compare(ref, gpu, parent, drafts, rows=None, logits_ref=None, logits_gpu=None, report=None, greedy=True):
     """Element-wise parity of the rows in `rows` (default all) and the trees
-    that contain them.  Returns a dict of the worst errors."""
+    that contain them (their greedy acceptance outputs when `greedy`).
+    Returns a dict of the worst errors."""
     parent = list(np.asarray(parent))
     n = len(parent)
     rows = list(range(n)) if rows is None else list(rows)
@@ -110,6 +113,8 @@ def compare(ref, gpu, parent, drafts, rows=None, logits_ref=None, logits_gpu=Non
         if not all(i in rs for i in range(s, e)):
             continue
         assert abs(float(gpu["surv_sum"][t]) - ref["surv_sum"][t]) <= OV_ABS * (e - s), (t, gpu["surv_sum"][t], ref["surv_sum"][t])
+        if not greedy:
+            continue
         # rows the oracle's walk consults: accepted rows (their argmax decides)
         acc, bonus, last = int(ref["accept_len"][t]), int(ref["bonus"][t]), int(ref["last_row"][t])
         path = []
@@ -121,6 +126,90 @@ def compare(ref, gpu, parent, drafts, rows=None, logits_ref=None, logits_gpu=Non
             assert (int(gpu["accept_len"][t]), int(gpu["bonus"][t]), int(gpu["last_row"][t])) == (acc, bonus, last), t
         else:
             worst["near_ties"] += 1
+    if report is not None:
+        report.update(worst)
+    return worst
+
+
+def _softmax64(x):
+    x = np.asarray(x, np.float64)
+    e = np.exp(x - x.max())
+    return e / e.sum()
+
+
+def check_sample(parent, drafts, u_accept, u_bonus, logits_ref, drafter_ref, gpu, trees=None, report=None):
+    """T = 1 acceptance outputs of the GPU against the oracle's fp64
+    distributions.  Along the GPU's walk, each accept test u * q(d) < p(d)
+    must go the oracle's way unless the two sides are within the logit
+    tolerance of each other in log terms (|ln(u q) - ln p| <= 2 LOGIT_REL
+    max(|l_d|, rms of the row's logits): the test then may go either way);
+    the walk must stop where the oracle rejects (or at a leaf), and the bonus
+    token t must satisfy C(t-1) - tol <= u_bonus <= C(t) + tol for the
+    oracle's normalised running weights C of the GPU's stop row, with tol =
+    OV_ABS (a CDF value is a sum of probabilities, like the overlap).
+    `drafter_ref[k]` are the drafter logits of the k-th draft row.  Returns
+    the number of trees whose walk had no near decision and matched
+    `ref`-style exact outputs."""
+    parent = list(np.asarray(parent))
+    n = len(parent)
+    child = [-1] * n
+    for i, p in enumerate(parent):
+        if p >= 0:
+            assert child[p] < 0, "chains only"
+            child[p] = i
+    draft_index = {}
+    for i, p in enumerate(parent):
+        if p >= 0:
+            draft_index[i] = len(draft_index)
+    worst = {"near_decisions": 0, "draw_slack": 0.0, "walks": 0}
+    for t, (s, e) in enumerate(tree_ranges(parent)):
+        if trees is not None and t not in trees:
+            continue
+        acc, last, bonus = int(gpu["accept_len"][t]), int(gpu["last_row"][t]), int(gpu["bonus"][t])
+        cur, k = s, 0
+
+        def decision(cur, c):
+            lc = np.asarray(logits_ref[cur], np.float64)
+            d = int(drafts[c])
+            p = _softmax64(lc)[d]
+            q = _softmax64(drafter_ref[draft_index[c]])[d]
+            lhs, rhs = float(u_accept[c]) * q, p
+            rms = float(np.sqrt(np.mean(lc * lc)))
+            delta = 2 * LOGIT_REL * max(abs(float(lc[d])), rms)
+            if lhs == 0.0:
+                return True, True
+            near = abs(np.log(lhs) - np.log(rhs)) <= delta
+            return lhs < rhs, not near
+
+        while k < acc - 1:
+            c = child[cur]
+            assert c >= 0, (t, "GPU walk past a leaf")
+            ok, clear = decision(cur, c)
+            if clear:
+                assert ok, (t, cur, c, "GPU accepted where the oracle rejects")
+            else:
+                worst["near_decisions"] += 1
+            cur, k = c, k + 1
+        assert last == cur, (t, last, cur)
+        c = child[cur]
+        if c >= 0:
+            ok, clear = decision(cur, c)
+            if clear:
+                assert not ok, (t, cur, c, "GPU rejected where the oracle accepts")
+            else:
+                worst["near_decisions"] += 1
+        p = _softmax64(logits_ref[cur])
+        w = np.maximum(p - _softmax64(drafter_ref[draft_index[c]]), 0.0) if c >= 0 else p
+        if w.sum() <= 0:
+            w = p
+        cdf = np.cumsum(w) / w.sum()
+        lo = float(cdf[bonus - 1]) if bonus > 0 else 0.0
+        hi = float(cdf[bonus])
+        u = float(u_bonus[t])
+        slack = max(lo - u, u - hi, 0.0)
+        worst["draw_slack"] = max(worst["draw_slack"], slack)
+        assert slack <= OV_ABS, (t, bonus, lo, u, hi)
+        worst["walks"] += 1
     if report is not None:
         report.update(worst)
     return worst

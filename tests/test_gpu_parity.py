@@ -268,6 +268,83 @@ def test_error_paths_enqueue_nothing():
 
 
 # ----------------------------------------------------------------------------
+# T = 1 stochastic verification (chains)
+# ----------------------------------------------------------------------------
+
+
+def run_sample_case(cfg, seed, sigma=None):
+    """Drafts drawn from the drafter (optionally a drafter correlated with the
+    target: its logits = the target's + N(0, sigma)), seeded uniforms."""
+    from draft_block_verification_verify_amd.runner import DeviceCase
+    _say(f"[sample case] {cfg.name} seed={seed} sigma={sigma}")
+    inp = W.make_inputs(cfg, seed)
+    cd = O.cfg_dict(cfg)
+    if sigma is not None:
+        ref0 = O.verify(cd, O.inp_dict(inp), keep_logits=True)
+        rows = W.draft_rows(inp.st.parent)
+        lg = np.stack([ref0["logits"][inp.st.parent[i]] for i in rows])
+        rng = np.random.default_rng(4321 + seed)
+        q = (lg + rng.standard_normal(lg.shape) * float(sigma)).astype(np.float32)
+        inp.drafter_logits = W.f32_to_bf16_bits(q) if cfg.dtype == "bf16" else q
+    W.sample_tree_drafts(inp)
+    ua, ub = W.make_uniforms(inp)
+    d = dict(O.inp_dict(inp))
+    d.update(mode=1, u_accept=ua, u_bonus=ub)
+    ref = O.verify(cd, d, keep_logits=True)
+    dc = DeviceCase(inp, with_logits=True, uniforms=(ua, ub))
+    dc.run()
+    gpu = dc.results()
+    dc.close()
+    return inp, ref, gpu, ua, ub
+
+
+@pytest.mark.parametrize("name,sigma", [("c1", None), ("c2m", None), ("c3m", 0.4), ("c4m", 0.3),
+                                        ("c5m", 0.5), ("c5s", 0.8), ("c1", 0.3)])
+def test_parity_sample_mode(name, sigma):
+    cfg = MINIS[name]
+    inp, ref, gpu, ua, ub = run_sample_case(cfg, 0, sigma)
+    st = inp.st
+    P.check_self_consistency(st.parent, inp.draft_ids, gpu, greedy=False)
+    rep = {}
+    P.compare(ref, gpu, st.parent, inp.draft_ids, logits_ref=ref["logits"], logits_gpu=gpu["logits"], report=rep,
+              greedy=False)
+    dl = O.decode(inp.drafter_logits, cfg.dtype)
+    rs = P.check_sample(st.parent, inp.draft_ids, ua, ub, ref["logits"], dl, gpu)
+    same = sum(int((gpu["accept_len"][t], gpu["bonus"][t], gpu["last_row"][t]) ==
+                   (ref["accept_len"][t], ref["bonus"][t], ref["last_row"][t])) for t in range(st.n_roots))
+    rep.update(rs)
+    rep["same_as_oracle"] = same / st.n_roots
+    _record(f"{name}/sample{sigma}", rep)
+
+
+def test_sample_mode_refuses_branching_and_bad_mode():
+    import torch
+    from draft_block_verification_verify_amd import binding as B
+    from draft_block_verification_verify_amd.runner import DeviceCase
+    cfg = W.CONFIGS[1]
+    inp = W.make_inputs(cfg, 0)
+    ua, ub = W.make_uniforms(inp)
+    dc = DeviceCase(inp, uniforms=(ua, ub))
+    for v in dc.outs.values():
+        if v is not None:
+            v.fill_(-7)
+    par = inp.st.parent.copy()
+    par[3] = 1                      # rows 2 and 3 both children of row 1
+    inp.st.parent = par
+    dc.refresh()
+    with pytest.raises(B.SpecVerifyError) as e:
+        dc.run()
+    assert e.value.status == B.SV_ERR_UNSUPPORTED
+    dc.sv_in.mode = 5
+    with pytest.raises(B.SpecVerifyError) as e:
+        dc.run()
+    assert e.value.status == B.SV_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert (dc.outs["accept_len"] == -7).all()
+    dc.close()
+
+
+# ----------------------------------------------------------------------------
 # full sizes, in the bench's launch configuration, on sampled trees
 # ----------------------------------------------------------------------------
 
