@@ -37,6 +37,7 @@ struct sv_handle {
   sv_config cfg{};
   sv::Dims dm{};
   const void *w_o = nullptr, *w_lm = nullptr;   // weights the kernels read (fp16 copies for bf16)
+  const void *w_lm_blk = nullptr;               // bf16 and max_rows > 64: fp16 W_lm in the blocked layout
   int32_t *d_bad = nullptr;
   int device = 0, n_cu = 256, target_items = 1024;
   int elt = 2;
@@ -171,7 +172,9 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
   }
   A(&h->o_act, size_t(R * Hq * D * 4));       // fp16 hi + lo planes, fp16, or fp32
   A(&h->h_part, h->h_part_floats * 4);
-  A(&h->hn, size_t(R * H * 4));
+  // normalised rows: fp16 hi + lo planes (<= 64 rows) or the blocked fp16
+  // layout of the tiled LM head (rows padded to 256)
+  A(&h->hn, std::max<size_t>(size_t(R * H * 4), size_t(sv::blocked_elems(R, H) * 2)));
   A(&h->logits, size_t(R * V * 4));
   A(&h->t_max, size_t(R * h->n_tiles_cap * 4));
   A(&h->t_sum, size_t(R * h->n_tiles_cap * 4));
@@ -183,15 +186,23 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
   A(&h->rpart, size_t(dm.max_roots) * h->n_och * 4);
   if (dm.dtype == SV_BF16) {
     // the projections run on fp16 MFMA: keep fp16 copies of the weights
-    uint16_t *wo16 = nullptr, *wlm16 = nullptr;
+    // (row-major; plus W_lm in the blocked layout when runs can take the
+    // tiled LM-head launch)
+    uint16_t *wo16 = nullptr, *wlm16 = nullptr, *wlm_blk = nullptr;
+    const bool tiled = dm.max_rows > 64;
     A(&wo16, size_t(H * Hq * D * 2));
     A(&wlm16, size_t(V * H * 2));
+    if (tiled) A(&wlm_blk, size_t(sv::blocked_elems(V, H) * 2));
     A(&h->d_bad, 4);
     if (st == SV_OK) {
       e = hipMemsetAsync(h->d_bad, 0, 4, nullptr);
+      // padding rows of the blocked activations are read by the LM head:
+      // start them at zero
+      if (e == hipSuccess) e = hipMemsetAsync(h->hn, 0, std::max<size_t>(size_t(R * H * 4), size_t(sv::blocked_elems(R, H) * 2)), nullptr);
       if (e == hipSuccess) {
         sv::launch_bf16_to_f16(static_cast<const uint16_t *>(w_o), wo16, H * Hq * D, h->d_bad, nullptr);
         sv::launch_bf16_to_f16(static_cast<const uint16_t *>(w_lm), wlm16, V * H, h->d_bad, nullptr);
+        if (tiled) sv::launch_bf16_to_f16_blocked(static_cast<const uint16_t *>(w_lm), wlm_blk, int(V), int(H), nullptr);
         e = hipGetLastError();
       }
       int32_t bad = 0;
@@ -206,6 +217,7 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
       }
       h->w_o = wo16;
       h->w_lm = wlm16;
+      h->w_lm_blk = wlm_blk;
     }
   }
   if (st != SV_OK) {
@@ -438,8 +450,9 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   int k_split = 0;
   const int splits = bf16 ? sv::gemm_splits(n, int(H), int(Hq * D), h->n_cu, &k_split) : 1;
   // activation format of the projections: fp16 hi + lo planes for the
-  // skinny launch, fp16 for the tiled one
+  // skinny launch, fp16 for the tiled one (blocked layout for the LM head)
   const int act_mode = n <= 64 ? sv::ACT_SPLIT : sv::ACT_F16;
+  const int lm_act_mode = n <= 64 ? sv::ACT_SPLIT : sv::ACT_F16_BLOCKED;
   const int64_t q_lo = int64_t(dm.max_rows) * Hq * D;   // lo planes start one capacity further
   const int64_t o_lo = int64_t(dm.max_rows) * Hq * D;
   const int64_t h_lo = int64_t(dm.max_rows) * H;
@@ -509,13 +522,13 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     sv::launch_gemm_bf16(g, false, splits, stream);
     end();
     begin("final_norm");
-    sv::launch_norm(h->h_part, splits, int64_t(n) * H, n, int(H), h->cfg.norm_eps, act_mode, h->hn, h_lo, stream);
+    sv::launch_norm(h->h_part, splits, int64_t(n) * H, n, int(H), h->cfg.norm_eps, lm_act_mode, h->hn, h_lo, stream);
     end();
     sv::GemmArgs l{};
     l.act = static_cast<const uint16_t *>(h->hn);
     l.act_lo = l.act + h_lo;
     l.rows = n;
-    l.W = static_cast<const uint16_t *>(h->w_lm);
+    l.W = static_cast<const uint16_t *>(n <= 64 ? h->w_lm : h->w_lm_blk);
     l.N = int(V);
     l.K = int(H);
     l.k_split = int(H);

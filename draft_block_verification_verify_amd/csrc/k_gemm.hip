@@ -242,7 +242,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 // 4-stage LDS ring by DMA (weights 256 rows, then activations 256 rows; 16-B
 // chunk c of row R at slot c ^ ((R >> 1) & 3), so that any 8 consecutive
 // rows of one chunk fall in 8 distinct bank groups), three steps ahead of the
-// MFMAs.  When a tile's K loop ends, the epilogue (per-row max / sumexp /
+// MFMAs.  BLOCKED (the LM head): both operands are stored in that same stage
+// image, block after block, so each DMA instruction reads 1 KB of consecutive
+// bytes; row-strided 64-byte pieces stream markedly slower from HBM and L2
+// together.  When a tile's K loop ends, the epilogue (per-row max / sumexp /
 // argmax of the tile, logit stores) is issued and the first stages of the
 // workgroup's next tile follow at once, so the stores drain while those
 // loads are in flight.  Tile order: tiles i and i+8 share the weight
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 constexpr int kTBN = 256, kTBT = 256, kTST = 4, kTSST = (kTBN + kTBT) * 64;
 constexpr size_t kTiledLds = size_t(kTST) * kTSST;
 
-template <bool STATS>
+template <bool STATS, bool BLOCKED>
 __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
   constexpr int PER = 4;     // DMA instructions per wave per stage (2 weight + 2 activation)
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int R = w * 32 + i * 16 + (lane >> 2);
-    off[i] = R * Kb + ((c4 ^ ((R >> 1) & 3)) << 4);
+    off[i] = BLOCKED ? (w * 32 + i * 16) * 64 + lane * 16 : R * Kb + ((c4 ^ ((R >> 1) & 3)) << 4);
   }
   // tile i -> (weight tile, row tile); i and i+8 share the weight tile
   auto tile_of = [&](int i, int &n_tile, int &t_tile) {
@@ -286,13 +289,21 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
   auto src_of = [&](int n_tile, int t_tile) {
     const int n0 = n_tile * kTBN, t0 = t_tile * kTBT;
     Src r;
-    r.rw = make_rsrc(g.W + int64_t(n0) * g.K, uint32_t(min(kTBN, g.N - n0)) * Kb);
-    r.ra = make_rsrc(g.act + int64_t(t0) * g.K, uint32_t(min(kTBT, g.rows - t0)) * Kb);
+    if constexpr (BLOCKED) {
+      // one column of blocks per 256-row tile; padding rows hold zeros (W)
+      // or values whose outputs are dropped (act)
+      const int64_t tb = int64_t(g.K) * 256;
+      r.rw = make_rsrc(g.W + int64_t(n_tile) * tb, uint32_t(tb * 2));
+      r.ra = make_rsrc(g.act + int64_t(t_tile) * tb, uint32_t(tb * 2));
+    } else {
+      r.rw = make_rsrc(g.W + int64_t(n0) * g.K, uint32_t(min(kTBN, g.N - n0)) * Kb);
+      r.ra = make_rsrc(g.act + int64_t(t0) * g.K, uint32_t(min(kTBT, g.rows - t0)) * Kb);
+    }
     return r;
   };
   auto issue = [&](const Src &sr, int s) {
     const uint32_t base = lds0 + (s % kTST) * kTSST;
-    const int soff = (ks + s * 32) * 2;
+    const int soff = BLOCKED ? (ks / 32 + s) * 16384 : (ks + s * 32) * 2;
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16(sr.rw, base + (w * 32 + i * 16) * 64, off[i], soff);
 #pragma unroll
@@ -424,13 +435,16 @@ int lm_tile_width(int rows) { return rows <= 64 ? 4 * 2 * 32 : kTBN; }
 // Split-K factor of a projection with `rows` rows: enough workgroups to
 // cover the chip, K pieces of at least 256.
 int gemm_splits(int rows, int N, int K, int n_cu, int *k_split) {
-  int tiles;
-  if (rows <= 64)
-    tiles = (N + 127) / 128;
-  else
-    tiles = ((N + kTBN - 1) / kTBN) * ((rows + kTBT - 1) / kTBT);
-  int s = (2 * n_cu + tiles - 1) / tiles;
-  if (rows > 64) s = (n_cu + tiles - 1) / tiles;
+  int s;
+  if (rows <= 64) {
+    const int tiles = (N + 127) / 128;
+    s = (2 * n_cu + tiles - 1) / tiles;
+  } else {
+    // the tiled launch pads its grid to a multiple of 8 workgroups (one per
+    // CU); every split must fit in one dispatch round
+    const int grid_x = ((N + kTBN - 1) / kTBN + 7) / 8 * 8 * ((rows + kTBT - 1) / kTBT);
+    s = n_cu / grid_x;
+  }
   s = max(1, min(s, K / 256));
   const int ks = ((K + s - 1) / s + 63) / 64 * 64;
   *k_split = ks;
@@ -463,9 +477,9 @@ void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s) 
   static bool attr_set = false;
   static int n_cu = 256;
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_tiled_kernel<true>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_tiled_kernel<true, true>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, int(kTiledLds));
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_tiled_kernel<false>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_tiled_kernel<false, false>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, int(kTiledLds));
     int dev = 0;
     if (hipGetDevice(&dev) == hipSuccess) {
@@ -480,10 +494,11 @@ void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s) 
   const int tiles = ((n_ntiles + 7) / 8) * 8 * n_ttiles;
   const int grid_x = std::min(tiles, std::max(16, n_cu / 16 * 16));
   const dim3 grid(grid_x, splits);
+  // the LM head (stats) reads both operands in the blocked layout
   if (stats)
-    hipLaunchKernelGGL(gemm_tiled_kernel<true>, grid, dim3(512), kTiledLds, s, g);
+    hipLaunchKernelGGL((gemm_tiled_kernel<true, true>), grid, dim3(512), kTiledLds, s, g);
   else
-    hipLaunchKernelGGL(gemm_tiled_kernel<false>, grid, dim3(512), kTiledLds, s, g);
+    hipLaunchKernelGGL((gemm_tiled_kernel<false, false>), grid, dim3(512), kTiledLds, s, g);
 }
 
 // ----------------------------------------------------------------------------
@@ -583,6 +598,10 @@ __global__ __launch_bounds__(1024) void norm_kernel(const float *part, int split
       static_cast<uint16_t *>(out)[lo_off + idx] = lo;
     } else if (mode == ACT_F16) {
       static_cast<uint16_t *>(out)[idx] = f2h(y);
+    } else if (mode == ACT_F16_BLOCKED) {
+      const int R = row & 255, q = (c >> 3) & 3;
+      const int64_t b = (int64_t(row >> 8) * (hidden >> 5) + (c >> 5)) * 8192;
+      static_cast<uint16_t *>(out)[b + R * 32 + ((q ^ ((R >> 1) & 3)) << 3) + (c & 7)] = f2h(y);
     } else {
       static_cast<float *>(out)[idx] = y;
     }
@@ -616,6 +635,29 @@ __global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint16_t *__rest
     reinterpret_cast<uint4 *>(dst)[i] = bf8_to_h8(v);
   }
   if (local_bad) atomicAdd(bad, local_bad);
+}
+
+// one 16-byte output chunk per thread step: block i >> 10, position i & 1023
+__global__ __launch_bounds__(256) void bf16_to_f16_blocked_kernel(const uint16_t *__restrict__ src,
+                                                                 uint16_t *__restrict__ dst, int rows, int K,
+                                                                 int64_t n16) {
+  const int kbs = K >> 5;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += int64_t(gridDim.x) * 256) {
+    const int64_t blk = i >> 10;
+    const int R = int(i >> 2) & 255, p = int(i & 3);
+    const int64_t row = (blk / kbs) * 256 + R;
+    const int kb = int(blk % kbs), q = p ^ ((R >> 1) & 3);
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (row < rows) v = bf8_to_h8(*reinterpret_cast<const uint4 *>(src + row * K + kb * 32 + q * 8));
+    reinterpret_cast<uint4 *>(dst)[i] = v;
+  }
+}
+
+void launch_bf16_to_f16_blocked(const uint16_t *src, uint16_t *dst, int rows, int K, hipStream_t s) {
+  const int64_t n16 = blocked_elems(rows, K) / 8;
+  const int64_t blocks = std::min<int64_t>((n16 + 255) / 256, 8192);
+  hipLaunchKernelGGL(bf16_to_f16_blocked_kernel, dim3(unsigned(std::max<int64_t>(blocks, 1))), dim3(256), 0, s, src,
+                     dst, rows, K, n16);
 }
 
 void launch_bf16_to_f16(const uint16_t *src, uint16_t *dst, int64_t n, int32_t *bad, hipStream_t s) {

@@ -9,8 +9,17 @@
 namespace sv {
 
 // Formats of the projections' small (activation) operand: ACT_SPLIT = fp16
-// hi plane + fp16 lo plane (hi + lo = value to ~22 bits), ACT_F16, ACT_F32.
-enum ActMode : int { ACT_SPLIT = 0, ACT_F16 = 1, ACT_F32 = 2 };
+// hi plane + fp16 lo plane (hi + lo = value to ~22 bits), ACT_F16, ACT_F32,
+// ACT_F16_BLOCKED = fp16 in the blocked layout below.
+enum ActMode : int { ACT_SPLIT = 0, ACT_F16 = 1, ACT_F32 = 2, ACT_F16_BLOCKED = 3 };
+
+// Blocked fp16 layout of a [M, K] operand of the tiled LM-head launch: rows
+// padded to a multiple of 256; blocks [M / 256][K / 32], each 256 rows x 64
+// bytes (one K step) = 16 KB.  Inside a block, row R's 16-byte chunk q
+// (elements 8q .. 8q+7 of the K step) sits at byte R * 64 + ((q ^ ((R >> 1)
+// & 3)) << 4): the image of one ring stage in LDS, so that every DMA
+// instruction reads 1 KB of consecutive bytes.
+constexpr int64_t blocked_elems(int64_t rows, int64_t K) { return (rows + 255) / 256 * 256 * K; }
 
 struct AttnArgs {
   const uint16_t *kv_k, *kv_v;     // [T, Hkv, D] bf16, keys already rotated
@@ -46,7 +55,9 @@ struct AttnF32Args {
 };
 
 // out[rows, N] = act[rows, K] . W[N, K]^T, W in fp16, fp32 accumulation.
-// rows <= 64: act is an fp16 hi + lo pair (ACT_SPLIT); rows > 64: fp16.
+// rows <= 64: act is an fp16 hi + lo pair (ACT_SPLIT), W row-major; rows > 64:
+// fp16, both row-major, or (stats launch: the LM head) both in the blocked
+// layout.
 // Split-K (grid.y) writes out + split * split_stride.  With stats, each
 // workgroup also writes (max, sum exp(x - max), argmax) of its N tile per row.
 struct GemmArgs {
@@ -83,13 +94,16 @@ void launch_gemm_f32(const float *act, int rows, const float *W, int N, int K, f
 void launch_stats_from_logits(const float *logits, int rows, int V, int tile, float *t_max, float *t_sum,
                               int32_t *t_arg, int n_tiles, hipStream_t s);
 // Writes the normalised rows in `mode` (ACT_SPLIT: fp16 hi plane at out, lo
-// plane at out + lo_off; ACT_F16; ACT_F32).
+// plane at out + lo_off; ACT_F16; ACT_F32; ACT_F16_BLOCKED).
 void launch_norm(const float *part, int splits, int64_t split_stride, int rows, int hidden, float eps, int mode,
                  void *out, int64_t lo_off, hipStream_t s);
 
 // bf16 -> fp16 copy of n values (n % 8 == 0); adds the count of values
 // outside the fp16 range to *bad (device int).
 void launch_bf16_to_f16(const uint16_t *src, uint16_t *dst, int64_t n, int32_t *bad, hipStream_t s);
+// bf16 [rows, K] row-major -> fp16 blocked layout (blocked_elems(rows, K)
+// values, padding rows zero); K % 32 == 0.
+void launch_bf16_to_f16_blocked(const uint16_t *src, uint16_t *dst, int rows, int K, hipStream_t s);
 
 // ---- vocabulary reductions and acceptance ----
 struct VocabArgs {
