@@ -36,8 +36,9 @@ struct Stage {
 struct sv_handle {
   sv_config cfg{};
   sv::Dims dm{};
-  const void *w_o = nullptr, *w_lm = nullptr;   // weights the kernels read (fp16 copies for bf16)
-  const void *w_lm_blk = nullptr;               // bf16 and max_rows > 64: fp16 W_lm in the blocked layout
+  // weights the kernels read: for bf16, fp16 copies (W_o row-major, W_lm in
+  // the blocked layout of the LM-head launches)
+  const void *w_o = nullptr, *w_lm = nullptr;
   int32_t *d_bad = nullptr;
   int device = 0, n_cu = 256, target_items = 1024;
   int elt = 2;
@@ -186,13 +187,10 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
   A(&h->rpart, size_t(dm.max_roots) * h->n_och * 4);
   if (dm.dtype == SV_BF16) {
     // the projections run on fp16 MFMA: keep fp16 copies of the weights
-    // (row-major; plus W_lm in the blocked layout when runs can take the
-    // tiled LM-head launch)
-    uint16_t *wo16 = nullptr, *wlm16 = nullptr, *wlm_blk = nullptr;
-    const bool tiled = dm.max_rows > 64;
+    // (W_o row-major, W_lm in the blocked layout)
+    uint16_t *wo16 = nullptr, *wlm16 = nullptr;
     A(&wo16, size_t(H * Hq * D * 2));
-    A(&wlm16, size_t(V * H * 2));
-    if (tiled) A(&wlm_blk, size_t(sv::blocked_elems(V, H) * 2));
+    A(&wlm16, size_t(sv::blocked_elems(V, H) * 2));
     A(&h->d_bad, 4);
     if (st == SV_OK) {
       e = hipMemsetAsync(h->d_bad, 0, 4, nullptr);
@@ -201,8 +199,7 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
       if (e == hipSuccess) e = hipMemsetAsync(h->hn, 0, std::max<size_t>(size_t(R * H * 4), size_t(sv::blocked_elems(R, H) * 2)), nullptr);
       if (e == hipSuccess) {
         sv::launch_bf16_to_f16(static_cast<const uint16_t *>(w_o), wo16, H * Hq * D, h->d_bad, nullptr);
-        sv::launch_bf16_to_f16(static_cast<const uint16_t *>(w_lm), wlm16, V * H, h->d_bad, nullptr);
-        if (tiled) sv::launch_bf16_to_f16_blocked(static_cast<const uint16_t *>(w_lm), wlm_blk, int(V), int(H), nullptr);
+        sv::launch_bf16_to_f16_blocked(static_cast<const uint16_t *>(w_lm), wlm16, int(V), int(H), h->d_bad, nullptr);
         e = hipGetLastError();
       }
       int32_t bad = 0;
@@ -217,7 +214,6 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
       }
       h->w_o = wo16;
       h->w_lm = wlm16;
-      h->w_lm_blk = wlm_blk;
     }
   }
   if (st != SV_OK) {
@@ -528,7 +524,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     l.act = static_cast<const uint16_t *>(h->hn);
     l.act_lo = l.act + h_lo;
     l.rows = n;
-    l.W = static_cast<const uint16_t *>(n <= 64 ? h->w_lm : h->w_lm_blk);
+    l.W = static_cast<const uint16_t *>(h->w_lm);
     l.N = int(V);
     l.K = int(H);
     l.k_split = int(H);

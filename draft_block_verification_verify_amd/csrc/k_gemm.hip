@@ -105,6 +105,9 @@ __device__ __forceinline__ uint4 lds16(const uint8_t *p) { return *reinterpret_c
 // 3-stage LDS ring by DMA: weights [NR rows][128 B] and the activation hi and
 // lo planes [TB*32 rows][128 B], row-XOR-swizzled (16-B chunk c of row R at
 // slot c ^ (R & 7)).  Two fp16 MFMAs per product (activation hi + lo).
+// BLOCKED (the LM head, NR = 256): the weights come from the blocked layout
+// of the tiled launch; one K step is two consecutive 16 KB blocks, copied to
+// LDS as they are.
 // ----------------------------------------------------------------------------
 
 constexpr int kSkST = 3;
@@ -114,7 +117,7 @@ constexpr int skinny_stage_bytes() {
   return 4 * WV * 32 * 128 + 2 * TB * 32 * 128;
 }
 
-template <int TB, int WV, bool STATS>
+template <int TB, int WV, bool STATS, bool BLOCKED>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
   constexpr int NR = 4 * WV * 32;            // weight rows per workgroup
   constexpr int WST = NR * 128;              // weight bytes per stage
@@ -130,7 +133,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
   const int ks = blockIdx.y * g.k_split;
   const int nk = (min(g.K, ks + g.k_split) - ks) / 64;
   const int Kb = g.K * 2;
-  const i32x4 rw = make_rsrc(g.W + int64_t(n0) * g.K, uint32_t(min(NR, g.N - n0)) * Kb);
+  static_assert(!BLOCKED || NR == 256, "blocked weights come in 256-row tiles");
+  const i32x4 rw = BLOCKED ? make_rsrc(g.W + int64_t(blockIdx.x) * 256 * g.K, uint32_t(256 * Kb))
+                           : make_rsrc(g.W + int64_t(n0) * g.K, uint32_t(min(NR, g.N - n0)) * Kb);
   const i32x4 rah = make_rsrc(g.act, uint32_t(g.rows) * Kb);
   const i32x4 ral = make_rsrc(g.act_lo, uint32_t(g.rows) * Kb);
   const uint32_t lds0 = lds_addr(smem);
@@ -139,7 +144,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < WI; ++i) {
     const int R = (w * WI + i) * 8 + (lane >> 3);
-    woff[i] = R * Kb + ((c8 ^ (R & 7)) << 4);
+    woff[i] = BLOCKED ? (w * WI + i) * 1024 + lane * 16 : R * Kb + ((c8 ^ (R & 7)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
@@ -151,7 +156,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     const uint32_t base = lds0 + (s % kSkST) * SST;
     const int soff = (ks + s * 64) * 2;
 #pragma unroll
-    for (int i = 0; i < WI; ++i) dma16(rw, base + (w * WI + i) * 1024, woff[i], soff);
+    for (int i = 0; i < WI; ++i) dma16(rw, base + (w * WI + i) * 1024, woff[i], BLOCKED ? (ks / 32 + 2 * s) * 16384 : soff);
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       const int ia = w * AI + i;
@@ -177,7 +182,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < WV; ++v) {
         const int R = w * WV * 32 + v * 32 + r32;
-        af[v] = lds16(base + R * 128 + ((q ^ (R & 7)) << 4));
+        // blocked: chunk q of the 128-B step is chunk q & 3 of block q >> 2
+        af[v] = BLOCKED ? lds16(base + (q >> 2) * 16384 + R * 64 + (((q & 3) ^ ((R >> 1) & 3)) << 4))
+                        : lds16(base + R * 128 + ((q ^ (R & 7)) << 4));
       }
 #pragma unroll
       for (int t = 0; t < TB; ++t) {
@@ -454,14 +461,15 @@ int gemm_splits(int rows, int N, int K, int n_cu, int *k_split) {
 template <int TB, int WV, bool ST>
 static void launch_skinny(const GemmArgs &g, int splits, hipStream_t s) {
   constexpr size_t lds = size_t(kSkST) * skinny_stage_bytes<TB, WV>();
+  constexpr bool BL = ST;   // the LM head reads the blocked weight copy
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_skinny_kernel<TB, WV, ST>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_skinny_kernel<TB, WV, ST, BL>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     attr = true;
   }
   const dim3 grid((g.N + 4 * WV * 32 - 1) / (4 * WV * 32), splits);
-  hipLaunchKernelGGL((gemm_skinny_kernel<TB, WV, ST>), grid, dim3(256), lds, s, g);
+  hipLaunchKernelGGL((gemm_skinny_kernel<TB, WV, ST, BL>), grid, dim3(256), lds, s, g);
 }
 
 void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s) {
@@ -640,24 +648,33 @@ __global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint16_t *__rest
 // one 16-byte output chunk per thread step: block i >> 10, position i & 1023
 __global__ __launch_bounds__(256) void bf16_to_f16_blocked_kernel(const uint16_t *__restrict__ src,
                                                                  uint16_t *__restrict__ dst, int rows, int K,
-                                                                 int64_t n16) {
+                                                                 int64_t n16, int32_t *__restrict__ bad) {
   const int kbs = K >> 5;
+  int local_bad = 0;
   for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += int64_t(gridDim.x) * 256) {
     const int64_t blk = i >> 10;
     const int R = int(i >> 2) & 255, p = int(i & 3);
     const int64_t row = (blk / kbs) * 256 + R;
     const int kb = int(blk % kbs), q = p ^ ((R >> 1) & 3);
     uint4 v = {0u, 0u, 0u, 0u};
-    if (row < rows) v = bf8_to_h8(*reinterpret_cast<const uint4 *>(src + row * K + kb * 32 + q * 8));
+    if (row < rows) {
+      const uint4 b = *reinterpret_cast<const uint4 *>(src + row * K + kb * 32 + q * 8);
+      const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        local_bad += (fabsf(__uint_as_float(w[k] << 16)) > 65504.f) + (fabsf(__uint_as_float(w[k] & 0xFFFF0000u)) > 65504.f);
+      v = bf8_to_h8(b);
+    }
     reinterpret_cast<uint4 *>(dst)[i] = v;
   }
+  if (local_bad) atomicAdd(bad, local_bad);
 }
 
-void launch_bf16_to_f16_blocked(const uint16_t *src, uint16_t *dst, int rows, int K, hipStream_t s) {
+void launch_bf16_to_f16_blocked(const uint16_t *src, uint16_t *dst, int rows, int K, int32_t *bad, hipStream_t s) {
   const int64_t n16 = blocked_elems(rows, K) / 8;
   const int64_t blocks = std::min<int64_t>((n16 + 255) / 256, 8192);
   hipLaunchKernelGGL(bf16_to_f16_blocked_kernel, dim3(unsigned(std::max<int64_t>(blocks, 1))), dim3(256), 0, s, src,
-                     dst, rows, K, n16);
+                     dst, rows, K, n16, bad);
 }
 
 void launch_bf16_to_f16(const uint16_t *src, uint16_t *dst, int64_t n, int32_t *bad, hipStream_t s) {

@@ -55,9 +55,9 @@ struct AttnF32Args {
 };
 
 // out[rows, N] = act[rows, K] . W[N, K]^T, W in fp16, fp32 accumulation.
-// rows <= 64: act is an fp16 hi + lo pair (ACT_SPLIT), W row-major; rows > 64:
-// fp16, both row-major, or (stats launch: the LM head) both in the blocked
-// layout.
+// rows <= 64: act is an fp16 hi + lo pair (ACT_SPLIT); rows > 64: fp16.  The
+// stats launch (the LM head) reads W in the blocked layout, and for rows > 64
+// act too; otherwise both are row-major.
 // Split-K (grid.y) writes out + split * split_stride.  With stats, each
 // workgroup also writes (max, sum exp(x - max), argmax) of its N tile per row.
 struct GemmArgs {
@@ -102,8 +102,9 @@ void launch_norm(const float *part, int splits, int64_t split_stride, int rows, 
 // outside the fp16 range to *bad (device int).
 void launch_bf16_to_f16(const uint16_t *src, uint16_t *dst, int64_t n, int32_t *bad, hipStream_t s);
 // bf16 [rows, K] row-major -> fp16 blocked layout (blocked_elems(rows, K)
-// values, padding rows zero); K % 32 == 0.
-void launch_bf16_to_f16_blocked(const uint16_t *src, uint16_t *dst, int rows, int K, hipStream_t s);
+// values, padding rows zero); K % 32 == 0.  Adds the count of values outside
+// the fp16 range to *bad.
+void launch_bf16_to_f16_blocked(const uint16_t *src, uint16_t *dst, int rows, int K, int32_t *bad, hipStream_t s);
 
 // ---- vocabulary reductions and acceptance ----
 struct VocabArgs {
