@@ -86,8 +86,9 @@ _TAG = {"kv_k": 1, "kv_v": 2, "q": 3, "k": 4, "v": 5, "w_o": 6, "w_lm": 7,
         "drafter": 8, "struct": 9, "plant": 10, "sample": 11, "uniform": 12}
 
 
-def _rng(cfg_id: int, seed: int, tag: str, sub: int = 0) -> np.random.Generator:
-    return np.random.default_rng([cfg_id, seed, _TAG[tag], sub])
+def _rng(cfg_id: int, seed: int, tag: str, sub: int = 0, rnd: int = 0) -> np.random.Generator:
+    key = [cfg_id, seed, _TAG[tag], sub] + ([rnd] if rnd else [])
+    return np.random.default_rng(key)
 
 
 # ----------------------------------------------------------------------------
@@ -110,11 +111,12 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 _POOL_WORKERS = max(1, min(16, os.cpu_count() or 1))
 
 
-def _normal(cfg: Config, seed: int, tag: str, shape, std: float) -> np.ndarray:
+def _normal(cfg: Config, seed: int, tag: str, shape, std: float, rnd: int = 0) -> np.ndarray:
     """N(0, std^2) of `shape` in the config dtype (uint16 bits for bf16).
 
     Large tensors are drawn in fixed 4M-element chunks, each from its own
-    stream, so the values do not depend on the thread count.
+    stream, so the values do not depend on the thread count.  `rnd` > 0
+    selects the streams of step `rnd` of a multi-step run.
     """
     total = int(np.prod(shape))
     chunk = 1 << 22
@@ -124,7 +126,7 @@ def _normal(cfg: Config, seed: int, tag: str, shape, std: float) -> np.ndarray:
     def fill(c: int) -> None:
         lo = c * chunk
         hi = min(total, lo + chunk)
-        r = _rng(cfg.cfg_id, seed, tag, c)
+        r = _rng(cfg.cfg_id, seed, tag, c, rnd)
         v = r.standard_normal(hi - lo, dtype=np.float32) * np.float32(std)
         out[lo:hi] = f32_to_bf16_bits(v) if cfg.dtype == "bf16" else v
 
@@ -159,11 +161,12 @@ class Structure:
         return int(self.root_kv_off.shape[0])
 
 
-def chain_structure(prefix_lens, gamma: int) -> Structure:
+def chain_structure(prefix_lens, gamma: int, slack: int = 0) -> Structure:
     """Independent chains: sequence s = root (last committed token) + gamma drafts.
 
-    Each sequence owns a packed KV segment; its rows sit at positions
-    L_s, L_s+1, ..., L_s+gamma.
+    Each sequence owns a KV segment of L_s + slack entries (the slack takes
+    committed rows of later steps); its rows sit at positions L_s, L_s+1,
+    ..., L_s+gamma.
     """
     parent, pos, offs, lens = [], [], [], []
     off = 0
@@ -174,7 +177,7 @@ def chain_structure(prefix_lens, gamma: int) -> Structure:
             pos.append(int(L) + i)
         offs.append(off)
         lens.append(int(L))
-        off += int(L)
+        off += int(L) + int(slack)
     return Structure(np.array(parent, np.int32), np.array(pos, np.int32),
                      np.array(offs, np.int64), np.array(lens, np.int32), off)
 
@@ -195,13 +198,15 @@ def tree_structure(stem: int, anchors, branch_w: int) -> Structure:
                      anchors=np.asarray(anchors, np.int64))
 
 
-def make_structure(cfg: Config, seed: int) -> Structure:
+def make_structure(cfg: Config, seed: int, slack: int = 0) -> Structure:
     r = _rng(cfg.cfg_id, seed, "struct")
     if cfg.kind == "chain":
-        return chain_structure([cfg.prefix], cfg.gamma)
+        return chain_structure([cfg.prefix], cfg.gamma, slack)
     if cfg.kind == "multichain":
         lens = r.integers(cfg.min_len, cfg.max_len + 1, size=cfg.n_seqs)
-        return chain_structure(lens, cfg.gamma)
+        return chain_structure(lens, cfg.gamma, slack)
+    if slack:
+        raise ValueError("slack applies to chain workloads")
     if cfg.kind == "tree":
         a = np.sort(r.choice(np.arange(1, cfg.stem + 1), size=cfg.anchors,
                              replace=False))
@@ -236,9 +241,9 @@ class Inputs:
     extras: dict = field(default_factory=dict)
 
 
-def make_inputs(cfg_id: int | Config, seed: int = 0, *, with_weights: bool = True) -> Inputs:
+def make_inputs(cfg_id: int | Config, seed: int = 0, *, with_weights: bool = True, slack: int = 0) -> Inputs:
     cfg = cfg_id if isinstance(cfg_id, Config) else CONFIGS[cfg_id]
-    st = make_structure(cfg, seed)
+    st = make_structure(cfg, seed, slack)
     n, Hq, Hkv, d = st.n_rows, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     n_draft = int((st.parent >= 0).sum())
     T = max(st.kv_tokens, 0)
@@ -255,6 +260,17 @@ def make_inputs(cfg_id: int | Config, seed: int = 0, *, with_weights: bool = Tru
     dl = _normal(cfg, seed, "drafter", (n_draft, cfg.vocab), 2.0)
     draft_ids = np.zeros(n, np.int32)
     return Inputs(cfg, seed, st, kv_k, kv_v, q, k, v, w_o, w_lm, dl, draft_ids)
+
+
+def round_rows(cfg: Config, seed: int, rnd: int, n_rows: int, n_draft: int) -> dict:
+    """Row tensors of step `rnd` >= 1 of a multi-step run (step 0 uses those
+    of make_inputs): fresh q, k, v rows and drafter logits, same
+    distributions, streams of their own."""
+    Hq, Hkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    return {"q_rows": _normal(cfg, seed, "q", (n_rows, Hq, d), 1.0, rnd),
+            "k_rows": _normal(cfg, seed, "k", (n_rows, Hkv, d), 1.0, rnd),
+            "v_rows": _normal(cfg, seed, "v", (n_rows, Hkv, d), 1.0, rnd),
+            "drafter_logits": _normal(cfg, seed, "drafter", (n_draft, cfg.vocab), 2.0, rnd)}
 
 
 def make_weights(cfg_id: int | Config, seed: int = 0):

@@ -52,6 +52,15 @@ from their fp32 / bf16 bits):
    u_bonus (the smallest token whose running weight exceeds u_bonus times
    the total; a residual without mass falls back to p_cur).  The uniforms
    are inputs.  Trees with branching nodes are not taken in this mode.
+10. Commit (the step after verify: sionic.ai page, section 1, generation
+   resumes after the matching leading drafts; section 6, committing accepted
+   tokens follows verify).  Each tree's accepted path, its root and then
+   every accepted draft in depth order (accept_len rows, ending at last_row),
+   joins the tree's cache right after its visible prefix: entry off + len + j
+   holds the j-th path row's key rotated at its semantic position and its
+   value, in the cache's number format (bf16 or fp32).  The bonus token is
+   not committed; it is the root of the next step, at the position after the
+   last committed row, seeing len + accept_len cache entries.
 """
 from __future__ import annotations
 
@@ -420,3 +429,60 @@ def inp_dict(inp) -> dict:
             "q_rows": inp.q_rows, "k_rows": inp.k_rows, "v_rows": inp.v_rows,
             "w_o": inp.w_o, "w_lm": inp.w_lm, "drafter_logits": inp.drafter_logits,
             "draft_ids": inp.draft_ids}
+
+
+# ----------------------------------------------------------------------------
+# 10. commit and the next step's layout
+# ----------------------------------------------------------------------------
+
+
+def to_cache_format(x, dtype: str) -> np.ndarray:
+    """fp64 values as stored in the cache: fp32 by round-to-nearest-even; for
+    bf16, that fp32 rounded to nearest-even on its upper 16 bits, returned as
+    the bf16 bit patterns (uint16)."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if dtype != "bf16":
+        return f
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+
+
+def commit(cfg, inp, res, kv_k, kv_v):
+    """Step 10 for every tree: returns copies of (kv_k, kv_v) with the
+    accepted paths written after the visible prefixes.  `res` gives
+    accept_len and last_row per tree; `inp` the step's structure and rows."""
+    dt = cfg["dtype"]
+    forest = Forest(inp["parent"])
+    kk = np.array(kv_k, copy=True)
+    vv = np.array(kv_v, copy=True)
+    for t in range(len(forest.roots)):
+        acc, last = int(res["accept_len"][t]), int(res["last_row"][t])
+        path = forest.path(last)
+        if len(path) != acc:
+            raise ValueError(f"tree {t}: last_row {last} is at depth {len(path) - 1}, accept_len {acc}")
+        end = int(inp["root_kv_off"][t]) + int(inp["root_kv_len"][t])
+        for j, row in enumerate(path):
+            k = rope(decode(inp["k_rows"][row], dt), int(inp["pos"][row]), cfg["rope_base"])
+            kk[end + j] = to_cache_format(k, dt)
+            vv[end + j] = inp["v_rows"][row]
+    return kk, vv
+
+
+def advance(inp, res, gamma: int):
+    """Layout of the next chain step after a commit: tree t keeps its cache
+    offset, sees len + accept_len entries, and its new root (the bonus token)
+    sits at the position after the last committed row, followed by gamma
+    draft rows.  Returns (parent, pos, root_kv_off, root_kv_len)."""
+    forest = Forest(inp["parent"])
+    parent, pos, lens = [], [], []
+    for t, root in enumerate(forest.roots):
+        acc = int(res["accept_len"][t])
+        p0 = int(inp["pos"][root]) + acc
+        start = len(parent)
+        for i in range(gamma + 1):
+            parent.append(-1 if i == 0 else start + i - 1)
+            pos.append(p0 + i)
+        lens.append(int(inp["root_kv_len"][t]) + acc)
+    return (np.array(parent, np.int32), np.array(pos, np.int32),
+            np.array(inp["root_kv_off"], np.int64), np.array(lens, np.int32))
