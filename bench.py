@@ -99,6 +99,116 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 3) -> None:
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
 
 
+def bench_rounds(args, cfg) -> int:
+    """R chain decode steps: verify, commit the accepted paths into the KV
+    cache, read the accept lengths back, lay out the next step (its roots
+    after the committed rows; fresh seeded rows).  Drafts are planted on the
+    target's greedy tokens by an untimed dry run of the same R steps; the
+    timed replay must reproduce its accept lengths."""
+    import torch
+    from draft_block_verification_verify_amd import binding as B
+    from draft_block_verification_verify_amd import workloads as W
+    from draft_block_verification_verify_amd.runner import DeviceCase, to_device
+
+    if cfg.kind == "tree":
+        print("--rounds takes chain workloads (a shared stem cannot take commits)", file=sys.stderr)
+        return 2
+    R, gamma = args.rounds, cfg.gamma
+    log(f"[rounds] generating {cfg.name} seed {args.seed}, {R} steps")
+    inp = W.make_inputs(cfg, args.seed, slack=R * (gamma + 1))
+    st = inp.st
+    n, nd = st.n_rows, int((st.parent >= 0).sum())
+    dc = DeviceCase(inp, max_pos=int(st.pos.max()) + 1 + R * (gamma + 1))
+    dt = cfg.dtype
+    rows = [{"q": dc.q, "k": dc.k, "v": dc.v, "dl": dc.dl}]
+    for r in range(1, R):
+        h = W.round_rows(cfg, args.seed, r, n, nd)
+        rows.append({"q": to_device(h["q_rows"], dt, dc.device), "k": to_device(h["k_rows"], dt, dc.device),
+                     "v": to_device(h["v_rows"], dt, dc.device), "dl": to_device(h["drafter_logits"], dt, dc.device)})
+    kv0 = (dc.kv_k.clone(), dc.kv_v.clone())
+    pos0, len0 = st.pos.copy(), st.root_kv_len.copy()
+
+    # dry run: plant each step's drafts from the target's greedy tokens
+    drafts, accs = [], []
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    commit_ms = []
+    for r in range(R):
+        if r:
+            dc.next_step(accs[-1], rows[r])
+        dc.run()
+        W.plant_chain_drafts(inp, dc.results()["argmax"], rnd=r)
+        dc.refresh()
+        drafts.append(dc.draft_ids.clone())
+        dc.run()
+        ev[0].record()
+        dc.commit()
+        ev[1].record()
+        accs.append(dc.results()["accept_len"].astype(np.int64))
+        commit_ms.append(ev[0].elapsed_time(ev[1]))
+
+    def reset():
+        dc.kv_k.copy_(kv0[0])
+        dc.kv_v.copy_(kv0[1])
+        st.pos, st.root_kv_len = pos0.copy(), len0.copy()
+        dc.q, dc.k, dc.v, dc.dl = rows[0]["q"], rows[0]["k"], rows[0]["v"], rows[0]["dl"]
+        dc.draft_ids = drafts[0]
+        dc.refresh(upload_drafts=False)
+        torch.cuda.synchronize()
+
+    def replay():
+        got = []
+        acc = None
+        for r in range(R):
+            if r:
+                dc.next_step(acc, rows[r], drafts[r])
+            dc.run()
+            dc.commit()
+            acc = dc.outs["accept_len"].cpu().numpy().astype(np.int64)   # the host waits here
+            got.append(acc)
+        return got
+
+    reset()
+    replay()                                   # warmup
+    reset()
+    log(f"[rounds] timing {R} steps")
+    t0 = time.perf_counter()
+    got = replay()
+    torch.cuda.synchronize()
+    t_loop = time.perf_counter() - t0
+    replay_ok = all((a == b).all() for a, b in zip(got, accs))
+    # the same steps' verify alone, back to back without commits or host waits
+    reset()
+    t0 = time.perf_counter()
+    for _ in range(R):
+        dc.run()
+    torch.cuda.synchronize()
+    t_verify = (time.perf_counter() - t0) / R
+    dc.close()
+    tokens = int(sum(a.sum() for a in got))
+    res = {
+        "metric": "decode tokens/s over R verify + commit steps (accepted drafts + bonus per sequence)",
+        "value": tokens / t_loop,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": R,
+        "warmup": 1,
+        "ms_per_step": t_loop * 1e3 / R,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dt == "bf16" else "f32",
+        "data": "synthetic (seeded; random-init weights; drafts planted on the target's greedy tokens)",
+        "config": {"workload": cfg.name, "sequences": st.n_roots, "gamma": gamma, "rounds": R, "seed": args.seed},
+        "rounds": {"tokens": tokens, "accept_len_mean": float(np.mean([a.mean() for a in got])),
+                   "verify_only_ms_per_step": t_verify * 1e3,
+                   "fixed_cost_ms_per_step": t_loop * 1e3 / R - t_verify * 1e3,
+                   "commit_kernel_ms_median": float(np.median(commit_ms)),
+                   "replay_matches_dry_run": bool(replay_ok)},
+    }
+    print(json.dumps(res))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +221,9 @@ def main() -> int:
     ap.add_argument("--sample", action="store_true",
                     help="T = 1 stochastic verification (drafts drawn from the drafter, seeded uniforms)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--rounds", type=int, default=0,
+                    help="chain workloads: time R decode steps of verify + commit (host reads the accept "
+                         "lengths each step) instead of the single verify step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the verify step is not "
@@ -128,6 +241,8 @@ def main() -> int:
 
     B.lib()                                   # fails loudly without the HIP library
     cfg = W.CONFIGS[args.workload]
+    if args.rounds:
+        return bench_rounds(args, cfg)
     log(f"[bench] generating {cfg.name} seed {args.seed}")
     t0 = time.perf_counter()
     inp = W.make_inputs(cfg, args.seed)

@@ -62,6 +62,8 @@ _lib = None
 SYMBOLS = {
     "spec_verify_create": (C.c_int, [C.POINTER(SvConfig), C.c_void_p, C.c_void_p, C.POINTER(C.c_void_p)]),
     "spec_verify_run": (C.c_int, [C.c_void_p, C.POINTER(SvInputs), C.POINTER(SvOutputs), C.c_void_p]),
+    "spec_verify_commit": (C.c_int, [C.c_void_p, C.POINTER(SvInputs), C.POINTER(SvOutputs), C.c_void_p, C.c_void_p,
+                                     C.c_void_p]),
     "spec_verify_destroy": (C.c_int, [C.c_void_p]),
     "spec_verify_last_error": (C.c_char_p, []),
     "spec_verify_profile": (C.c_int, [C.c_void_p, C.c_int32]),
@@ -104,6 +106,12 @@ def spec_verify_create(cfg: SvConfig, w_o_ptr: int, w_lm_ptr: int) -> C.c_void_p
 
 def spec_verify_run(h, inputs: SvInputs, outputs: SvOutputs, stream: int | None = None) -> None:
     _check(lib().spec_verify_run(h, C.byref(inputs), C.byref(outputs), C.c_void_p(stream or 0)))
+
+
+def spec_verify_commit(h, inputs: SvInputs, outputs: SvOutputs, kv_k: int, kv_v: int,
+                       stream: int | None = None) -> None:
+    _check(lib().spec_verify_commit(h, C.byref(inputs), C.byref(outputs), C.c_void_p(kv_k), C.c_void_p(kv_v),
+                                    C.c_void_p(stream or 0)))
 
 
 def spec_verify_destroy(h) -> None:
@@ -198,3 +206,6 @@ class Verifier:
 
     def run(self, inp: SvInputs, out: SvOutputs, stream: int | None = None):
         spec_verify_run(self.h, inp, out, stream)
+
+    def commit(self, inp: SvInputs, out: SvOutputs, kv_k, kv_v, stream: int | None = None):
+        spec_verify_commit(self.h, inp, out, _ptr(kv_k), _ptr(kv_v), stream)

@@ -2,6 +2,8 @@
 // metadata upload and the launch sequence of one run.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -61,6 +63,19 @@ struct sv_handle {
   float *rpart = nullptr;          // T = 1 mode: [max_roots, n_och]
   size_t h_part_floats = 0;
   std::vector<void *> allocs;
+  // the most recent run, for spec_verify_commit (its plan stays in d_meta
+  // until the next run's upload, which is ordered after the commit on the
+  // same stream)
+  struct LastRun {
+    bool valid = false;
+    void *stream = nullptr;
+    int32_t n = 0, R = 0;
+    int64_t kv_tokens = 0;
+    const void *v_rows = nullptr;
+    std::vector<int32_t> parent, pos, kv_len, depth;   // depth: deepest row of each tree
+    std::vector<int64_t> kv_off;
+    sv::MetaLayout lay{};
+  } last;
   // completion / profiling
   hipEvent_t done = nullptr;
   bool ran = false;
@@ -605,6 +620,96 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   e = hipEventRecord(h->done, stream);
   if (e != hipSuccess) return hip_fail("hipEventRecord", e);
   h->ran = true;
+  {
+    auto &L = h->last;
+    L.valid = true;
+    L.stream = stream_v;
+    L.n = n;
+    L.R = plan.R;
+    L.kv_tokens = in->kv_tokens;
+    L.v_rows = in->v_rows;
+    L.parent.assign(in->parent, in->parent + n);
+    L.pos.assign(in->pos, in->pos + n);
+    L.kv_off = plan.tree_kv_off;
+    L.kv_len = plan.tree_kv_len;
+    L.depth.assign(plan.R, 0);
+    std::vector<int32_t> dep(n, 0);
+    for (int i = 0; i < n; ++i) {
+      dep[i] = in->parent[i] < 0 ? 0 : dep[in->parent[i]] + 1;
+      L.depth[plan.row_tree[i]] = std::max(L.depth[plan.row_tree[i]], dep[i]);
+    }
+    L.lay = lay;
+  }
+  return SV_OK;
+}
+
+sv_status spec_verify_commit(sv_handle *h, const sv_inputs *in, const sv_outputs *out, void *kv_k, void *kv_v,
+                             void *stream_v) {
+  g_err.clear();
+  if (!h || !in || !out) return fail(SV_ERR_INVALID_ARG, "handle, inputs and outputs must be non-null");
+  const auto &L = h->last;
+  if (!L.valid) return fail(SV_ERR_INVALID_ARG, "spec_verify_commit follows a spec_verify_run on the same handle");
+  if (stream_v != L.stream)
+    return fail(SV_ERR_INVALID_ARG, "spec_verify_commit must be enqueued on the stream of the run it commits");
+  const int n = L.n, R = L.R;
+  bool same = in->n_rows == n && in->n_roots == R && in->parent && in->pos && in->root_kv_off && in->root_kv_len &&
+              in->kv_tokens == L.kv_tokens && in->v_rows == L.v_rows;
+  if (same) same = std::equal(L.parent.begin(), L.parent.end(), in->parent) &&
+                   std::equal(L.pos.begin(), L.pos.end(), in->pos) &&
+                   std::equal(L.kv_off.begin(), L.kv_off.end(), in->root_kv_off) &&
+                   std::equal(L.kv_len.begin(), L.kv_len.end(), in->root_kv_len);
+  if (!same) return fail(SV_ERR_INVALID_ARG, "inputs differ from those of the handle's most recent run");
+  if (!out->accept_len || !out->last_row)
+    return fail(SV_ERR_INVALID_ARG, "accept_len and last_row must be the device outputs of that run");
+  if (!kv_k || !kv_v) return fail(SV_ERR_INVALID_ARG, "kv_k and kv_v must be non-null");
+  if ((reinterpret_cast<uintptr_t>(kv_k) | reinterpret_cast<uintptr_t>(kv_v) |
+       reinterpret_cast<uintptr_t>(in->v_rows)) % 16 != 0)
+    return fail(SV_ERR_INVALID_ARG, "kv_k, kv_v and v_rows must be 16-byte aligned");
+  // write ranges: tree t may write [off + len, off + len + depth + 1); none
+  // may leave the cache or meet another tree's prefix or write range
+  struct Iv {
+    int64_t a, b;
+    int t;   // tree of a write range, -1 for a prefix
+  };
+  std::vector<Iv> iv;
+  iv.reserve(2 * size_t(R));
+  for (int t = 0; t < R; ++t) {
+    const int64_t w0 = L.kv_off[t] + L.kv_len[t], w1 = w0 + L.depth[t] + 1;
+    if (w1 > L.kv_tokens)
+      return fail(SV_ERR_BAD_TREE, "tree " + std::to_string(t) + ": its accepted path may need cache entries up to " +
+                                       std::to_string(w1) + " but kv_tokens is " + std::to_string(L.kv_tokens));
+    if (L.kv_len[t] > 0) iv.push_back({L.kv_off[t], w0, -1});
+    iv.push_back({w0, w1, t});
+  }
+  std::sort(iv.begin(), iv.end(), [](const Iv &x, const Iv &y) { return x.a < y.a || (x.a == y.a && x.b < y.b); });
+  int64_t max_end = INT64_MIN;
+  for (size_t i = 0; i < iv.size(); ++i) {
+    if (iv[i].t >= 0 && (iv[i].a < max_end || (i + 1 < iv.size() && iv[i + 1].a < iv[i].b)))
+      return fail(SV_ERR_BAD_TREE, "tree " + std::to_string(iv[i].t) +
+                                       ": the cache entries after its prefix overlap another tree's prefix or path");
+    max_end = std::max(max_end, iv[i].b);
+  }
+
+  const hipStream_t stream = static_cast<hipStream_t>(stream_v);
+  const char *m = h->d_meta;
+  sv::CommitArgs ca{};
+  ca.row_parent = reinterpret_cast<const int32_t *>(m + L.lay.row_parent);
+  ca.tree_start = reinterpret_cast<const int32_t *>(m + L.lay.tree_start);
+  ca.tree_rows = reinterpret_cast<const int32_t *>(m + L.lay.tree_rows);
+  ca.accept_len = out->accept_len;
+  ca.last_row = out->last_row;
+  ca.kv_off = reinterpret_cast<const int64_t *>(m + L.lay.tree_kv_off);
+  ca.kv_len = reinterpret_cast<const int32_t *>(m + L.lay.tree_kv_len);
+  ca.k_rot = static_cast<const uint8_t *>(h->k_rot);
+  ca.v_rows = static_cast<const uint8_t *>(in->v_rows);
+  ca.kv_k = static_cast<uint8_t *>(kv_k);
+  ca.kv_v = static_cast<uint8_t *>(kv_v);
+  ca.row_bytes = int(int64_t(h->dm.Hkv) * h->dm.d * h->elt);
+  sv::launch_commit(ca, R, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail("kernel launch", e);
+  e = hipEventRecord(h->done, stream);
+  if (e != hipSuccess) return hip_fail("hipEventRecord", e);
   return SV_OK;
 }
 

@@ -136,6 +136,22 @@ struct SampleArgs {
 };
 void launch_sample(const VocabArgs &a, const SampleArgs &sa, hipStream_t s);
 
+// ---- commit (the step after verify) ----
+// Tree t's accepted path (root first, accept_len[t] rows ending at
+// last_row[t]) is copied to cache entries kv_off[t] + kv_len[t] + j: K from
+// the run's rotated row keys, V from the row values; row_bytes per KV row.
+struct CommitArgs {
+  const int32_t *row_parent;    // [n] global parent row, -1 for roots
+  const int32_t *tree_start, *tree_rows;
+  const int32_t *accept_len, *last_row;   // [R] outputs of the run
+  const int64_t *kv_off;        // [R] the tree's first visible cache entry
+  const int32_t *kv_len;        // [R] visible prefix length
+  const uint8_t *k_rot, *v_rows;          // [n] rows of row_bytes
+  uint8_t *kv_k, *kv_v;         // cache, rows of row_bytes
+  int row_bytes;                // Hkv * d * element size, a multiple of 16
+};
+void launch_commit(const CommitArgs &a, int n_roots, hipStream_t s);
+
 void launch_drafter_partial(const VocabArgs &a, hipStream_t s);
 void launch_row_combine(const VocabArgs &a, hipStream_t s);
 void launch_overlap_partial(const VocabArgs &a, hipStream_t s);

@@ -33,7 +33,7 @@ class DeviceCase:
 
     def __init__(self, inp: Inputs, device="cuda:0", *, with_logits: bool = False, verifier=None,
                  weights=None, max_rows: int | None = None, max_roots: int | None = None,
-                 uniforms=None):
+                 uniforms=None, max_pos: int | None = None):
         import torch
         self.inp = inp
         cfg, st = inp.cfg, inp.st
@@ -52,7 +52,7 @@ class DeviceCase:
         if verifier is None:
             verifier = B.Verifier(sv_config(cfg, max_rows=max_rows or st.n_rows,
                                             max_roots=max_roots or st.n_roots,
-                                            max_pos=int(st.pos.max()) + 1),
+                                            max_pos=max_pos or int(st.pos.max()) + 1),
                                   self.w_o, self.w_lm)
         self.ver = verifier
         self.outs = verifier.alloc_outputs(st.n_rows, st.n_roots, self.device, with_logits)
@@ -69,11 +69,12 @@ class DeviceCase:
             self.u_bonus = torch.from_numpy(np.ascontiguousarray(uniforms[1], np.float32)).to(self.device)
         self.refresh()
 
-    def refresh(self):
+    def refresh(self, upload_drafts: bool = True):
         """Rebuild the C structs (after draft ids or structure change)."""
         import torch
         st = self.inp.st
-        self.draft_ids = torch.from_numpy(np.ascontiguousarray(self.inp.draft_ids, np.int32)).to(self.device)
+        if upload_drafts:
+            self.draft_ids = torch.from_numpy(np.ascontiguousarray(self.inp.draft_ids, np.int32)).to(self.device)
         self.sv_in, self.sv_out, self._keep = B.Verifier.make_structs(
             st.parent, st.pos, st.root_kv_off, st.root_kv_len, self.kv_k, self.kv_v, self.q, self.k,
             self.v, self.draft_ids, self.dl, self.outs,
@@ -85,6 +86,50 @@ class DeviceCase:
         import torch
         s = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
         self.ver.run(self.sv_in, self.sv_out, s)
+
+    def commit(self, stream=None):
+        """Enqueue the commit of the last run (accepted paths into the cache)."""
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
+        self.ver.commit(self.sv_in, self.sv_out, self.kv_k, self.kv_v, s)
+
+    def next_step(self, accept_len, rows=None, draft_ids=None):
+        """Lay out the next chain step after a commit: each tree keeps its
+        cache segment and sees accept_len more entries, and its rows move
+        accept_len positions on (the new root follows the last committed
+        row).  `rows` replaces the row tensors: a dict of host arrays
+        (q_rows, k_rows, v_rows, drafter_logits) or of device tensors
+        (q, k, v, dl).  Draft ids: `draft_ids` (host or device int32) or
+        zeros."""
+        import torch
+        st = self.inp.st
+        acc = np.asarray(accept_len, np.int64)
+        roots = np.nonzero(st.parent < 0)[0]
+        ends = list(roots[1:]) + [st.n_rows]
+        pos = st.pos.astype(np.int64)
+        for t, (a, b) in enumerate(zip(roots, ends)):
+            pos[a:b] += acc[t]
+        st.pos = pos.astype(np.int32)
+        st.root_kv_len = (st.root_kv_len.astype(np.int64) + acc).astype(np.int32)
+        if rows is not None:
+            dt = self.inp.cfg.dtype
+            if "q" in rows:
+                self.q, self.k, self.v, self.dl = rows["q"], rows["k"], rows["v"], rows["dl"]
+            else:
+                self.q = to_device(rows["q_rows"], dt, self.device)
+                self.k = to_device(rows["k_rows"], dt, self.device)
+                self.v = to_device(rows["v_rows"], dt, self.device)
+                self.dl = to_device(rows["drafter_logits"], dt, self.device)
+                self.inp.q_rows, self.inp.k_rows = rows["q_rows"], rows["k_rows"]
+                self.inp.v_rows, self.inp.drafter_logits = rows["v_rows"], rows["drafter_logits"]
+        on_device = draft_ids is not None and not isinstance(draft_ids, np.ndarray)
+        if draft_ids is None:
+            self.inp.draft_ids = np.zeros(st.n_rows, np.int32)
+        elif not on_device:
+            self.inp.draft_ids = draft_ids.astype(np.int32)
+        else:
+            self.draft_ids = draft_ids
+        self.refresh(upload_drafts=not on_device)
 
     def results(self) -> dict:
         import torch

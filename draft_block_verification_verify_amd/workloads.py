@@ -286,16 +286,17 @@ def make_weights(cfg_id: int | Config, seed: int = 0):
 
 
 def plant_chain_drafts(inp: Inputs, target_argmax: np.ndarray, *,
-                       k_per_tree=None) -> np.ndarray:
+                       k_per_tree=None, rnd: int = 0) -> np.ndarray:
     """Plant chain drafts: per sequence draw k ~ U{0..gamma}; drafts 1..k copy
     the target's greedy token at the parent row, draft k+1 (if any) is uniform
     over the vocabulary minus that token, later drafts are uniform.
 
     `target_argmax` is whatever the caller uses as the target's greedy token
-    per row.  Returns k per tree and writes inp.draft_ids in place.
+    per row.  `rnd` > 0 draws the plants of step `rnd` of a multi-step run.
+    Returns k per tree and writes inp.draft_ids in place.
     """
     st, V = inp.st, inp.cfg.vocab
-    r = _rng(inp.cfg.cfg_id, inp.seed, "plant")
+    r = _rng(inp.cfg.cfg_id, inp.seed, "plant", 0, rnd)
     roots = np.nonzero(st.parent < 0)[0]
     ends = list(roots[1:]) + [st.n_rows]
     ids = np.zeros(st.n_rows, np.int32)

@@ -144,6 +144,33 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
  * one handle must be ordered by the caller (same stream, or events). */
 sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *out, void *stream);
 
+/* Commit of the handle's most recent step: the step after verify, which keeps
+ * the accepted drafts and resumes after them (sionic.ai "Solar Open2 250B
+ * DSpark", section 1; section 6 names committing accepted tokens as the part
+ * of the loop that follows verify).  For tree t with visible prefix
+ * [root_kv_off[t], root_kv_off[t] + root_kv_len[t]), the accepted path -- the
+ * root, then every accepted draft in depth order, accept_len[t] rows ending at
+ * last_row[t] -- is written to cache entries root_kv_off[t] + root_kv_len[t]
+ * + j, j = 0 .. accept_len[t] - 1: K = the row key rotated at its semantic
+ * position (as the step computed it), V = the row value, both in cfg->dtype.
+ * Paths through a tree are compacted this way.  The bonus token is not
+ * written: it is the next step's root, at the position after the last
+ * committed row, seeing root_kv_len[t] + accept_len[t] entries.
+ *
+ * `in` and `out` are those of the most recent spec_verify_run on this handle
+ * (same host arrays, same v_rows; accept_len and last_row are read on the
+ * device, so the host does not wait), and `stream` is that run's stream:
+ * otherwise SV_ERR_INVALID_ARG.  kv_k and kv_v are the cache, DEVICE
+ * [in->kv_tokens, Hkv, d], writable, 16-byte aligned (normally the run's
+ * in->kv_k and in->kv_v).  SV_ERR_BAD_TREE when some tree's possible write
+ * range [off + len, off + len + depth + 1), depth = its deepest row, leaves
+ * [0, kv_tokens) or overlaps another tree's visible prefix or write range (a
+ * shared stem cannot take commits).  Enqueues one kernel; never synchronises.
+ * The next spec_verify_run on the handle replaces what a later commit would
+ * read. */
+sv_status spec_verify_commit(sv_handle *h, const sv_inputs *in, const sv_outputs *out, void *kv_k, void *kv_v,
+                             void *stream);
+
 /* Wait for the handle's last enqueued step, then free everything it owns.
  * NULL is accepted. */
 sv_status spec_verify_destroy(sv_handle *h);
