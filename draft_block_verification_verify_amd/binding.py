@@ -64,6 +64,9 @@ SYMBOLS = {
     "spec_verify_run": (C.c_int, [C.c_void_p, C.POINTER(SvInputs), C.POINTER(SvOutputs), C.c_void_p]),
     "spec_verify_commit": (C.c_int, [C.c_void_p, C.POINTER(SvInputs), C.POINTER(SvOutputs), C.c_void_p, C.c_void_p,
                                      C.c_void_p]),
+    "spec_verify_schedule": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
+                                       C.c_void_p, C.c_int32, C.c_void_p, C.POINTER(C.c_double),
+                                       C.POINTER(C.c_double)]),
     "spec_verify_destroy": (C.c_int, [C.c_void_p]),
     "spec_verify_last_error": (C.c_char_p, []),
     "spec_verify_profile": (C.c_int, [C.c_void_p, C.c_int32]),
@@ -112,6 +115,23 @@ def spec_verify_commit(h, inputs: SvInputs, outputs: SvOutputs, kv_k: int, kv_v:
                        stream: int | None = None) -> None:
     _check(lib().spec_verify_commit(h, C.byref(inputs), C.byref(outputs), C.c_void_p(kv_k), C.c_void_p(kv_v),
                                     C.c_void_p(stream or 0)))
+
+
+def spec_verify_schedule(n_cand, cand_parent, cand_conf, curve_rows, curve_ms, max_rows: int = 0):
+    """Host-only budget schedule (see spec_verify.h).  Candidate arrays are
+    the requests' candidates one after another.  Returns (selected int32
+    array, expected tokens, step ms)."""
+    n_cand = host_i32(n_cand)
+    par = host_i32(cand_parent)
+    conf = np.ascontiguousarray(np.asarray(cand_conf, dtype=np.float32))
+    cr = host_i32(curve_rows)
+    cm = np.ascontiguousarray(np.asarray(curve_ms, dtype=np.float32))
+    sel = np.zeros(max(int(n_cand.sum()), 1), np.int32)
+    tok, ms = C.c_double(), C.c_double()
+    _check(lib().spec_verify_schedule(int(n_cand.shape[0]), n_cand.ctypes.data, par.ctypes.data, conf.ctypes.data,
+                                      int(cr.shape[0]), cr.ctypes.data, cm.ctypes.data, int(max_rows),
+                                      sel.ctypes.data, C.byref(tok), C.byref(ms)))
+    return sel[:int(n_cand.sum())], tok.value, ms.value
 
 
 def spec_verify_destroy(h) -> None:

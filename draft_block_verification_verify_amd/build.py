@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libspecverify.so")
 
-SOURCES = ["host.cpp", "plan.cpp", "k_attn.hip", "k_gemm.hip", "k_vocab.hip", "k_commit.hip"]
+SOURCES = ["host.cpp", "plan.cpp", "schedule.cpp", "k_attn.hip", "k_gemm.hip", "k_vocab.hip", "k_commit.hip"]
 ARCH = "gfx950"
 
 

@@ -11,6 +11,7 @@
 
 #include "launch.hpp"
 #include "plan.hpp"
+#include "schedule.hpp"
 #include "spec_verify.h"
 
 namespace {
@@ -640,6 +641,18 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     }
     L.lay = lay;
   }
+  return SV_OK;
+}
+
+sv_status spec_verify_schedule(int32_t n_req, const int32_t *n_cand, const int32_t *cand_parent,
+                               const float *cand_conf, int32_t n_curve, const int32_t *curve_rows,
+                               const float *curve_ms, int32_t max_rows, int32_t *selected,
+                               double *expected_tokens, double *step_ms) {
+  g_err.clear();
+  std::string err;
+  const int st = sv::schedule_budget(n_req, n_cand, cand_parent, cand_conf, n_curve, curve_rows, curve_ms, max_rows,
+                                     selected, expected_tokens, step_ms, &err);
+  if (st != sv::P_OK) return fail(sv_status(st), err);
   return SV_OK;
 }
 

@@ -171,6 +171,41 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
 sv_status spec_verify_commit(sv_handle *h, const sv_inputs *in, const sv_outputs *out, void *kv_k, void *kv_v,
                              void *stream);
 
+/* Verify budget over a batch of requests: which draft candidates each request
+ * verifies in the next step.  A confidence head's per-position pass
+ * probabilities, multiplied along a path, give the probability that the
+ * position is accepted; the batch's verify budget goes to the positions most
+ * likely to pass, across all requests, to maximise throughput on a measured
+ * hardware curve, so gamma varies per request and with load (VESSL AI
+ * "Speculative Decoding Part 2", DSpark section; branch scores as path
+ * products, EAGLE-2, same page).
+ *
+ * Request r offers n_cand[r] >= 0 candidates; the candidate arrays hold the
+ * requests one after another.  cand_parent[k] is the candidate (request-local
+ * index, earlier than k) that candidate k follows, or -1 for the request's
+ * last committed token (its verify root); cand_conf[k] in [0, 1] is the
+ * probability that k passes given that its parent passed (a chain: parent k-1).
+ * A candidate's score is the product of conf along its path.  Every request
+ * verifies its root, so selecting m candidates makes a step of n_req + m rows
+ * with expected n_req + (sum of their scores) committed tokens.  Step times
+ * come from the measured curve (curve_rows strictly increasing, curve_ms
+ * positive and non-decreasing): linear between points, the first value below
+ * the first point, extended from the last two points past the last.  The call
+ * selects the candidates that maximise expected tokens per ms -- the m highest
+ * scores (ties: earlier request, then earlier candidate; this keeps each
+ * selected candidate's parent selected) for the best m, the smallest m on ties
+ * -- with at most max_rows rows when max_rows > 0.
+ *
+ * HOST memory only, no GPU work, no handle.  selected[k] (int32 per
+ * candidate) is set to 1 or 0; *expected_tokens and *step_ms (may be NULL)
+ * receive the chosen step's figures.  SV_ERR_INVALID_ARG for bad counts,
+ * confidences or curve, SV_ERR_BAD_TREE for a bad parent, SV_ERR_CAPACITY when
+ * max_rows is below n_req. */
+sv_status spec_verify_schedule(int32_t n_req, const int32_t *n_cand, const int32_t *cand_parent,
+                               const float *cand_conf, int32_t n_curve, const int32_t *curve_rows,
+                               const float *curve_ms, int32_t max_rows, int32_t *selected,
+                               double *expected_tokens, double *step_ms);
+
 /* Wait for the handle's last enqueued step, then free everything it owns.
  * NULL is accepted. */
 sv_status spec_verify_destroy(sv_handle *h);
