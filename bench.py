@@ -209,6 +209,119 @@ def bench_rounds(args, cfg) -> int:
     return 0
 
 
+def _sub_batch(W, inp, gam, drafts_full):
+    """The chains' first gam[i] + 1 rows of a generated chain batch (same
+    prefixes, same row tensors), with the full batch's draft ids."""
+    import dataclasses
+    st = inp.st
+    roots = np.nonzero(st.parent < 0)[0]
+    idx, parent = [], []
+    for r, g in zip(roots, gam):
+        s0 = len(idx)
+        for j in range(int(g) + 1):
+            idx.append(int(r) + j)
+            parent.append(-1 if j == 0 else s0 + j - 1)
+    idx = np.array(idx)
+    draft_of = np.cumsum(st.parent >= 0) - 1          # draft-row number of each non-root row
+    drows = [draft_of[i] for i in idx if st.parent[i] >= 0]
+    sub_st = W.Structure(np.array(parent, np.int32), st.pos[idx].astype(np.int32), st.root_kv_off.copy(),
+                         st.root_kv_len.copy(), st.kv_tokens)
+    sub = dataclasses.replace(inp, st=sub_st, q_rows=inp.q_rows[idx], k_rows=inp.k_rows[idx],
+                              v_rows=inp.v_rows[idx], drafter_logits=inp.drafter_logits[drows],
+                              draft_ids=drafts_full[idx].astype(np.int32))
+    return sub
+
+
+def bench_schedule(args, cfg) -> int:
+    """Verify budget over the concurrency batch: measure the step time of
+    the batch at uniform gamma = 0..7 (the hardware curve), give request i a
+    pass probability a_i ~ U(0.4, 0.95) per position and plant its drafts so
+    that each next draft is accepted with probability a_i (draws fixed by the
+    seed), then run, on the GPU, fixed-gamma batches and the scheduled
+    ragged batch and count the tokens they commit per ms."""
+    import torch
+    from draft_block_verification_verify_amd import binding as B
+    from draft_block_verification_verify_amd import workloads as W
+    from draft_block_verification_verify_amd.runner import DeviceCase
+
+    if cfg.kind != "multichain":
+        print("--schedule takes the concurrency workload (--workload 5)", file=sys.stderr)
+        return 2
+    G = cfg.gamma
+    inp = W.make_inputs(cfg, args.seed)
+    st = inp.st
+    R = st.n_roots
+    full = DeviceCase(inp)
+    full.run()
+    greedy = full.results()["argmax"]
+    # planted acceptance: k_i ~ truncated geometric with continuation a_i
+    rng = np.random.default_rng([args.seed, 4242])
+    a = rng.uniform(0.4, 0.95, R).astype(np.float32)
+    ks = np.zeros(R, np.int64)
+    for i in range(R):
+        while ks[i] < G and rng.random() < a[i]:
+            ks[i] += 1
+    W.plant_chain_drafts(inp, greedy, k_per_tree=ks)
+    drafts_full = inp.draft_ids.copy()
+    kv = (full.kv_k, full.kv_v)
+    weights = (full.w_o, full.w_lm)
+
+    def timed(gam, steps):
+        sub = _sub_batch(W, inp, gam, drafts_full)
+        dc = DeviceCase(sub, verifier=full.ver, weights=weights, kv=kv)
+        for _ in range(3):
+            dc.run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            dc.run()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        out = dc.results()
+        return ms, int(out["accept_len"].sum()), sub.st.n_rows, out["accept_len"]
+
+    curve_g = [0, 1, 2, 3, 5, 7]
+    curve = []
+    for g in curve_g:
+        ms, _, rows, _ = timed([g] * R, args.steps)
+        curve.append((rows, ms))
+        log(f"[schedule] gamma {g}: {rows} rows, {ms:.3f} ms")
+    xs = [c[0] for c in curve]
+    ys = list(np.maximum.accumulate(np.array([c[1] for c in curve], np.float32)))
+    par = [j - 1 for _ in range(R) for j in range(G)]
+    conf = [float(a[i]) for i in range(R) for _ in range(G)]
+    sel, pred_tok, pred_ms = B.spec_verify_schedule([G] * R, par, conf, xs, ys)
+    gam = sel.reshape(R, G).sum(axis=1)
+    strategies = {}
+    for name, gv in [("fixed_gamma_1", [1] * R), ("fixed_gamma_3", [3] * R), ("fixed_gamma_7", [G] * R),
+                     ("scheduled", list(gam))]:
+        ms, tok, rows, acc = timed(gv, args.steps)
+        want = np.minimum(ks, np.asarray(gv)) + 1
+        strategies[name] = {"rows": rows, "ms": ms, "tokens": tok, "tokens_per_ms": tok / ms,
+                            "planted_ok": bool((acc == want).all())}
+        log(f"[schedule] {name}: {rows} rows, {ms:.3f} ms, {tok} tokens")
+    full.close()
+    res = {
+        "metric": "committed tokens per ms of one verify step, scheduled budget vs fixed gamma",
+        "value": strategies["scheduled"]["tokens_per_ms"] * 1e3,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": 3,
+        "ms_per_step": strategies["scheduled"]["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; per-request pass probabilities U(0.4, 0.95), planted acceptance)",
+        "config": {"workload": cfg.name, "sequences": R, "max_gamma": G, "seed": args.seed},
+        "schedule": {"curve_rows": xs, "curve_ms": [float(y) for y in ys], "gamma": [int(g) for g in gam],
+                     "predicted_tokens": pred_tok, "predicted_ms": pred_ms, "strategies": strategies},
+    }
+    print(json.dumps(res))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,6 +334,9 @@ def main() -> int:
     ap.add_argument("--sample", action="store_true",
                     help="T = 1 stochastic verification (drafts drawn from the drafter, seeded uniforms)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--schedule", action="store_true",
+                    help="conc32: measure the rows -> ms curve, then compare fixed gamma with the verify-budget "
+                         "schedule on synthetic per-request confidences")
     ap.add_argument("--rounds", type=int, default=0,
                     help="chain workloads: time R decode steps of verify + commit (host reads the accept "
                          "lengths each step) instead of the single verify step")
@@ -243,6 +359,8 @@ def main() -> int:
     cfg = W.CONFIGS[args.workload]
     if args.rounds:
         return bench_rounds(args, cfg)
+    if args.schedule:
+        return bench_schedule(args, cfg)
     log(f"[bench] generating {cfg.name} seed {args.seed}")
     t0 = time.perf_counter()
     inp = W.make_inputs(cfg, args.seed)

@@ -33,14 +33,17 @@ class DeviceCase:
 
     def __init__(self, inp: Inputs, device="cuda:0", *, with_logits: bool = False, verifier=None,
                  weights=None, max_rows: int | None = None, max_roots: int | None = None,
-                 uniforms=None, max_pos: int | None = None):
+                 uniforms=None, max_pos: int | None = None, kv=None):
         import torch
         self.inp = inp
         cfg, st = inp.cfg, inp.st
         self.device = torch.device(device)
         dt = cfg.dtype
-        self.kv_k = to_device(inp.kv_k, dt, device) if st.kv_tokens > 0 else None
-        self.kv_v = to_device(inp.kv_v, dt, device) if st.kv_tokens > 0 else None
+        if kv is not None:                    # the cache already on the device (shared)
+            self.kv_k, self.kv_v = kv
+        else:
+            self.kv_k = to_device(inp.kv_k, dt, device) if st.kv_tokens > 0 else None
+            self.kv_v = to_device(inp.kv_v, dt, device) if st.kv_tokens > 0 else None
         self.q = to_device(inp.q_rows, dt, device)
         self.k = to_device(inp.k_rows, dt, device)
         self.v = to_device(inp.v_rows, dt, device)

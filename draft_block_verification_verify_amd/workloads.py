@@ -161,18 +161,20 @@ class Structure:
         return int(self.root_kv_off.shape[0])
 
 
-def chain_structure(prefix_lens, gamma: int, slack: int = 0) -> Structure:
-    """Independent chains: sequence s = root (last committed token) + gamma drafts.
+def chain_structure(prefix_lens, gamma, slack: int = 0) -> Structure:
+    """Independent chains: sequence s = root (last committed token) + gamma
+    drafts (`gamma` an int, or one count per sequence).
 
     Each sequence owns a KV segment of L_s + slack entries (the slack takes
     committed rows of later steps); its rows sit at positions L_s, L_s+1,
-    ..., L_s+gamma.
+    ..., L_s+gamma_s.
     """
     parent, pos, offs, lens = [], [], [], []
     off = 0
-    for L in prefix_lens:
+    gammas = [int(gamma)] * len(prefix_lens) if np.isscalar(gamma) else [int(g) for g in gamma]
+    for L, g in zip(prefix_lens, gammas):
         start = len(parent)
-        for i in range(gamma + 1):
+        for i in range(g + 1):
             parent.append(-1 if i == 0 else start + i - 1)
             pos.append(int(L) + i)
         offs.append(off)

@@ -380,3 +380,35 @@ def test_parity_full_size_sampled(cfg_id):
     P.compare(ref, gpu, st.parent, inp.draft_ids, rows=rows, logits_ref=ref["logits"], logits_gpu=gpu["logits"],
               report=rep)
     _record(f"{cfg.name}/full-sampled", rep)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_parity_ragged_gamma(seed):
+    # per-sequence draft counts, zero included (what a verify-budget schedule
+    # produces); fresh rows on the same prefixes
+    from draft_block_verification_verify_amd.runner import DeviceCase
+    cfg = MINIS["c5m"]
+    base = W.make_inputs(cfg, seed)
+    lens = base.st.root_kv_len
+    r = np.random.default_rng(50 + seed)
+    gam = r.integers(0, cfg.gamma + 1, size=len(lens))
+    gam[0] = 0
+    st = W.chain_structure(lens, gam)
+    n, nd = st.n_rows, int((st.parent >= 0).sum())
+    rows = W.round_rows(cfg, seed, 1, n, nd)
+    inp = dataclasses.replace(base, st=st, q_rows=rows["q_rows"], k_rows=rows["k_rows"], v_rows=rows["v_rows"],
+                              drafter_logits=rows["drafter_logits"], draft_ids=np.zeros(n, np.int32))
+    _say(f"[case] ragged gamma seed={seed} rows={n}")
+    cd = O.cfg_dict(cfg)
+    W.plant_chain_drafts(inp, O.target_greedy(cd, O.inp_dict(inp)))
+    ref = O.verify(cd, O.inp_dict(inp), keep_logits=True)
+    dc = DeviceCase(inp, with_logits=True)
+    try:
+        dc.run()
+        gpu = dc.results()
+    finally:
+        dc.close()
+    rep = {}
+    P.check_self_consistency(st.parent, inp.draft_ids, gpu)
+    P.compare(ref, gpu, st.parent, inp.draft_ids, logits_ref=ref["logits"], logits_gpu=gpu["logits"], report=rep)
+    _record(f"ragged/seed{seed}", rep)
