@@ -61,6 +61,14 @@ from their fp32 / bf16 bits):
    value, in the cache's number format (bf16 or fp32).  The bonus token is
    not committed; it is the root of the next step, at the position after the
    last committed row, seeing len + accept_len cache entries.
+11. FP8 LM head (weight format "fp8"; the pages' fastest serving runs the
+   target in FP8: sionic.ai page, section 5).  W8A8 in OCP e4m3 (4 exponent
+   bits, bias 7, 3 mantissa bits, largest finite 448, subnormal step 2^-9,
+   no infinities), values rounded to nearest, ties to even.  Each LM-head
+   row n gets the power-of-two scale s_n = 2^e, e the smallest integer with
+   max_k |W[n, k]| <= 448 * 2^e (1 for a zero row); each normalised hidden
+   row t likewise a_t from max |h_t|.  q = e4m3(value / scale) (an exact
+   division), and logits[t, n] = a_t s_n sum_k q_h[t, k] q_w[n, k].
 """
 from __future__ import annotations
 
@@ -331,6 +339,43 @@ def hidden_states(cfg, inp, rows) -> dict:
     return {i: project_norm(w_o, att[i], cfg["norm_eps"]) for i in rows}
 
 
+def e4m3(x) -> np.ndarray:
+    """Nearest OCP e4m3 value (ties to even) of each |x| <= 448, as fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if np.any(a > 448.0):
+        raise ValueError("e4m3 takes |x| <= 448")
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))        # a = m 2^ex, m in [0.5, 1)
+    step = np.where(a < 2.0 ** -6, 2.0 ** -9, np.ldexp(1.0, ex - 4))   # 3 mantissa bits below 2^(ex-1)
+    return np.sign(x) * np.round(a / step) * step     # np.round: half to even
+
+
+def pow2_scale(amax: float) -> float:
+    """Smallest 2^e with amax <= 448 * 2^e (1 when amax is 0)."""
+    if amax == 0.0:
+        return 1.0
+    e = int(np.ceil(np.log2(amax / 448.0)))
+    while amax > 448.0 * 2.0 ** e:
+        e += 1
+    while amax <= 448.0 * 2.0 ** (e - 1):
+        e -= 1
+    return 2.0 ** e
+
+
+def lm_head_fp8(cfg, w_lm, hs: np.ndarray, chunk: int = 8192) -> np.ndarray:
+    """Step 11: logits [m, V] of the W8A8 e4m3 LM head."""
+    a = np.array([pow2_scale(float(np.abs(h).max())) for h in hs])
+    qh = np.stack([e4m3(h / s) for h, s in zip(hs, a)]) if len(hs) else hs
+    V = w_lm.shape[0]
+    out = np.empty((hs.shape[0], V))
+    for lo in range(0, V, chunk):
+        w = decode(w_lm[lo:lo + chunk], cfg["dtype"])
+        sw = np.array([pow2_scale(float(np.abs(r).max())) for r in w])
+        qw = e4m3(w / sw[:, None])
+        out[:, lo:lo + chunk] = (qh @ qw.T) * a[:, None] * sw[None, :]
+    return out
+
+
 def lm_head(cfg, w_lm, hs: np.ndarray, chunk: int = 8192) -> np.ndarray:
     """logits [m, V] = hs [m, hidden] . W_lm^T, decoding W_lm chunk by chunk."""
     V = w_lm.shape[0]
@@ -357,7 +402,8 @@ def verify(cfg, inp, trees=None, keep_logits: bool = False) -> dict:
     rows = [i for t in trees for i in forest.tree_rows[t]]
     hs = hidden_states(cfg, inp, rows)
     H = np.stack([hs[i] for i in rows]) if rows else np.zeros((0, 1))
-    logits = lm_head(cfg, inp["w_lm"], H) if rows else np.zeros((0, 0))
+    head = lm_head_fp8 if cfg.get("weight_format") == "fp8" else lm_head
+    logits = head(cfg, inp["w_lm"], H) if rows else np.zeros((0, 0))
     V = logits.shape[1] if rows else 0
 
     res = {k: np.full(n, np.nan) for k in ("row_max", "row_lse", "gap", "overlap", "survival")}

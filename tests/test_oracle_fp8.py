@@ -1,0 +1,117 @@
+"""Pins of the oracle's FP8 (e4m3) LM head."""
+import numpy as np
+import pytest
+
+from oracle import verify_oracle as O
+
+
+def e4m3_table():
+    """Every finite e4m3 value, from the format's definition (sign, 4-bit
+    exponent with bias 7, 3-bit mantissa; code 0x7F / 0xFF is NaN)."""
+    vals = []
+    for code in range(128):
+        if code == 0x7F:
+            continue
+        e, m = code >> 3, code & 7
+        v = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        vals.append((v, m))
+    return vals
+
+
+def test_table_range():
+    vals = [v for v, _ in e4m3_table()]
+    assert max(vals) == 448.0 and sorted(vals)[1] == 2.0 ** -9
+
+
+def test_e4m3_is_nearest_even():
+    table = e4m3_table()
+    vs = np.array([v for v, _ in table])
+    ms = np.array([m for _, m in table])
+    r = np.random.default_rng(3)
+    x = np.concatenate([r.uniform(-448, 448, 3000), r.uniform(-0.05, 0.05, 3000),
+                        # exact midpoints between neighbours
+                        (np.sort(vs)[:-1] + np.sort(vs)[1:]) / 2])
+    got = O.e4m3(x)
+    for xi, g in zip(x, got):
+        d = np.abs(vs - abs(xi))
+        best = np.nonzero(d == d.min())[0]
+        if len(best) == 1:
+            want = vs[best[0]]
+        else:                       # a tie: the even mantissa
+            want = vs[best[ms[best] % 2 == 0][0]]
+        assert abs(g) == want and (g == 0 or np.sign(g) == np.sign(xi))
+    with pytest.raises(ValueError):
+        O.e4m3([449.0])
+
+
+def test_pow2_scale_definition():
+    for amax in [0.0, 1e-30, 0.3, 1.0, 447.99, 448.0, 448.01, 896.0, 1e6]:
+        s = O.pow2_scale(amax)
+        if amax == 0:
+            assert s == 1.0
+            continue
+        e = int(np.log2(s))
+        assert s == 2.0 ** e and amax <= 448 * s and amax > 448 * s / 2
+
+
+def test_representable_inputs_are_lossless():
+    # every weight row and hidden row is a power of two times values e4m3
+    # holds exactly at that scale: the FP8 head equals the exact product
+    r = np.random.default_rng(1)
+    vals = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, -1.0, -2.5, 448.0])
+    k = 2.0 ** r.integers(-6, 6, size=(40, 1))
+    w = r.choice(vals, size=(40, 64)) * k
+    w[:, 0] = 448.0 * k[:, 0]                     # pins each row's scale to k
+    h = r.choice(vals, size=(3, 64)) * 0.25
+    h[:, 0] = 448.0 * 0.25
+    cfg = {"dtype": "f64"}
+    got = O.lm_head_fp8(cfg, w, h)
+    np.testing.assert_array_equal(got, h @ w.T)
+
+
+def test_power_of_two_row_scaling_is_exact():
+    r = np.random.default_rng(2)
+    w = r.standard_normal((16, 128)) * 0.02
+    h = r.standard_normal((2, 128))
+    cfg = {"dtype": "f64"}
+    base = O.lm_head_fp8(cfg, w, h)
+    w2 = w.copy()
+    w2[3] *= 2.0 ** 5
+    got = O.lm_head_fp8(cfg, w2, h)
+    np.testing.assert_array_equal(got[:, 3], base[:, 3] * 32.0)
+    np.testing.assert_array_equal(np.delete(got, 3, axis=1), np.delete(base, 3, axis=1))
+
+
+def test_error_within_the_rounding_bound():
+    # each quantised value is within half a step of its input: a relative
+    # 2^-4 for normals, 2^-10 absolute (times the scale) for subnormals
+    r = np.random.default_rng(4)
+    w = r.standard_normal((64, 256)) * 0.02
+    h = r.standard_normal((4, 256))
+    cfg = {"dtype": "f64"}
+    got = O.lm_head_fp8(cfg, w, h)
+    exact = h @ w.T
+    sw = np.array([O.pow2_scale(np.abs(x).max()) for x in w])
+    sh = np.array([O.pow2_scale(np.abs(x).max()) for x in h])
+    dw = np.maximum(np.abs(w) * 2.0 ** -4, 2.0 ** -10 * sw[:, None])
+    dh = np.maximum(np.abs(h) * 2.0 ** -4, 2.0 ** -10 * sh[:, None])
+    bound = (np.abs(h) + dh) @ dw.T + dh @ np.abs(w).T
+    assert (np.abs(got - exact) <= bound * (1 + 1e-12)).all()
+    assert np.abs(got - exact).max() > 0          # not trivially exact
+
+
+def test_fp8_verify_step():
+    from draft_block_verification_verify_amd import workloads as W
+    cfg = W.Config(cfg_id=93, name="tiny-fp8", dtype="bf16", n_q_heads=4, n_kv_heads=2, head_dim=16, hidden=64,
+                   vocab=500, kind="multichain", gamma=5, n_seqs=3, min_len=0, max_len=40, w_lm_std=0.15)
+    inp = W.make_inputs(cfg, 0)
+    c8 = dict(O.cfg_dict(cfg), weight_format="fp8")
+    a = O.inp_dict(inp)
+    res8 = O.verify(c8, a, keep_logits=True)
+    W.plant_chain_drafts(inp, res8["argmax"], k_per_tree=[cfg.gamma] * inp.st.n_roots)
+    res8 = O.verify(c8, O.inp_dict(inp), keep_logits=True)
+    assert (res8["accept_len"] == cfg.gamma + 1).all()
+    ref = O.verify(O.cfg_dict(cfg), O.inp_dict(inp), keep_logits=True)
+    # sanity only (the bounds are pinned above): the FP8 head tracks the bf16 one
+    a8, ab = res8["logits"].ravel(), ref["logits"].ravel()
+    assert np.abs(a8 - ab).max() > 0 and np.corrcoef(a8, ab)[0, 1] > 0.99
