@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "_lib", "libspecverify.so")
 SV_OK, SV_ERR_INVALID_ARG, SV_ERR_BAD_TREE, SV_ERR_CAPACITY = 0, -1, -2, -3
 SV_ERR_UNSUPPORTED, SV_ERR_HIP, SV_ERR_OOM = -4, -5, -6
 SV_F32, SV_BF16 = 0, 1
+SV_WEIGHTS_NATIVE, SV_WEIGHTS_FP8 = 0, 1
 STATUS_NAMES = {0: "SV_OK", -1: "SV_ERR_INVALID_ARG", -2: "SV_ERR_BAD_TREE", -3: "SV_ERR_CAPACITY",
                 -4: "SV_ERR_UNSUPPORTED", -5: "SV_ERR_HIP", -6: "SV_ERR_OOM"}
 
@@ -26,7 +27,7 @@ class SvConfig(C.Structure):
                 ("hidden", C.c_int32), ("vocab", C.c_int32), ("dtype", C.c_int32),
                 ("rope_base", C.c_float), ("norm_eps", C.c_float),
                 ("max_rows", C.c_int32), ("max_roots", C.c_int32), ("max_tree_rows", C.c_int32),
-                ("max_pos", C.c_int32)]
+                ("max_pos", C.c_int32), ("weight_format", C.c_int32)]
 
 
 class SvInputs(C.Structure):

@@ -42,6 +42,10 @@ struct sv_handle {
   // weights the kernels read: for bf16, fp16 copies (W_o row-major, W_lm in
   // the blocked layout of the LM-head launches)
   const void *w_o = nullptr, *w_lm = nullptr;
+  // FP8 LM head: e4m3 W_lm (blocked) and its row scales; per-run row scales
+  // of the activations
+  uint8_t *w_lm8 = nullptr;
+  float *w_scale = nullptr, *a_scale = nullptr;
   int32_t *d_bad = nullptr;
   int device = 0, n_cu = 256, target_items = 1024;
   int elt = 2;
@@ -132,7 +136,7 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
   *out = nullptr;
   if (!w_o || !w_lm) return fail(SV_ERR_INVALID_ARG, "w_o and w_lm must be non-null device pointers");
   sv::Dims dm{cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, cfg->hidden, cfg->vocab, cfg->dtype,
-              cfg->max_rows,  cfg->max_roots,  cfg->max_tree_rows, cfg->max_pos};
+              cfg->max_rows,  cfg->max_roots,  cfg->max_tree_rows, cfg->max_pos, cfg->weight_format};
   std::string err;
   const int pc = sv::check_dims(dm, &err);
   if (pc != sv::P_OK) return fail(sv_status(pc), err);
@@ -205,8 +209,15 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
     // the projections run on fp16 MFMA: keep fp16 copies of the weights
     // (W_o row-major, W_lm in the blocked layout)
     uint16_t *wo16 = nullptr, *wlm16 = nullptr;
+    const bool fp8 = dm.weight_format == SV_WEIGHTS_FP8;
     A(&wo16, size_t(H * Hq * D * 2));
-    A(&wlm16, size_t(sv::blocked_elems(V, H) * 2));
+    if (fp8) {
+      A(&h->w_lm8, size_t(sv::blocked_elems(V, H)));
+      A(&h->w_scale, size_t(ceil_div(V, 256) * 256 * 4));
+      A(&h->a_scale, size_t(R * 4));
+    } else {
+      A(&wlm16, size_t(sv::blocked_elems(V, H) * 2));
+    }
     A(&h->d_bad, 4);
     if (st == SV_OK) {
       e = hipMemsetAsync(h->d_bad, 0, 4, nullptr);
@@ -215,7 +226,12 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
       if (e == hipSuccess) e = hipMemsetAsync(h->hn, 0, std::max<size_t>(size_t(R * H * 4), size_t(sv::blocked_elems(R, H) * 2)), nullptr);
       if (e == hipSuccess) {
         sv::launch_bf16_to_f16(static_cast<const uint16_t *>(w_o), wo16, H * Hq * D, h->d_bad, nullptr);
-        sv::launch_bf16_to_f16_blocked(static_cast<const uint16_t *>(w_lm), wlm16, int(V), int(H), h->d_bad, nullptr);
+        if (fp8)
+          sv::launch_quant_fp8_blocked(static_cast<const uint16_t *>(w_lm), h->w_lm8, h->w_scale, int(V), int(H),
+                                       nullptr);
+        else
+          sv::launch_bf16_to_f16_blocked(static_cast<const uint16_t *>(w_lm), wlm16, int(V), int(H), h->d_bad,
+                                         nullptr);
         e = hipGetLastError();
       }
       int32_t bad = 0;
@@ -421,7 +437,8 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   };
 
   float *logits = out->logits ? out->logits : h->logits;
-  const int tile_w = bf16 ? sv::lm_tile_width(n) : 256;
+  const bool fp8 = dm.weight_format == SV_WEIGHTS_FP8;
+  const int tile_w = bf16 && !fp8 ? sv::lm_tile_width(n) : 256;
   const int n_tiles = int(ceil_div(V, tile_w));
 
   sv::VocabArgs va{};
@@ -464,7 +481,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   // activation format of the projections: fp16 hi + lo planes for the
   // skinny launch, fp16 for the tiled one (blocked layout for the LM head)
   const int act_mode = n <= 64 ? sv::ACT_SPLIT : sv::ACT_F16;
-  const int lm_act_mode = n <= 64 ? sv::ACT_SPLIT : sv::ACT_F16_BLOCKED;
+  const int lm_act_mode = fp8 ? sv::ACT_FP8_BLOCKED : n <= 64 ? sv::ACT_SPLIT : sv::ACT_F16_BLOCKED;
   const int64_t q_lo = int64_t(dm.max_rows) * Hq * D;   // lo planes start one capacity further
   const int64_t o_lo = int64_t(dm.max_rows) * Hq * D;
   const int64_t h_lo = int64_t(dm.max_rows) * H;
@@ -534,7 +551,8 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     sv::launch_gemm_bf16(g, false, splits, stream);
     end();
     begin("final_norm");
-    sv::launch_norm(h->h_part, splits, int64_t(n) * H, n, int(H), h->cfg.norm_eps, lm_act_mode, h->hn, h_lo, stream);
+    sv::launch_norm(h->h_part, splits, int64_t(n) * H, n, int(H), h->cfg.norm_eps, lm_act_mode, h->hn, h_lo,
+                    h->a_scale, stream);
     end();
     sv::GemmArgs l{};
     l.act = static_cast<const uint16_t *>(h->hn);
@@ -552,7 +570,15 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     l.t_arg = h->t_arg;
     l.n_tiles = n_tiles;
     begin("lm_head");
-    sv::launch_gemm_bf16(l, true, 1, stream);
+    if (fp8) {
+      l.W8 = h->w_lm8;
+      l.act8 = static_cast<const uint8_t *>(h->hn);
+      l.w_scale = h->w_scale;
+      l.a_scale = h->a_scale;
+      sv::launch_gemm_fp8(l, stream);
+    } else {
+      sv::launch_gemm_bf16(l, true, 1, stream);
+    }
     end();
   } else {
     begin("rope");
@@ -587,7 +613,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
                         int(Hq * D), h->h_part, stream);
     end();
     begin("final_norm");
-    sv::launch_norm(h->h_part, 1, 0, n, int(H), h->cfg.norm_eps, sv::ACT_F32, h->hn, 0, stream);
+    sv::launch_norm(h->h_part, 1, 0, n, int(H), h->cfg.norm_eps, sv::ACT_F32, h->hn, 0, nullptr, stream);
     end();
     begin("lm_head");
     sv::launch_gemm_f32(static_cast<const float *>(h->hn), n, static_cast<const float *>(h->w_lm), int(V), int(H),

@@ -437,6 +437,230 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
   }
 }
 
+
+// ----------------------------------------------------------------------------
+// FP8 LM head: the tiled launch's structure (persistent 256 x 256 tiles, 8
+// waves of 128 x 64, 4-stage DMA ring of 32 KB) on e4m3 operands in the
+// blocked layout, K steps of 64 (64 bytes per row): per step one
+// 32x32x64 e4m3 MFMA per 32 x 32 block, its operands 32 bytes of the lane's
+// row (the two lane halves take the two halves of the step).  The epilogue
+// multiplies by the row scales, then writes the tile statistics and logits.
+// ----------------------------------------------------------------------------
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ i32x8 cat8(uint4 a, uint4 b) {
+  return i32x8{int(a.x), int(a.y), int(a.z), int(a.w), int(b.x), int(b.y), int(b.z), int(b.w)};
+}
+
+// D += A . B^T on e4m3 operands (format 0), unit block scales (E8M0 127 = 2^0)
+__device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
+  constexpr bool STATS = true;
+  constexpr int PER = 4;     // DMA instructions per wave per stage (2 weight + 2 activation)
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r32 = lane & 31, kg = lane >> 5;
+  const int wn = w & 1, wt = w >> 1;
+  const int n_ttiles = (g.rows + kTBT - 1) / kTBT;
+  const int n_ntiles = (g.N + kTBN - 1) / kTBN;
+  const int n_tiles_all = ((n_ntiles + 7) / 8) * 8 * n_ttiles;
+  const int nk = g.K / 64;   // K steps of 64 e4m3 values (64 bytes per row)
+  const int Kb = g.K * 2;
+  const uint32_t lds0 = lds_addr(smem);
+  const int c4 = lane & 3;
+  int off[2];     // 2 instructions of 16 rows: rows w*32 + 16 i + lane/4 (weights and activations alike)
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int R = w * 32 + i * 16 + (lane >> 2);
+    off[i] = (w * 32 + i * 16) * 64 + lane * 16;
+    (void)R;
+  }
+  // tile i -> (weight tile, row tile); i and i+8 share the weight tile
+  auto tile_of = [&](int i, int &n_tile, int &t_tile) {
+    const int grp = i / (8 * n_ttiles), rem = i % (8 * n_ttiles);
+    n_tile = grp * 8 + rem % 8;
+    t_tile = rem / 8;
+  };
+  struct Src {
+    i32x4 rw, ra;
+  };
+  auto src_of = [&](int n_tile, int t_tile) {
+    const int n0 = n_tile * kTBN, t0 = t_tile * kTBT;
+    Src r;
+    // one column of blocks per 256-row tile: 256 * K bytes
+    const int64_t tb = int64_t(g.K) * 256;
+    r.rw = make_rsrc(g.W8 + int64_t(n_tile) * tb, uint32_t(tb));
+    r.ra = make_rsrc(g.act8 + int64_t(t_tile) * tb, uint32_t(tb));
+    (void)n0;
+    (void)t0;
+    return r;
+  };
+  auto issue = [&](const Src &sr, int s) {
+    const uint32_t base = lds0 + (s % kTST) * kTSST;
+    const int soff = s * 16384;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(sr.rw, base + (w * 32 + i * 16) * 64, off[i], soff);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(sr.ra, base + kTBN * 64 + (w * 32 + i * 16) * 64, off[i], soff);
+  };
+
+  int tile = blockIdx.x;
+  // skip tiles past the weight rows (grid rounding)
+  auto valid = [&](int i) {
+    if (i >= n_tiles_all) return false;
+    int a, b;
+    tile_of(i, a, b);
+    return a < n_ntiles;
+  };
+  while (tile < n_tiles_all && !valid(tile)) tile += gridDim.x;
+  if (tile >= n_tiles_all) return;      // whole workgroup, before any barrier
+  int n_tile, t_tile;
+  tile_of(tile, n_tile, t_tile);
+  Src cur = src_of(n_tile, t_tile);
+#pragma unroll
+  for (int p = 0; p < kTST - 1; ++p)
+    if (p < nk) issue(cur, p);
+
+  for (;;) {
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[v][t][j] = 0.f;
+
+    for (int s = 0; s < nk; ++s) {
+      const int younger = min(kTST - 2, nk - 1 - s);
+      if (younger >= 2)
+        wait_and_barrier<2 * PER>();
+      else if (younger == 1)
+        wait_and_barrier<PER>();
+      else
+        wait_and_barrier<0>();
+      if (s + kTST - 1 < nk) issue(cur, s + kTST - 1);
+      const uint8_t *base = smem + (s % kTST) * kTSST;
+      // 32 bytes of the lane's row per operand: chunks 2 kg and 2 kg + 1
+      i32x8 af[4], bf[2];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int R = wn * 128 + v * 32 + r32, sw = (R >> 1) & 3;
+        af[v] = cat8(lds16(base + R * 64 + (((2 * kg) ^ sw) << 4)), lds16(base + R * 64 + (((2 * kg + 1) ^ sw) << 4)));
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int R = wt * 64 + t * 32 + r32, sw = (R >> 1) & 3;
+        bf[t] = cat8(lds16(base + kTBN * 64 + R * 64 + (((2 * kg) ^ sw) << 4)),
+                     lds16(base + kTBN * 64 + R * 64 + (((2 * kg + 1) ^ sw) << 4)));
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[v][t] = mfma32_fp8(af[v], bf[t], acc[v][t]);
+    }
+
+    // epilogue of this tile (vector-memory waits count stores too, so the
+    // next tile's loads are issued only after the stores)
+    asm volatile("s_barrier" ::: "memory");   // every wave is done reading the ring
+    const int n0 = n_tile * kTBN, t0 = t_tile * kTBT;
+    int nb[4], tb[2];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) nb[v] = n0 + wn * 128 + v * 32;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) tb[t] = t0 + wt * 64 + t * 32;
+    GemmArgs go = g;
+    // scales: logit = a_t s_n * (code products); padding rows have scale 1
+    {
+      const float at0 = g.a_scale[min(tb[0] + r32, g.rows - 1)], at1 = g.a_scale[min(tb[1] + r32, g.rows - 1)];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float4 *ws = reinterpret_cast<const float4 *>(g.w_scale + nb[v] + 4 * kg);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 w4 = ws[2 * q];   // columns nb[v] + 8 q + 4 kg + 0..3
+          const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[v][0][4 * q + e] *= at0 * wv[e];
+            acc[v][1][4 * q + e] *= at1 * wv[e];
+          }
+        }
+      }
+    }
+    if constexpr (STATS) {
+      // (max, sumexp, argmax) per row over this wave's 128 N, then across
+      // the two N halves through a small static LDS array
+      __shared__ MaxSumArg red[2][kTBT];
+      if (n0 + kTBN > g.N) {
+        // last tile: columns past N (zero weights) must not take part
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              if (nb[v] + 8 * (j >> 2) + 4 * kg + (j & 3) >= g.N) acc[v][t][j] = -INFINITY;
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const MaxSumArg r = lane_stats<4, 2, false>(g, acc, nb, t, lane);
+        if (kg == 0) red[wn][wt * 64 + t * 32 + r32] = r;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (tid < kTBT && t0 + tid < g.rows) {
+        const MaxSumArg r = msa_merge(red[0][tid], red[1][tid]);
+        const int64_t o = int64_t(t0 + tid) * g.n_tiles + n_tile;
+        g.t_max[o] = r.m;
+        g.t_sum[o] = r.s;
+        g.t_arg[o] = r.i;
+      }
+    }
+    store_tile<4, 2>(go, acc, nb, tb, lane);
+
+    int next = tile + gridDim.x;
+    while (next < n_tiles_all && !valid(next)) next += gridDim.x;
+    const bool more = next < n_tiles_all;
+    int nn_tile = 0, nt_tile = 0;
+    Src nsrc = cur;
+    if (more) {
+      tile_of(next, nn_tile, nt_tile);
+      nsrc = src_of(nn_tile, nt_tile);
+#pragma unroll
+      for (int p = 0; p < kTST - 1; ++p)
+        if (p < nk) issue(nsrc, p);
+    }
+    if (!more) break;
+    tile = next;
+    n_tile = nn_tile;
+    t_tile = nt_tile;
+    cur = nsrc;
+  }
+}
+
+
+void launch_gemm_fp8(const GemmArgs &g, hipStream_t s) {
+  static bool attr = false;
+  static int n_cu = 256;
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_fp8_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(kTiledLds));
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess) {
+      int cu = 0;
+      if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cu > 0) n_cu = cu;
+    }
+    attr = true;
+  }
+  const int n_ntiles = (g.N + kTBN - 1) / kTBN, n_ttiles = (g.rows + kTBT - 1) / kTBT;
+  const int tiles = ((n_ntiles + 7) / 8) * 8 * n_ttiles;
+  const int grid_x = std::min(tiles, std::max(16, n_cu / 16 * 16));
+  hipLaunchKernelGGL(gemm_fp8_kernel, dim3(grid_x), dim3(512), kTiledLds, s, g);
+}
+
 int lm_tile_width(int rows) { return rows <= 64 ? 4 * 2 * 32 : kTBN; }
 
 // Split-K factor of a projection with `rows` rows: enough workgroups to
@@ -562,8 +786,83 @@ void launch_stats_from_logits(const float *logits, int rows, int V, int tile, fl
 // One workgroup of 1024 threads per row: each thread sums the split-K
 // partials of 4 columns (16-B loads, splits unrolled by 4), keeps h in LDS,
 // then scales.
+// ----------------------------------------------------------------------------
+// FP8 (OCP e4m3) encoding: 4 exponent bits (bias 7), 3 mantissa bits, largest
+// finite 448, subnormal step 2^-9; rounded to nearest, ties to even.
+// ----------------------------------------------------------------------------
+
+// code of x, |x| <= 448
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(x);
+  uint32_t code;
+  if (a < 0.015625f) {                      // below 2^-6: multiples of 2^-9
+    code = uint32_t(rintf(a * 512.0f));     // exact product; rintf rounds half to even
+  } else {
+    const uint32_t b = __float_as_uint(a);
+    const uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) & ~0xFFFFFu;   // 3 mantissa bits, half to even
+    const int e = int(r >> 23) - 127;
+    code = (uint32_t(e + 7) << 3) | ((r >> 20) & 7u);
+  }
+  return sign | code;
+}
+
+// smallest e with amax <= 448 * 2^e (0 for amax == 0)
+__device__ __forceinline__ int fp8_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int e = int(ceilf(log2f(amax / 448.0f)));
+  while (amax > ldexpf(448.0f, e)) ++e;
+  while (amax <= ldexpf(448.0f, e - 1)) --e;
+  return e;
+}
+
+// 16 consecutive values (already divided by the row scale) -> 16 codes
+__device__ __forceinline__ uint4 e4m3_pack16(const float (&v)[16]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = e4m3_code(v[4 * i]) | (e4m3_code(v[4 * i + 1]) << 8) | (e4m3_code(v[4 * i + 2]) << 16) |
+           (e4m3_code(v[4 * i + 3]) << 24);
+  return uint4{w[0], w[1], w[2], w[3]};
+}
+
+// byte offset of (row, 16-value chunk c16 of the row) in the e4m3 blocked layout
+__device__ __forceinline__ int64_t fp8_blocked_off(int64_t row, int c16, int K) {
+  const int R = int(row & 255), kb = c16 >> 2, q = c16 & 3;
+  return ((row >> 8) * (K >> 6) + kb) * 16384 + R * 64 + ((q ^ ((R >> 1) & 3)) << 4);
+}
+
+__global__ __launch_bounds__(256) void quant_fp8_blocked_kernel(const uint16_t *__restrict__ src,
+                                                               uint8_t *__restrict__ dst, float *__restrict__ scale,
+                                                               int rows, int K) {
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const bool live = row < rows;
+  float m = 0.f;
+  if (live)
+    for (int k = tid; k < K; k += 256) m = fmaxf(m, fabsf(bf2f(src[row * K + k])));
+  m = wave_max(m);
+  __shared__ float red[4];
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  const int e = fp8_exponent(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+  for (int c = tid; c < K / 16; c += 256) {
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = live ? ldexpf(bf2f(src[row * K + c * 16 + i]), -e) : 0.f;
+    *reinterpret_cast<uint4 *>(dst + fp8_blocked_off(row, c, K)) = e4m3_pack16(v);
+  }
+  if (tid == 0) scale[row] = ldexpf(1.0f, e);
+}
+
+void launch_quant_fp8_blocked(const uint16_t *src, uint8_t *dst, float *scale, int rows, int K, hipStream_t s) {
+  const int padded = (rows + 255) / 256 * 256;
+  hipLaunchKernelGGL(quant_fp8_blocked_kernel, dim3(padded), dim3(256), 0, s, src, dst, scale, rows, K);
+}
+
 __global__ __launch_bounds__(1024) void norm_kernel(const float *part, int splits, int64_t split_stride, int hidden,
-                                                    float eps, int mode, void *out, int64_t lo_off) {
+                                                    float eps, int mode, void *out, int64_t lo_off, float *a_scale) {
   extern __shared__ float hrow[];     // [hidden]
   const int row = blockIdx.x, tid = threadIdx.x;
   const float *p = part + int64_t(row) * hidden;
@@ -596,6 +895,28 @@ __global__ __launch_bounds__(1024) void norm_kernel(const float *part, int split
 #pragma unroll
   for (int i = 0; i < 16; ++i) tot += red[i];
   const float inv = 1.0f / sqrtf(tot / float(hidden) + eps);
+  if (mode == ACT_FP8_BLOCKED) {
+    // row scale from the largest |y|, then 16 codes per thread step
+    float m = 0.f;
+    for (int c = tid; c < hidden; c += 1024) m = fmaxf(m, fabsf(hrow[c] * inv));
+    m = wave_max(m);
+    __shared__ float redm[16];
+    __syncthreads();   // every wave is past its read of red[]
+    if ((tid & 63) == 0) redm[tid >> 6] = m;
+    __syncthreads();
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, redm[i]);
+    const int e = fp8_exponent(amax);
+    for (int c = tid; c < hidden / 16; c += 1024) {
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = ldexpf(hrow[c * 16 + i] * inv, -e);
+      *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(out) + fp8_blocked_off(row, c, hidden)) = e4m3_pack16(v);
+    }
+    if (tid == 0) a_scale[row] = ldexpf(1.0f, e);
+    return;
+  }
   for (int c = tid; c < hidden; c += 1024) {
     const float y = hrow[c] * inv;
     const int64_t idx = int64_t(row) * hidden + c;
@@ -617,9 +938,9 @@ __global__ __launch_bounds__(1024) void norm_kernel(const float *part, int split
 }
 
 void launch_norm(const float *part, int splits, int64_t split_stride, int rows, int hidden, float eps, int mode,
-                 void *out, int64_t lo_off, hipStream_t s) {
+                 void *out, int64_t lo_off, float *a_scale, hipStream_t s) {
   hipLaunchKernelGGL(norm_kernel, dim3(rows), dim3(1024), size_t(hidden) * 4, s, part, splits, split_stride, hidden,
-                     eps, mode, out, lo_off);
+                     eps, mode, out, lo_off, a_scale);
 }
 
 

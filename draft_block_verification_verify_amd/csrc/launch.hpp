@@ -11,7 +11,14 @@ namespace sv {
 // Formats of the projections' small (activation) operand: ACT_SPLIT = fp16
 // hi plane + fp16 lo plane (hi + lo = value to ~22 bits), ACT_F16, ACT_F32,
 // ACT_F16_BLOCKED = fp16 in the blocked layout below.
-enum ActMode : int { ACT_SPLIT = 0, ACT_F16 = 1, ACT_F32 = 2, ACT_F16_BLOCKED = 3 };
+enum ActMode : int { ACT_SPLIT = 0, ACT_F16 = 1, ACT_F32 = 2, ACT_F16_BLOCKED = 3, ACT_FP8_BLOCKED = 4 };
+
+// FP8 (OCP e4m3) operands of the FP8 LM head: each row of W and of the
+// activations is stored as e4m3 codes of value / 2^e, 2^e the smallest
+// power of two with max |row| <= 448 * 2^e, in a blocked layout like the fp16
+// one with K steps of 64 (64 bytes per row): blocks [rows / 256][K / 64] of
+// 256 x 64 bytes, 16-byte chunk q of row R at byte R * 64 + ((q ^ ((R >> 1) &
+// 3)) << 4).  The scales 2^e are kept per row as floats.
 
 // Blocked fp16 layout of a [M, K] operand of the tiled LM-head launch: rows
 // padded to a multiple of 256; blocks [M / 256][K / 32], each 256 rows x 64
@@ -73,6 +80,9 @@ struct GemmArgs {
   float *t_max, *t_sum;
   int32_t *t_arg;
   int n_tiles;
+  // FP8 LM head: e4m3 operands in the blocked layout and their row scales
+  const uint8_t *W8, *act8;
+  const float *w_scale, *a_scale;
 };
 
 // ---- attention ----
@@ -94,9 +104,17 @@ void launch_gemm_f32(const float *act, int rows, const float *W, int N, int K, f
 void launch_stats_from_logits(const float *logits, int rows, int V, int tile, float *t_max, float *t_sum,
                               int32_t *t_arg, int n_tiles, hipStream_t s);
 // Writes the normalised rows in `mode` (ACT_SPLIT: fp16 hi plane at out, lo
-// plane at out + lo_off; ACT_F16; ACT_F32; ACT_F16_BLOCKED).
+// plane at out + lo_off; ACT_F16; ACT_F32; ACT_F16_BLOCKED; ACT_FP8_BLOCKED,
+// with each row's scale at a_scale[row]).
 void launch_norm(const float *part, int splits, int64_t split_stride, int rows, int hidden, float eps, int mode,
-                 void *out, int64_t lo_off, hipStream_t s);
+                 void *out, int64_t lo_off, float *a_scale, hipStream_t s);
+// FP8 LM head: logits and tile statistics like the stats launch, from g.W8,
+// g.act8, g.w_scale, g.a_scale (any row count).
+void launch_gemm_fp8(const GemmArgs &g, hipStream_t s);
+// bf16 [rows, K] row-major -> e4m3 blocked layout (blocked_elems(rows, K)
+// bytes, K % 64 == 0) and scale[] (rows padded to 256; padding rows: codes 0,
+// scale 1).
+void launch_quant_fp8_blocked(const uint16_t *src, uint8_t *dst, float *scale, int rows, int K, hipStream_t s);
 
 // bf16 -> fp16 copy of n values (n % 8 == 0); adds the count of values
 // outside the fp16 range to *bad (device int).

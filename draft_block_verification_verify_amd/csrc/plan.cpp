@@ -50,6 +50,14 @@ int check_dims(const Dims &dm, std::string *err) {
     *err = cat("max_tree_rows ", dm.max_tree_rows, " must be in [1, ", kMaxTreeRows, "]");
     return P_INVALID;
   }
+  if (dm.weight_format != 0 && dm.weight_format != 1) {
+    *err = cat("weight_format ", dm.weight_format, " is neither SV_WEIGHTS_NATIVE (0) nor SV_WEIGHTS_FP8 (1)");
+    return P_INVALID;
+  }
+  if (dm.weight_format == 1 && dm.dtype != 1) {
+    *err = "SV_WEIGHTS_FP8 takes bf16 models";
+    return P_UNSUPPORTED;
+  }
   if (dm.max_roots > dm.max_rows) {
     *err = "max_roots exceeds max_rows";
     return P_INVALID;

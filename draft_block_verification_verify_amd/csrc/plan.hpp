@@ -18,6 +18,7 @@ constexpr int kMaxSplits = 1024;   // most key-range items per (tree, KV head, q
 struct Dims {
   int32_t Hq, Hkv, d, hidden, vocab, dtype;
   int32_t max_rows, max_roots, max_tree_rows, max_pos;
+  int32_t weight_format = 0;   // 0 native, 1 FP8 LM head (bf16 only)
 };
 
 // Keys per attention tile for head dimension d: one tile of K (or V) is

@@ -12,10 +12,11 @@ from .workloads import Config, Inputs
 
 
 def sv_config(cfg: Config, *, max_rows: int, max_roots: int, max_tree_rows: int = 64,
-              max_pos: int = 1 << 20) -> B.SvConfig:
+              max_pos: int = 1 << 20, fp8: bool = False) -> B.SvConfig:
     return B.SvConfig(cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.hidden, cfg.vocab,
                       B.SV_BF16 if cfg.dtype == "bf16" else B.SV_F32, cfg.rope_base, cfg.norm_eps,
-                      max_rows, max_roots, max_tree_rows, max_pos)
+                      max_rows, max_roots, max_tree_rows, max_pos,
+                      B.SV_WEIGHTS_FP8 if fp8 else B.SV_WEIGHTS_NATIVE)
 
 
 def to_device(x: np.ndarray | None, dtype: str, device):
@@ -33,7 +34,7 @@ class DeviceCase:
 
     def __init__(self, inp: Inputs, device="cuda:0", *, with_logits: bool = False, verifier=None,
                  weights=None, max_rows: int | None = None, max_roots: int | None = None,
-                 uniforms=None, max_pos: int | None = None, kv=None):
+                 uniforms=None, max_pos: int | None = None, kv=None, fp8: bool = False):
         import torch
         self.inp = inp
         cfg, st = inp.cfg, inp.st
@@ -55,7 +56,7 @@ class DeviceCase:
         if verifier is None:
             verifier = B.Verifier(sv_config(cfg, max_rows=max_rows or st.n_rows,
                                             max_roots=max_roots or st.n_roots,
-                                            max_pos=max_pos or int(st.pos.max()) + 1),
+                                            max_pos=max_pos or int(st.pos.max()) + 1, fp8=fp8),
                                   self.w_o, self.w_lm)
         self.ver = verifier
         self.outs = verifier.alloc_outputs(st.n_rows, st.n_roots, self.device, with_logits)

@@ -62,6 +62,17 @@ typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
  * alpha = 1 - D_TV (VESSL part 2, DSpark section), which this rule has. */
 typedef enum sv_mode { SV_MODE_GREEDY = 0, SV_MODE_SAMPLE = 1 } sv_mode;
 
+/* Number format of the LM head.  SV_WEIGHTS_NATIVE: cfg->dtype (bf16 weights
+ * run as exact fp16 copies, fp32 as given).  SV_WEIGHTS_FP8 (bf16 models
+ * only): W8A8 in OCP e4m3, as the pages' fastest serving runs the target in
+ * FP8 (sionic.ai "Solar Open2 250B DSpark", section 5).  Each LM-head row n
+ * and each normalised hidden row t is divided by a power of two, s_n = 2^e
+ * with e the smallest integer such that max |row| <= 448 * 2^e (1 for a zero
+ * row), and rounded to the nearest e4m3 value (ties to even); logits[t, n] =
+ * a_t s_n sum_k q_h[t, k] q_w[n, k], accumulated in fp32.  W_o stays in the
+ * native format. */
+typedef enum sv_weights { SV_WEIGHTS_NATIVE = 0, SV_WEIGHTS_FP8 = 1 } sv_weights;
+
 /* Model shape and capacities, fixed for the handle's lifetime. */
 typedef struct sv_config {
   int32_t n_q_heads;     /* Hq; a multiple of n_kv_heads                       */
@@ -76,6 +87,7 @@ typedef struct sv_config {
   int32_t max_roots;     /* most trees in one run                             */
   int32_t max_tree_rows; /* most rows in one tree, <= 64                      */
   int32_t max_pos;       /* every semantic position must be < max_pos         */
+  int32_t weight_format; /* sv_weights of the LM head; 0 when zero-initialised */
 } sv_config;
 
 typedef struct sv_handle sv_handle;
@@ -124,8 +136,9 @@ typedef struct sv_outputs {
  * w_lm is DEVICE [vocab, hidden], both row-major in cfg->dtype.  For SV_BF16
  * the handle converts them once into fp16 copies it owns (exact for bf16
  * values of magnitude up to 65504; larger weights fail with
- * SV_ERR_UNSUPPORTED) and the caller's buffers are not used afterwards; for
- * SV_F32 they are borrowed for the handle's lifetime.  Allocates the handle's
+ * SV_ERR_UNSUPPORTED), or with SV_WEIGHTS_FP8 W_lm into e4m3 codes and row
+ * scales, and the caller's buffers are not used afterwards; for SV_F32 they
+ * are borrowed for the handle's lifetime.  Allocates the handle's
  * device scratch (sized from the capacities) and pinned host staging;
  * synchronises the device.  Fails with SV_ERR_UNSUPPORTED unless the device
  * is gfx950. */

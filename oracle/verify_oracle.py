@@ -362,15 +362,33 @@ def pow2_scale(amax: float) -> float:
     return 2.0 ** e
 
 
-def lm_head_fp8(cfg, w_lm, hs: np.ndarray, chunk: int = 8192) -> np.ndarray:
-    """Step 11: logits [m, V] of the W8A8 e4m3 LM head."""
-    a = np.array([pow2_scale(float(np.abs(h).max())) for h in hs])
-    qh = np.stack([e4m3(h / s) for h, s in zip(hs, a)]) if len(hs) else hs
+def pow2_scales(amax) -> np.ndarray:
+    """pow2_scale of each entry (vectorised: the same smallest power of two)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    pos = amax > 0
+    e = np.ceil(np.log2(np.where(pos, amax, 448.0) / 448.0))
+    e = np.where(amax > 448.0 * np.exp2(e), e + 1, e)
+    e = np.where(amax <= 448.0 * np.exp2(e - 1), e - 1, e)
+    return np.where(pos, np.exp2(e), 1.0)
+
+
+def lm_head_fp8(cfg, w_lm, hs: np.ndarray, chunk: int = 8192, scales=None) -> np.ndarray:
+    """Step 11: logits [m, V] of the W8A8 e4m3 LM head.  `scales` forces the
+    hidden rows' scales (the other valid outcome when a row's largest value
+    sits on a scale boundary)."""
+    a = pow2_scales(np.abs(hs).max(axis=1)) if len(hs) else np.zeros(0)
+    if scales is not None:
+        # a forced scale may be the next lower power of two, where the row's
+        # largest values sit just past 448: they are held at +-448
+        a = np.asarray(scales, dtype=np.float64)
+        qh = e4m3(np.clip(hs / a[:, None], -448.0, 448.0))
+    else:
+        qh = e4m3(hs / a[:, None]) if len(hs) else hs
     V = w_lm.shape[0]
     out = np.empty((hs.shape[0], V))
     for lo in range(0, V, chunk):
         w = decode(w_lm[lo:lo + chunk], cfg["dtype"])
-        sw = np.array([pow2_scale(float(np.abs(r).max())) for r in w])
+        sw = pow2_scales(np.abs(w).max(axis=1))
         qw = e4m3(w / sw[:, None])
         out[:, lo:lo + chunk] = (qh @ qw.T) * a[:, None] * sw[None, :]
     return out

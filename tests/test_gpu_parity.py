@@ -60,11 +60,13 @@ MINIS = {
 }
 
 
-def run_case(cfg, seed, *, plant=True, with_logits=True, drafter=None, greedy_all=False):
+def run_case(cfg, seed, *, plant=True, with_logits=True, drafter=None, greedy_all=False, fp8=False):
     from draft_block_verification_verify_amd.runner import DeviceCase
-    _say(f"[case] {cfg.name} seed={seed} plant={plant} drafter={drafter}")
+    _say(f"[case] {cfg.name} seed={seed} plant={plant} drafter={drafter} fp8={fp8}")
     inp = W.make_inputs(cfg, seed)
     cd, idict = O.cfg_dict(cfg), O.inp_dict(inp)
+    if fp8:
+        cd["weight_format"] = "fp8"
     if cfg.kind == "tree":
         W.sample_tree_drafts(inp)
     elif plant:
@@ -86,7 +88,7 @@ def run_case(cfg, seed, *, plant=True, with_logits=True, drafter=None, greedy_al
         q = q.astype(np.float32)
         inp.drafter_logits = W.f32_to_bf16_bits(q) if cfg.dtype == "bf16" else q
     ref = O.verify(cd, O.inp_dict(inp), keep_logits=True)
-    dc = DeviceCase(inp, with_logits=with_logits)
+    dc = DeviceCase(inp, with_logits=with_logits, fp8=fp8)
     dc.run()
     gpu = dc.results()
     dc.close()
@@ -412,3 +414,55 @@ def test_parity_ragged_gamma(seed):
     P.check_self_consistency(st.parent, inp.draft_ids, gpu)
     P.compare(ref, gpu, st.parent, inp.draft_ids, logits_ref=ref["logits"], logits_gpu=gpu["logits"], report=rep)
     _record(f"ragged/seed{seed}", rep)
+
+
+# ----------------------------------------------------------------------------
+# FP8 (e4m3, W8A8) LM head against the oracle's FP8 head
+# ----------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("name", ["c2m", "c3m", "c4m", "c5m", "c5s"])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_parity_fp8(name, seed):
+    cfg = MINIS[name]
+    inp, ref, gpu = run_case(cfg, seed, fp8=True)
+    rep = {}
+    P.check_self_consistency(inp.st.parent, inp.draft_ids, gpu)
+    cd = dict(O.cfg_dict(cfg), weight_format="fp8")
+    rows = list(range(inp.st.n_rows))
+    alt = P.fp8_alternatives(cd, O.inp_dict(inp), rows)
+    bound = P.fp8_bounds(cd, O.inp_dict(inp), rows)
+    P.compare(ref, gpu, inp.st.parent, inp.draft_ids, logits_ref=ref["logits"], logits_gpu=gpu["logits"], report=rep,
+              tol=P.FP8_TOL, alt=alt, bound=bound)
+    rep["flip_bound_max_rel"] = max(float((bound[i] / np.sqrt(np.mean(ref["logits"][i] ** 2))).max()) for i in rows)
+    _record(f"{name}/fp8/seed{seed}", rep)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg_id", [5])
+def test_parity_fp8_full_size_sampled(cfg_id):
+    from draft_block_verification_verify_amd.runner import DeviceCase
+    cfg = W.CONFIGS[cfg_id]
+    _say(f"[full fp8] generating {cfg.name}")
+    inp = W.make_inputs(cfg, 0)
+    st = inp.st
+    R = st.n_roots
+    trees = sorted({0, R - 1, R // 2}) if R > 1 else [0]
+    cd = dict(O.cfg_dict(cfg), weight_format="fp8")
+    _say(f"[full fp8] oracle on trees {trees}")
+    g = O.target_greedy(cd, O.inp_dict(inp), trees=trees)
+    W.plant_chain_drafts(inp, np.where(g < 0, 0, g))
+    ref = O.verify(cd, O.inp_dict(inp), trees=trees, keep_logits=True)
+    _say("[full fp8] gpu run")
+    dc = DeviceCase(inp, with_logits=True, fp8=True)
+    dc.run()
+    gpu = dc.results()
+    dc.close()
+    P.check_self_consistency(st.parent, inp.draft_ids, gpu)
+    rows = [int(i) for i in ref["rows"]]
+    rep = {}
+    alt = P.fp8_alternatives(cd, O.inp_dict(inp), rows)
+    bound = P.fp8_bounds(cd, O.inp_dict(inp), rows)
+    P.compare(ref, gpu, st.parent, inp.draft_ids, rows=rows, logits_ref=ref["logits"], logits_gpu=gpu["logits"],
+              report=rep, tol=P.FP8_TOL, alt=alt, bound=bound)
+    _record(f"{cfg.name}/fp8/full-sampled", rep)

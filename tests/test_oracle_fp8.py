@@ -54,6 +54,12 @@ def test_pow2_scale_definition():
         assert s == 2.0 ** e and amax <= 448 * s and amax > 448 * s / 2
 
 
+def test_vector_scales_equal_the_definition():
+    r = np.random.default_rng(6)
+    amax = np.concatenate([[0.0, 448.0, 448.0 * 2.0 ** -3, 896.0 + 1e-9], np.exp(r.uniform(-30, 30, 500))])
+    np.testing.assert_array_equal(O.pow2_scales(amax), [O.pow2_scale(float(x)) for x in amax])
+
+
 def test_representable_inputs_are_lossless():
     # every weight row and hidden row is a power of two times values e4m3
     # holds exactly at that scale: the FP8 head equals the exact product
