@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 METRIC = "verify rows/s (attn+LM-head+accept) γ=7, 27B shape; step ms; % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 COUNTERS = os.path.join(ROOT, "profiles", "lm_head_counters.json")
 GEMM_SRC = [os.path.join(ROOT, "draft_block_verification_verify_amd", "csrc", f)
             for f in ("k_gemm.hip", "k_dma.hpp", "k_common.hpp")]
@@ -59,9 +60,10 @@ def counters_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(inp, min_seconds: float = 10.0) -> dict:
+def cpu_baseline(inp, min_seconds: float = 10.0, fp8: bool = False) -> dict:
     """The fp64 oracle, as it stands, on whole sequences (trees) of the same
-    workload, one after another until at least `min_seconds` of CPU work."""
+    workload, one after another until at least `min_seconds` of CPU work
+    (`fp8`: with the FP8 LM head)."""
     from oracle import verify_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -73,6 +75,8 @@ def cpu_baseline(inp, min_seconds: float = 10.0) -> dict:
     d["draft_ids"] = rng.integers(0, inp.cfg.vocab, inp.st.n_rows).astype(np.int32)
     roots = np.nonzero(inp.st.parent < 0)[0].tolist() + [inp.st.n_rows]
     cfg = O.cfg_dict(inp.cfg)
+    if fp8:
+        cfg["weight_format"] = "fp8"
     rows, done, dt = 0, 0, 0.0
     t0 = time.perf_counter()
     while done < inp.st.n_roots and dt < min_seconds:
@@ -334,6 +338,8 @@ def main() -> int:
     ap.add_argument("--sample", action="store_true",
                     help="T = 1 stochastic verification (drafts drawn from the drafter, seeded uniforms)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--fp8", action="store_true",
+                    help="FP8 (e4m3, W8A8) LM head (bf16 workloads)")
     ap.add_argument("--schedule", action="store_true",
                     help="conc32: measure the rows -> ms curve, then compare fixed gamma with the verify-budget "
                          "schedule on synthetic per-request confidences")
@@ -367,7 +373,7 @@ def main() -> int:
     st = inp.st
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s: rows {st.n_rows}, trees {st.n_roots}, "
         f"kv tokens {st.kv_tokens}")
-    dc = DeviceCase(inp, with_logits=False)
+    dc = DeviceCase(inp, with_logits=False, fp8=args.fp8)
     torch.cuda.synchronize()
 
     # draft ids: trees use draws from the drafter; chains get a planted
@@ -419,26 +425,27 @@ def main() -> int:
         ok = None
 
     n = st.n_rows
-    sb, sf = A.step_bytes(cfg, st), A.step_flops(cfg, st)
+    sb, sf = A.step_bytes(cfg, st, fp8=args.fp8), A.step_flops(cfg, st)
+    mfma_peak = FP8_PEAK_TFLOPS if args.fp8 else BF16_PEAK_TFLOPS
     lm_ms = lm_live
     lm_bytes = sb["lm_head"]
     lm_flops = sf["lm_head"]
     ai = lm_flops / lm_bytes
-    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     if ai < ridge:
         achieved = lm_bytes / (lm_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
     else:
         achieved = lm_flops / (lm_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / BF16_PEAK_TFLOPS}
-    roof["traffic"] = counters_traffic(cfg.name)
+        roof = {"bound": "mfma", "achieved": achieved, "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": achieved / mfma_peak}
+    roof["traffic"] = None if args.fp8 else counters_traffic(cfg.name)
     roof["kernel"] = "lm_head"
     roof["kernel_ms"] = lm_ms
     roof["algorithmic_bytes"] = lm_bytes
     roof["algorithmic_flops"] = lm_flops
-    roof["mfma_frac"] = lm_flops / (lm_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
+    roof["mfma_frac"] = lm_flops / (lm_ms * 1e-3) / 1e12 / mfma_peak
 
     step_s = ms * 1e-3
     res = {
@@ -452,12 +459,13 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "dtype": ("bf16, LM head e4m3" if args.fp8 else "bf16") if cfg.dtype == "bf16" else "f32",
         "data": "synthetic (seeded; random-init weights of the stated shapes)",
         "config": {"workload": cfg.name, "rows": n, "trees": st.n_roots, "kv_tokens": int(st.kv_tokens),
                    "heads_q_kv": [cfg.n_q_heads, cfg.n_kv_heads], "head_dim": cfg.head_dim,
                    "hidden": cfg.hidden, "vocab": cfg.vocab, "gamma": cfg.gamma, "seed": args.seed,
-                   "acceptance": "T=1 sampling" if args.sample else "greedy"},
+                   "acceptance": "T=1 sampling" if args.sample else "greedy",
+                   "lm_head_format": "fp8 e4m3 (W8A8)" if args.fp8 else "native"},
         "roofline": roof,
         "step": {"algorithmic_bytes": sb["total"], "algorithmic_flops": sf["total"],
                  "device_ms_staged": stages.get("step"), "ms_per_step_staged": ms_staged,
@@ -469,7 +477,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on one sequence)")
-        res["cpu_baseline"] = cpu_baseline(inp)
+        res["cpu_baseline"] = cpu_baseline(inp, fp8=args.fp8)
     else:
         res["cpu_baseline"] = None
     dc.close()

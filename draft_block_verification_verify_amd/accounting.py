@@ -48,8 +48,10 @@ def _tree_depths(parent):
     return depth
 
 
-def step_bytes(cfg, st) -> dict:
-    """Algorithmic HBM bytes of one step, by stage."""
+def step_bytes(cfg, st, fp8: bool = False) -> dict:
+    """Algorithmic HBM bytes of one step, by stage (`fp8`: the LM head reads
+    e4m3 weights, one byte each plus a 4-byte scale per row, and e4m3
+    activations)."""
     e = _elt(cfg.dtype)
     n = st.n_rows
     n_draft = int((np.asarray(st.parent) >= 0).sum())
@@ -57,10 +59,11 @@ def step_bytes(cfg, st) -> dict:
     kv = _visible_prefix_tokens(st) * Hkv * d * e * 2
     rows = n * (Hq + 2 * Hkv) * d * e
     w_o = H * Hq * d * e
-    w_lm = V * H * e
+    w_lm = V * H + V * 4 if fp8 else V * H * e
+    act = n * H * (1 if fp8 else e)
     drafter = n_draft * V * e
     outs = n * 4 * 6 + st.n_roots * 4 * 4
-    return {"attention": kv + rows, "w_o": w_o, "lm_head": w_lm + n * H * e,
+    return {"attention": kv + rows, "w_o": w_o, "lm_head": w_lm + act,
             "drafter": drafter, "outputs": outs,
             "total": kv + rows + w_o + w_lm + drafter + outs}
 

@@ -458,6 +458,7 @@ __device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+template <bool SPARSE>
 __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
   constexpr bool STATS = true;
   constexpr int PER = 4;     // DMA instructions per wave per stage (2 weight + 2 activation)
@@ -487,6 +488,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
   };
   struct Src {
     i32x4 rw, ra;
+    int ao[2];   // activation DMA offsets: rows past the tile's valid rows point out of range (read 0, no traffic)
   };
   auto src_of = [&](int n_tile, int t_tile) {
     const int n0 = n_tile * kTBN, t0 = t_tile * kTBT;
@@ -496,7 +498,9 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
     r.rw = make_rsrc(g.W8 + int64_t(n_tile) * tb, uint32_t(tb));
     r.ra = make_rsrc(g.act8 + int64_t(t_tile) * tb, uint32_t(tb));
     (void)n0;
-    (void)t0;
+    const int live = SPARSE ? min(kTBT, g.rows - t0) : kTBT;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) r.ao[i] = (w * 32 + i * 16 + (lane >> 2) < live) ? off[i] : 0x40000000;
     return r;
   };
   auto issue = [&](const Src &sr, int s) {
@@ -505,7 +509,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16(sr.rw, base + (w * 32 + i * 16) * 64, off[i], soff);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(sr.ra, base + kTBN * 64 + (w * 32 + i * 16) * 64, off[i], soff);
+    for (int i = 0; i < 2; ++i) dma16(sr.ra, base + kTBN * 64 + (w * 32 + i * 16) * 64, sr.ao[i], soff);
   };
 
   int tile = blockIdx.x;
@@ -526,6 +530,9 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
     if (p < nk) issue(cur, p);
 
   for (;;) {
+    // 32-row blocks of this wave that hold rows of the batch
+    const int live_rows = g.rows - t_tile * kTBT;
+    const bool live_t0 = !SPARSE || wt * 64 < live_rows, live_t1 = !SPARSE || wt * 64 + 32 < live_rows;
     f32x16 acc[4][2];
 #pragma unroll
     for (int v = 0; v < 4; ++v)
@@ -544,6 +551,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
         wait_and_barrier<0>();
       if (s + kTST - 1 < nk) issue(cur, s + kTST - 1);
       const uint8_t *base = smem + (s % kTST) * kTSST;
+      if (!live_t0) continue;   // this wave's 64 rows are all padding: DMA and barriers only
       // 32 bytes of the lane's row per operand: chunks 2 kg and 2 kg + 1
       i32x8 af[4], bf[2];
 #pragma unroll
@@ -557,10 +565,15 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
         bf[t] = cat8(lds16(base + kTBN * 64 + R * 64 + (((2 * kg) ^ sw) << 4)),
                      lds16(base + kTBN * 64 + R * 64 + (((2 * kg + 1) ^ sw) << 4)));
       }
+      if (live_t1) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+        for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) acc[v][t] = mfma32_fp8(af[v], bf[t], acc[v][t]);
+          for (int t = 0; t < 2; ++t) acc[v][t] = mfma32_fp8(af[v], bf[t], acc[v][t]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[v][0] = mfma32_fp8(af[v], bf[0], acc[v][0]);
+      }
     }
 
     // epilogue of this tile (vector-memory waits count stores too, so the
@@ -646,7 +659,9 @@ void launch_gemm_fp8(const GemmArgs &g, hipStream_t s) {
   static bool attr = false;
   static int n_cu = 256;
   if (!attr) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_fp8_kernel),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_fp8_kernel<true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(kTiledLds));
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_fp8_kernel<false>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, int(kTiledLds));
     int dev = 0;
     if (hipGetDevice(&dev) == hipSuccess) {
@@ -658,7 +673,12 @@ void launch_gemm_fp8(const GemmArgs &g, hipStream_t s) {
   const int n_ntiles = (g.N + kTBN - 1) / kTBN, n_ttiles = (g.rows + kTBT - 1) / kTBT;
   const int tiles = ((n_ntiles + 7) / 8) * 8 * n_ttiles;
   const int grid_x = std::min(tiles, std::max(16, n_cu / 16 * 16));
-  hipLaunchKernelGGL(gemm_fp8_kernel, dim3(grid_x), dim3(512), kTiledLds, s, g);
+  // small batches: padding rows are neither fetched nor multiplied (the
+  // per-tile checks cost a few percent when every row is live)
+  if (g.rows < 128)
+    hipLaunchKernelGGL((gemm_fp8_kernel<true>), dim3(grid_x), dim3(512), kTiledLds, s, g);
+  else
+    hipLaunchKernelGGL((gemm_fp8_kernel<false>), dim3(grid_x), dim3(512), kTiledLds, s, g);
 }
 
 int lm_tile_width(int rows) { return rows <= 64 ? 4 * 2 * 32 : kTBN; }
