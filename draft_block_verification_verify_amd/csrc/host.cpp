@@ -42,6 +42,7 @@ struct sv_handle {
   // weights the kernels read: for bf16, fp16 copies (W_o row-major, W_lm in
   // the blocked layout of the LM-head launches)
   const void *w_o = nullptr, *w_lm = nullptr;
+  const void *w_o_blk = nullptr;   // bf16, max_rows > 64: W_o in the blocked layout of the tiled launch
   // FP8 LM head: e4m3 W_lm (blocked) and its row scales; per-run row scales
   // of the activations
   uint8_t *w_lm8 = nullptr;
@@ -191,7 +192,8 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
     A(&h->part_o, size_t(h->slot_cap * D * 4));
     A(&h->part_ml, size_t(h->slot_cap * 2 * 4));
   }
-  A(&h->o_act, size_t(R * Hq * D * 4));       // fp16 hi + lo planes, fp16, or fp32
+  // attention output: fp16 hi + lo planes, blocked fp16 (rows padded to 256), or fp32
+  A(&h->o_act, std::max<size_t>(size_t(R * Hq * D * 4), size_t(sv::blocked_elems(R, Hq * D) * 2)));
   A(&h->h_part, h->h_part_floats * 4);
   // normalised rows: fp16 hi + lo planes (<= 64 rows) or the blocked fp16
   // layout of the tiled LM head (rows padded to 256)
@@ -208,9 +210,11 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
   if (dm.dtype == SV_BF16) {
     // the projections run on fp16 MFMA: keep fp16 copies of the weights
     // (W_o row-major, W_lm in the blocked layout)
-    uint16_t *wo16 = nullptr, *wlm16 = nullptr;
+    uint16_t *wo16 = nullptr, *wlm16 = nullptr, *wo_blk = nullptr;
     const bool fp8 = dm.weight_format == SV_WEIGHTS_FP8;
+    const bool tiled = dm.max_rows > 64;
     A(&wo16, size_t(H * Hq * D * 2));
+    if (tiled) A(&wo_blk, size_t(sv::blocked_elems(H, Hq * D) * 2));
     if (fp8) {
       A(&h->w_lm8, size_t(sv::blocked_elems(V, H)));
       A(&h->w_scale, size_t(ceil_div(V, 256) * 256 * 4));
@@ -226,6 +230,9 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
       if (e == hipSuccess) e = hipMemsetAsync(h->hn, 0, std::max<size_t>(size_t(R * H * 4), size_t(sv::blocked_elems(R, H) * 2)), nullptr);
       if (e == hipSuccess) {
         sv::launch_bf16_to_f16(static_cast<const uint16_t *>(w_o), wo16, H * Hq * D, h->d_bad, nullptr);
+        if (tiled)
+          sv::launch_bf16_to_f16_blocked(static_cast<const uint16_t *>(w_o), wo_blk, int(H), int(Hq * D), h->d_bad,
+                                         nullptr);
         if (fp8)
           sv::launch_quant_fp8_blocked(static_cast<const uint16_t *>(w_lm), h->w_lm8, h->w_scale, int(V), int(H),
                                        nullptr);
@@ -245,6 +252,7 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
         return fail(SV_ERR_UNSUPPORTED, std::to_string(bad) + " weight values exceed the fp16 range (|w| > 65504)");
       }
       h->w_o = wo16;
+      h->w_o_blk = wo_blk;
       h->w_lm = wlm16;
     }
   }
@@ -479,8 +487,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   int k_split = 0;
   const int splits = bf16 ? sv::gemm_splits(n, int(H), int(Hq * D), h->n_cu, &k_split) : 1;
   // activation format of the projections: fp16 hi + lo planes for the
-  // skinny launch, fp16 for the tiled one (blocked layout for the LM head)
-  const int act_mode = n <= 64 ? sv::ACT_SPLIT : sv::ACT_F16;
+  // skinny launch, blocked fp16 for the tiled one (e4m3 for the FP8 LM head)
   const int lm_act_mode = fp8 ? sv::ACT_FP8_BLOCKED : n <= 64 ? sv::ACT_SPLIT : sv::ACT_F16_BLOCKED;
   const int64_t q_lo = int64_t(dm.max_rows) * Hq * D;   // lo planes start one capacity further
   const int64_t o_lo = int64_t(dm.max_rows) * Hq * D;
@@ -530,7 +537,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     ma.Hq = int(Hq);
     ma.Hkv = int(Hkv);
     ma.qg_max = plan.qg_max;
-    ma.mode = act_mode;
+    ma.mode = n <= 64 ? sv::ACT_SPLIT : sv::ACT_F16_BLOCKED;
     ma.lo_off = o_lo;
     ma.out = static_cast<uint16_t *>(h->o_act);
     begin("attn_merge");
@@ -540,7 +547,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     g.act = static_cast<const uint16_t *>(h->o_act);
     g.act_lo = g.act + o_lo;
     g.rows = n;
-    g.W = static_cast<const uint16_t *>(h->w_o);
+    g.W = static_cast<const uint16_t *>(n <= 64 ? h->w_o : h->w_o_blk);
     g.N = int(H);
     g.K = int(Hq * D);
     g.k_split = k_split;
@@ -548,7 +555,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     g.ldo = H;
     g.split_stride = int64_t(n) * H;
     begin("w_o");
-    sv::launch_gemm_bf16(g, false, splits, stream);
+    sv::launch_gemm_bf16(g, false, splits, stream, n > 64);
     end();
     begin("final_norm");
     sv::launch_norm(h->h_part, splits, int64_t(n) * H, n, int(H), h->cfg.norm_eps, lm_act_mode, h->hn, h_lo,

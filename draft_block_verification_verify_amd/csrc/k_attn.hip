@@ -455,6 +455,11 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(MergeArgs a) {
     split_h(val, hi, lo);
     a.out[idx] = hi;
     a.out[a.lo_off + idx] = lo;
+  } else if (a.mode == ACT_F16_BLOCKED) {
+    // blocked fp16 layout of the tiled W_o launch (K = Hq * D)
+    const int k = h * D + c, R = i & 255, q = (k >> 3) & 3;
+    const int64_t b = (int64_t(i >> 8) * ((a.Hq * D) >> 5) + (k >> 5)) * 8192;
+    a.out[b + R * 32 + ((q ^ ((R >> 1) & 3)) << 3) + (k & 7)] = f2h(val);
   } else {
     a.out[idx] = f2h(val);
   }

@@ -716,7 +716,7 @@ static void launch_skinny(const GemmArgs &g, int splits, hipStream_t s) {
   hipLaunchKernelGGL((gemm_skinny_kernel<TB, WV, ST, BL>), grid, dim3(256), lds, s, g);
 }
 
-void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s) {
+void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s, bool blocked) {
   if (g.rows <= 64) {
     // WV = 2 for the LM head (256 weight rows per workgroup), 1 for split-K W_o
     if (g.rows <= 32) {
@@ -732,6 +732,8 @@ void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s) 
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_tiled_kernel<true, true>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, int(kTiledLds));
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_tiled_kernel<false, false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(kTiledLds));
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_tiled_kernel<false, true>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, int(kTiledLds));
     int dev = 0;
     if (hipGetDevice(&dev) == hipSuccess) {
@@ -749,6 +751,8 @@ void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s) 
   // the LM head (stats) reads both operands in the blocked layout
   if (stats)
     hipLaunchKernelGGL((gemm_tiled_kernel<true, true>), grid, dim3(512), kTiledLds, s, g);
+  else if (blocked)
+    hipLaunchKernelGGL((gemm_tiled_kernel<false, true>), grid, dim3(512), kTiledLds, s, g);
   else
     hipLaunchKernelGGL((gemm_tiled_kernel<false, false>), grid, dim3(512), kTiledLds, s, g);
 }

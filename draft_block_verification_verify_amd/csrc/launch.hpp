@@ -47,7 +47,7 @@ struct MergeArgs {
   const AttnItem *items;
   const int32_t *group_first, *group_count, *row_tree, *row_local;
   int Hq, Hkv, qg_max;
-  int mode;                        // ACT_SPLIT: fp16 hi plane at out, lo at out + lo_off; ACT_F16
+  int mode;                        // ACT_SPLIT: fp16 hi plane at out, lo at out + lo_off; ACT_F16; ACT_F16_BLOCKED
   int64_t lo_off;
   uint16_t *out;                   // [n, Hq*D]
 };
@@ -99,7 +99,9 @@ void launch_attn_f32(const AttnF32Args &a, int n_rows, hipStream_t s);
 int lm_tile_width(int rows);
 // Split-K factor (and K per split, a multiple of 64) of a projection launch.
 int gemm_splits(int rows, int N, int K, int n_cu, int *k_split);
-void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s);
+// `blocked`: the tiled launch reads W and act in the blocked layout (always
+// for stats, the LM head)
+void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s, bool blocked = false);
 void launch_gemm_f32(const float *act, int rows, const float *W, int N, int K, float *out, hipStream_t s);
 void launch_stats_from_logits(const float *logits, int rows, int V, int tile, float *t_max, float *t_sum,
                               int32_t *t_arg, int n_tiles, hipStream_t s);
