@@ -71,25 +71,45 @@ __device__ __forceinline__ float load1(const void *base, int bf16, int64_t idx) 
 
 // ----------------------------------------------------------------------------
 
+constexpr int kDrafterChunk = 8192;   // the host's drafter-stats chunk (vocabulary values per workgroup)
+
 __global__ __launch_bounds__(256) void drafter_partial_kernel(VocabArgs a) {
   const int c = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
   const int lo = c * a.dchunk, hi = min(a.V, lo + a.dchunk);
   const int64_t row = int64_t(t) * a.V;
   const bool vec = (a.V % 8) == 0;
-  // pass 1: max; pass 2: sum exp (the chunk is re-read from L2)
-  float m = -INFINITY;
-  if (vec) {
+  float m = -INFINITY, s = 0.f;
+  if (vec && a.dchunk == kDrafterChunk) {
+    // the thread's kDrafterChunk / 2048 groups of 8, all loaded before use
+    // (one pass over HBM); values past the vocabulary read as -inf
+    constexpr int NG = kDrafterChunk / 2048;
+    float x[NG][8];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int u = lo + tid * 8 + g * 2048;
+      if (u < hi) {
+        load8(a.drafter, a.drafter_bf16, row + u, x[g]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[g][e] = -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, x[g][e]);
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += __expf(x[g][e] - m);   // exp(-inf) = 0
+  } else if (vec) {
+    // pass 1: max; pass 2: sum exp (the chunk is re-read from L2)
     for (int u = lo + tid * 8; u < hi; u += 256 * 8) {
       float x[8];
       load8(a.drafter, a.drafter_bf16, row + u, x);
 #pragma unroll
       for (int e = 0; e < 8; ++e) m = fmaxf(m, x[e]);
     }
-  } else {
-    for (int u = lo + tid; u < hi; u += 256) m = fmaxf(m, load1(a.drafter, a.drafter_bf16, row + u));
-  }
-  float s = 0.f;
-  if (vec) {
     for (int u = lo + tid * 8; u < hi; u += 256 * 8) {
       float x[8];
       load8(a.drafter, a.drafter_bf16, row + u, x);
@@ -97,6 +117,7 @@ __global__ __launch_bounds__(256) void drafter_partial_kernel(VocabArgs a) {
       for (int e = 0; e < 8; ++e) s += __expf(x[e] - m);
     }
   } else {
+    for (int u = lo + tid; u < hi; u += 256) m = fmaxf(m, load1(a.drafter, a.drafter_bf16, row + u));
     for (int u = lo + tid; u < hi; u += 256) s += __expf(load1(a.drafter, a.drafter_bf16, row + u) - m);
   }
   if (m == -INFINITY) s = 0.f;
