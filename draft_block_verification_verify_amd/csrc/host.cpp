@@ -1,5 +1,7 @@
 // C ABI of the verify step (include/spec_verify.h): handle lifetime, scratch,
-// metadata upload and the launch sequence of one run.
+// weight preparation (fp16 or e4m3 copies), metadata upload and the launch
+// sequence of one run, the commit of a run's accepted paths, and the
+// host-only verify-budget schedule.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

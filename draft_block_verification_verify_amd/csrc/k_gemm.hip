@@ -1,15 +1,18 @@
 // W_o and LM-head projections for the verify step (gfx950).
 //
-// Both are out[rows, N] = act[rows, K] . W[N, K]^T with a large, row-major
-// weight streamed once from HBM and a small activation block (the verify
-// rows).  The LM head spans the whole vocabulary (the full-vocab projection
-// is what makes a one-layer predictor expensive: VESSL "Speculative Decoding
-// Part 2", MTP section), so its epilogue also reduces every N tile to
-// (max, sum exp, argmax) per row, ready for the vocab-wide softmax.
+// Both are out[rows, N] = act[rows, K] . W[N, K]^T with a large weight
+// streamed once from HBM and a small activation block (the verify rows).
+// The LM head spans the whole vocabulary (the full-vocab projection is what
+// makes a one-layer predictor expensive: VESSL "Speculative Decoding Part 2",
+// MTP section), so its epilogue also reduces every N tile to (max, sum exp,
+// argmax) per row, ready for the vocab-wide softmax.
 //
 // The weights are the handle's fp16 copies (converted once from bf16 at
 // handle creation, exact for the weights accepted there); both operands of
-// every MFMA are fp16 with fp32 accumulation.
+// every fp16 MFMA are fp16 with fp32 accumulation.  The LM head's weights,
+// and W_o's for runs of more than 64 rows, are kept in a blocked layout (the
+// LDS image of one DMA stage, block after block; see launch.hpp) so that
+// every DMA instruction reads 1 KB of consecutive bytes.
 //
 // Skinny launch (rows <= 64, HBM-bound): weight rows and the activation
 // stream into a 3-stage LDS ring by direct global -> LDS loads; the
@@ -18,7 +21,11 @@
 //
 // Tiled launch (rows > 64, near the compute ridge): persistent, 256 x 256
 // output tiles, a 4-stage DMA ring, 32x32x16 fp16 MFMA; the activation is
-// plain fp16 (11 significant bits).
+// plain fp16 (11 significant bits), blocked like the weights.
+//
+// FP8 LM head (weight format SV_WEIGHTS_FP8): e4m3 codes of weights and
+// activations with power-of-two row scales, the tiled launch's structure on
+// 32x32x64 e4m3 MFMAs, the scales applied in the epilogue.
 #include <algorithm>
 #include <type_traits>
 

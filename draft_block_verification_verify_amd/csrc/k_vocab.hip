@@ -12,6 +12,9 @@
 //                   sum, and the greedy longest-matching walk with the bonus
 //                   token (sionic.ai Solar Open2 page, section 1; SpecOPD
 //                   summary, "premises and limits").
+//  swalk / residual_partial / sample
+//                   T = 1 stochastic verification of chains: the accept test
+//                   per draft and the inverse-CDF draw of the bonus token.
 // Every reduction runs in a fixed order, so repeated runs are bit-identical.
 #include "k_common.hpp"
 #include "launch.hpp"
