@@ -165,7 +165,7 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
   h->w_lm = w_lm;
   h->device = dev;
   h->n_cu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
-  h->target_items = 8 * h->n_cu;
+  h->target_items = 2 * h->n_cu;   // attention runs: one per resident four-wave workgroup
   h->elt = dm.dtype == SV_BF16 ? 2 : 4;
 
   const int64_t R = dm.max_rows, Hq = dm.Hq, Hkv = dm.Hkv, D = dm.d, H = dm.hidden, V = dm.vocab;
@@ -380,7 +380,8 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
       !out->row_lse || !out->overlap || !out->survival)
     return fail(SV_ERR_INVALID_ARG, "every output except logits must be a non-null device pointer");
   const sv::MetaLayout lay =
-      sv::meta_layout(plan.n, plan.R, plan.n_draft, int(plan.items.size()), plan.R * dm.Hkv * plan.qg_max);
+      sv::meta_layout(plan.n, plan.R, plan.n_draft, int(plan.items.size()), int(plan.runs.size()),
+                      plan.R * dm.Hkv * plan.qg_max);
   if (lay.total > h->meta_cap) return fail(SV_ERR_CAPACITY, "metadata exceeds the handle's staging capacity");
 
   const int n = plan.n;
@@ -426,6 +427,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   const int32_t *tree_kv_len = reinterpret_cast<const int32_t *>(m + lay.tree_kv_len);
   const int64_t *tree_kv_off = reinterpret_cast<const int64_t *>(m + lay.tree_kv_off);
   const sv::AttnItem *items = reinterpret_cast<const sv::AttnItem *>(m + lay.items);
+  const sv::AttnRun *runs = reinterpret_cast<const sv::AttnRun *>(m + lay.runs);
   const int32_t *group_first = reinterpret_cast<const int32_t *>(m + lay.group_first);
   const int32_t *group_count = reinterpret_cast<const int32_t *>(m + lay.group_count);
 
@@ -512,10 +514,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     aa.q_rot = static_cast<const uint16_t *>(h->q_rot);
     aa.q_lo_off = q_lo;
     aa.items = items;
-    aa.tree_start = tree_start;
-    aa.tree_rows = tree_rows;
-    aa.tree_kv_len = tree_kv_len;
-    aa.tree_kv_off = tree_kv_off;
+    aa.runs = runs;
     aa.row_anc = row_anc;
     aa.part_o = h->part_o;
     aa.part_ml = h->part_ml;
@@ -526,7 +525,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     int max_nq = 1;
     for (const auto &it : plan.items) max_nq = std::max(max_nq, int(it.nq));
     begin("attention");
-    sv::launch_attn_mfma(aa, int(plan.items.size()), int(D), int(ceil_div(max_nq, 16)), stream);
+    sv::launch_attn_mfma(aa, int(plan.runs.size()), int(D), int(ceil_div(max_nq, 16)), stream);
     end();
     sv::MergeArgs ma{};
     ma.part_o = h->part_o;

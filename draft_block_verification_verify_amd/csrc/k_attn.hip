@@ -4,17 +4,20 @@
 // with RoPE at the rows' semantic positions (onedev.kr SpecOPD summary,
 // "what differs": parent map, semantic positions, ancestor-and-self mask).
 //
-// bf16 path: split-KV flash-decode.  A work item is (tree, KV head, query
-// group, key range); its query vectors are the tree's (row, head-in-group)
-// pairs, so one K/V tile streamed from HBM serves every row and every query
-// head of the GQA group.  K/V tiles reach LDS by DMA in their natural layout,
+// bf16 path: split-KV flash-decode.  A query group is (tree, KV head, up to
+// 128 of the tree's (row, head-in-group) pairs), so one K/V tile streamed
+// from HBM serves every row and every query head of the GQA group.  The
+// tiles of all query groups, one group after another, are cut into runs of
+// equal length, one per workgroup; a work item is the part of one group that
+// one run covers.  K/V tiles reach LDS by DMA in their natural layout,
 // V^T fragments come from transposing LDS reads, S^T = K.Q^T and
-// O^T += V^T.P^T run on 16x16x32 bf16 MFMA, the online softmax is per wavefront in fp32 (log2
-// domain).  The rotated queries and the probabilities are each carried as a
-// bf16 pair hi + lo (two MFMAs per product), so the only bf16 rounding left
-// in the scores is the one of the cached keys themselves.  Each item leaves
-// (max, sum, unnormalised o) per query; a merge kernel combines the items of
-// a query and writes o in the format the W_o projection reads.
+// O^T += V^T.P^T run on 16x16x32 bf16 MFMA, the online softmax is per
+// wavefront in fp32 (log2 domain).  The rotated queries and the
+// probabilities are each carried as a bf16 pair hi + lo (two MFMAs per
+// product), so the only bf16 rounding left in the scores is the one of the
+// cached keys themselves.  Each item leaves (max, sum, unnormalised o) per
+// query; a merge kernel combines the items of a query and writes o in the
+// format the W_o projection reads.
 //
 // fp32 path: one workgroup per (row, query head), plain fp32 arithmetic.
 #include "k_common.hpp"
@@ -94,9 +97,12 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(const T *__restrict__ q,
 // ----------------------------------------------------------------------------
 // bf16 split-KV attention on MFMA
 //
-// A work item walks tiles of KT = 8192 / D keys (16 KB of K plus 16 KB of V)
-// through a 4-stage LDS ring filled by direct global -> LDS DMA, three tiles
-// ahead of the one being used.  A tile holds its keys in natural [key][d]
+// A workgroup walks its run's tiles of KT = 8192 / D keys (16 KB of K plus
+// 16 KB of V), item after item, through an STG-stage LDS ring filled by
+// direct global -> LDS DMA, STG - 1 tiles ahead of the one being used; the
+// DMA side crosses into the next item on its own, and the compute side
+// writes an item's partial records and loads the next item's queries as it
+// finishes the item's last tile.  A tile holds its keys in natural [key][d]
 // layout; 16-B chunk c of tile row r sits at chunk c ^ swz(r), which keeps
 // both the K fragment reads (16 rows, one chunk) and the transposing V reads
 // (4 rows x 32 B per 16 lanes) free of bank conflicts.  Wavefront w owns
@@ -142,6 +148,14 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint8_t *p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// Work-list records through the constant address space: the compiler then
+// reads them with scalar loads (counted apart from the vector-memory loads
+// whose count the DMA ring waits on) and keeps the fields in SGPRs.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T *as_const(const T *p) {
+  return reinterpret_cast<const __attribute__((address_space(4))) T *>(reinterpret_cast<uintptr_t>(p));
+}
+
 // STG: ring stages (tiles in flight = STG - 1); OCC: wavefronts per SIMD the
 // launch is built for (registers per wavefront <= 512 / OCC).
 template <int D, int NW, int STG, int OCC>
@@ -161,53 +175,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_mfma_kernel(AttnArgs a) {
   static_assert(PER * NW == 2 * TL::NI && PER % 2 == 0 && 2 * PER < 64, "DMA split");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // [stage][K tile | V tile]
 
-  const AttnItem it = a.items[blockIdx.x];
+  const auto &run = as_const(a.runs)[blockIdx.x];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n16 = lane & 15, kg = lane >> 4;
-  const int r = it.tree;
-  const int s0 = a.tree_start[r], T = a.tree_rows[r], klen = a.tree_kv_len[r];
-  const int64_t koff = a.tree_kv_off[r];
-  const int g = it.g, G = a.G, Hkv = a.Hkv, Hq = a.Hq;
-  const int np = (klen + KT - 1) / KT;          // prefix tiles of the tree
-  const int t0 = it.k0 / KT, nt = (it.k1 - it.k0) / KT;
-  const int QB = (it.nq + 15) / 16;             // <= NW
-  const bool wave_on = w < QB;
-
-  // ---- this wave's query fragments (B operand of S^T = K.Q^T), hi and lo
-  uint4 qh[DS], ql[DS];
-  const int mq = w * 16 + n16;
-  const bool qok = wave_on && mq < it.nq;
-  uint64_t anc = 0;
-#pragma unroll
-  for (int ds = 0; ds < DS; ++ds) qh[ds] = ql[ds] = make_uint4(0, 0, 0, 0);
-  if (qok) {
-    const int m = it.m0 + mq;
-    const int row = s0 + m / G;
-    const int head = g * G + m % G;
-    const uint16_t *qp = a.q_rot + (int64_t(row) * Hq + head) * D + kg * 8;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      qh[ds] = *reinterpret_cast<const uint4 *>(qp + ds * 32);
-      ql[ds] = *reinterpret_cast<const uint4 *>(qp + a.q_lo_off + ds * 32);
-    }
-    anc = a.row_anc[row];
-  }
-  // Complete these loads here: the compiler does not see the DMA below, and
-  // would otherwise re-wait for them (with every DMA in flight) in the loop.
-#pragma unroll
-  for (int ds = 0; ds < DS; ++ds) {
-    asm volatile("" : "+v"(qh[ds].x), "+v"(qh[ds].y), "+v"(qh[ds].z), "+v"(qh[ds].w));
-    asm volatile("" : "+v"(ql[ds].x), "+v"(ql[ds].y), "+v"(ql[ds].z), "+v"(ql[ds].w));
-  }
-  asm volatile("" : "+v"(anc));
-
-  // ---- DMA sources: the tree's prefix of KV head g, and its rows
+  const int G = a.G, Hkv = a.Hkv, Hq = a.Hq;
+  const int nt = run.tiles;                                  // the run's tiles, item after item
   const int64_t key_stride = int64_t(Hkv) * ROWB;            // bytes between keys
-  const int64_t head0 = int64_t(g) * D;
-  const uint32_t pre_bytes = klen > 0 ? uint32_t(int64_t(klen - 1) * key_stride + ROWB) : 0u;
-  const uint32_t row_bytes = uint32_t(int64_t(T - 1) * key_stride + ROWB);
-  const uint16_t *pk = a.kv_k + koff * Hkv * D + head0, *pv = a.kv_v + koff * Hkv * D + head0;
-  const uint16_t *rk = a.k_rot + int64_t(s0) * Hkv * D + head0, *rv = a.v_rows + int64_t(s0) * Hkv * D + head0;
+
   // DMA instruction i of this wave covers tile block w + NW * (i % HPER) of
   // K (i < HPER) or V (i >= HPER); voff_lane is the lane's byte offset from
   // the tile's first key (tile row, swizzled source chunk)
@@ -219,10 +193,32 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_mfma_kernel(AttnArgs a) {
     voff_lane[i] = int(row * key_stride + 16 * swz_chunk<D>(row, lane % CH));
   }
   const uint32_t lds0 = lds_addr(smem);
-  auto issue = [&](int s) {                   // DMA tile t0 + s into stage s % STG
-    const int t = t0 + s;
-    const bool pre = t < np;
-    const int vbase = int(int64_t((pre ? t : t - np) * KT) * key_stride);
+
+  // ---- DMA side: walks the run's tiles STG - 1 ahead of the compute side.
+  // Per item: the tree's prefix of KV head g, and its rows.
+  int d_item = run.first, d_tile = 0, d_end = 0, d_np = 0;
+  const uint16_t *pk = nullptr, *pv = nullptr, *rk = nullptr, *rv = nullptr;
+  uint32_t pre_bytes = 0, row_bytes = 0;
+  auto d_enter = [&](int i) {
+    const auto &e = as_const(a.items)[i];
+    const int64_t head0 = int64_t(e.g) * D;
+    d_item = i;
+    d_tile = e.k0 / KT;
+    d_end = e.k1 / KT;
+    d_np = (e.kv_len + KT - 1) / KT;
+    pre_bytes = e.kv_len > 0 ? uint32_t(int64_t(e.kv_len - 1) * key_stride + ROWB) : 0u;
+    row_bytes = uint32_t(int64_t(e.tree_rows - 1) * key_stride + ROWB);
+    pk = a.kv_k + e.kv_off * Hkv * D + head0;
+    pv = a.kv_v + e.kv_off * Hkv * D + head0;
+    rk = a.k_rot + int64_t(e.tree_start) * Hkv * D + head0;
+    rv = a.v_rows + int64_t(e.tree_start) * Hkv * D + head0;
+  };
+  d_enter(run.first);
+  auto issue = [&](int s) {                   // DMA the run's next tile into stage s % STG
+    if (d_tile == d_end) d_enter(d_item + 1);
+    const int t = d_tile++;
+    const bool pre = t < d_np;
+    const int vbase = int(int64_t((pre ? t : t - d_np) * KT) * key_stride);
     const i32x4 rsk = make_rsrc(pre ? pk : rk, pre ? pre_bytes : row_bytes);
     const i32x4 rsv = make_rsrc(pre ? pv : rv, pre ? pre_bytes : row_bytes);
     const uint32_t sbase = lds0 + uint32_t((s % STG) * 2 * TILEB) + uint32_t(w * 1024);
@@ -232,14 +228,60 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_mfma_kernel(AttnArgs a) {
     for (int i = 0; i < HPER; ++i) dma16(rsv, sbase + uint32_t(TILEB + NW * i * 1024), vbase + voff_lane[i], 0);
   };
 
+  // ---- compute side: the current item's query fragments (B operand of
+  // S^T = K.Q^T, hi and lo), ancestor bits and running softmax state
+  const int mq = w * 16 + n16;
+  int c_item = run.first, c_tile = 0, c_end = 0, c_np = 0, c_klen = 0, c_slot = 0;
+  bool wave_on = false, qok = false;
+  uint4 qh[DS], ql[DS];
+  uint64_t anc = 0;
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[DB];
+  auto c_enter = [&](int i) {
+    const auto &e = as_const(a.items)[i];
+    c_item = i;
+    c_tile = e.k0 / KT;
+    c_end = e.k1 / KT;
+    c_np = (e.kv_len + KT - 1) / KT;
+    c_klen = e.kv_len;
+    c_slot = e.slot;
+    wave_on = w < (e.nq + 15) / 16;
+    qok = wave_on && mq < e.nq;
+    anc = 0;
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ds = 0; ds < DS; ++ds) qh[ds] = ql[ds] = make_uint4(0, 0, 0, 0);
+    if (qok) {
+      const int m = e.m0 + mq;
+      const int row = e.tree_start + m / G;
+      const int head = e.g * G + m % G;
+      const uint16_t *qp = a.q_rot + (int64_t(row) * Hq + head) * D + kg * 8;
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        qh[ds] = *reinterpret_cast<const uint4 *>(qp + ds * 32);
+        ql[ds] = *reinterpret_cast<const uint4 *>(qp + a.q_lo_off + ds * 32);
+      }
+      anc = a.row_anc[row];
+    }
+    // Complete these loads here: the compiler does not see the DMA, and
+    // would otherwise re-wait for them (with every DMA in flight) inside the
+    // tile loop.  Here the wait also covers the DMA already issued, which
+    // the next tile needs anyway.
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      asm volatile("" : "+v"(qh[ds].x), "+v"(qh[ds].y), "+v"(qh[ds].z), "+v"(qh[ds].w));
+      asm volatile("" : "+v"(ql[ds].x), "+v"(ql[ds].y), "+v"(ql[ds].z), "+v"(ql[ds].w));
+    }
+    asm volatile("" : "+v"(anc));
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
 
 #pragma unroll
   for (int s = 0; s < STG - 1; ++s)
     if (s < nt) issue(s);
+  c_enter(run.first);
 
   for (int s = 0; s < nt; ++s) {
     const int ahead = min(STG - 2, nt - 1 - s);   // tiles in flight behind this one
@@ -250,152 +292,169 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_mfma_kernel(AttnArgs a) {
     else
       wait_and_barrier<0>();
     if (s + STG - 1 < nt) issue(s + STG - 1);
-    if (!wave_on) continue;
-    const int t = t0 + s;
-    const uint8_t *kt_lds = smem + (s % STG) * 2 * TILEB;
-    const uint8_t *vt_lds = kt_lds + TILEB;
+    if (wave_on) {
+      const int t = c_tile;
+      const uint8_t *kt_lds = smem + (s % STG) * 2 * TILEB;
+      const uint8_t *vt_lds = kt_lds + TILEB;
 
-    // S^T = K.(Q_hi + Q_lo)^T, KB blocks of 16 keys.  With one wavefront per
-    // SIMD, every K and V^T fragment of the tile is read up front (their LDS
-    // latency then overlaps the MFMAs and the softmax); with two, K and V^T
-    // are read in halves.
-    const int sl = lane & 15;
-    const int ra0 = 4 * kg + (sl >> 2);       // V^T source row within a 32-key step
-    auto read_k = [&](int ds, int kb) {
-      const int row = 16 * kb + n16;
-      return *reinterpret_cast<const uint4 *>(kt_lds + row * ROWB + 16 * swz_chunk<D>(row, ds * 4 + kg));
-    };
-    auto read_v = [&](int kp, int db) {
-      const int ra = 32 * kp + ra0, rb = ra + 16;
-      const int c = 2 * db + ((sl & 3) >> 1);
-      const uint2 lo = lds_read_tr16(vt_lds + ra * ROWB + 8 * (sl & 1) + 16 * swz_chunk<D>(ra, c));
-      const uint2 hi = lds_read_tr16(vt_lds + rb * ROWB + 8 * (sl & 1) + 16 * swz_chunk<D>(rb, c));
-      return make_uint4(lo.x, lo.y, hi.x, hi.y);
-    };
-    f32x4 sacc[KB];
+      // S^T = K.(Q_hi + Q_lo)^T, KB blocks of 16 keys.  With one wavefront per
+      // SIMD, every K and V^T fragment of the tile is read up front (their LDS
+      // latency then overlaps the MFMAs and the softmax); with two, K and V^T
+      // are read in halves.
+      const int sl = lane & 15;
+      const int ra0 = 4 * kg + (sl >> 2);       // V^T source row within a 32-key step
+      auto read_k = [&](int ds, int kb) {
+        const int row = 16 * kb + n16;
+        return *reinterpret_cast<const uint4 *>(kt_lds + row * ROWB + 16 * swz_chunk<D>(row, ds * 4 + kg));
+      };
+      auto read_v = [&](int kp, int db) {
+        const int ra = 32 * kp + ra0, rb = ra + 16;
+        const int c = 2 * db + ((sl & 3) >> 1);
+        const uint2 lo = lds_read_tr16(vt_lds + ra * ROWB + 8 * (sl & 1) + 16 * swz_chunk<D>(ra, c));
+        const uint2 hi = lds_read_tr16(vt_lds + rb * ROWB + 8 * (sl & 1) + 16 * swz_chunk<D>(rb, c));
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+      };
+      f32x4 sacc[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint4 vf[KP][DB / VSPLIT];
+      for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      uint4 vf[KP][DB / VSPLIT];
 #pragma unroll
-    for (int part = 0; part < KSPLIT; ++part) {
-      uint4 kf[DS / KSPLIT][KB];
+      for (int part = 0; part < KSPLIT; ++part) {
+        uint4 kf[DS / KSPLIT][KB];
 #pragma unroll
-      for (int dd = 0; dd < DS / KSPLIT; ++dd)
+        for (int dd = 0; dd < DS / KSPLIT; ++dd)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kf[dd][kb] = read_k(part * (DS / KSPLIT) + dd, kb);
-      if (part == 0) {
+          for (int kb = 0; kb < KB; ++kb) kf[dd][kb] = read_k(part * (DS / KSPLIT) + dd, kb);
+        if (part == 0) {
 #pragma unroll
-        for (int kp = 0; kp < KP; ++kp)
+          for (int kp = 0; kp < KP; ++kp)
 #pragma unroll
-          for (int dd = 0; dd < DB / VSPLIT; ++dd) vf[kp][dd] = read_v(kp, dd);
+            for (int dd = 0; dd < DB / VSPLIT; ++dd) vf[kp][dd] = read_v(kp, dd);
+        }
+#pragma unroll
+        for (int dd = 0; dd < DS / KSPLIT; ++dd)
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            const int ds = part * (DS / KSPLIT) + dd;
+            sacc[kb] = mfma16(kf[dd][kb], qh[ds], sacc[kb]);
+            sacc[kb] = mfma16(kf[dd][kb], ql[ds], sacc[kb]);
+          }
+        // order: the K reads, then the S^T MFMAs with the V^T reads (two per
+        // fragment) slotted one per MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, (DS / KSPLIT) * KB, 0);
+        if (part == 0) {
+#pragma unroll
+          for (int m = 0; m < 2 * (DS / KSPLIT) * KB; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (m < 2 * KP * (DB / VSPLIT)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * (DS / KSPLIT) * KB, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+
+      // visibility of the lane's 4 keys per block, as nibbles: a prefix tile
+      // shows its first klen - key0 keys, a row tile the ancestor-or-self rows
+      const bool pre = t < c_np;
+      const int key0 = (pre ? t : t - c_np) * KT;
+      const int lim = pre ? c_klen - key0 : 0;
+      const uint64_t rbits = (!pre && key0 < 64) ? (anc >> key0) : 0ull;
+      const uint32_t rlo = uint32_t(rbits), rhi = uint32_t(rbits >> 32);
+      float x[KB][4];
+      float tmax = -INFINITY;
+      if (pre && lim >= KT) {
+        // a prefix tile whose keys are all visible (every tile but a tree's
+        // last prefix tile and its row tiles): no mask.  Padding query lanes
+        // (zero queries) get finite scores here that are never written out.
 #pragma unroll
-      for (int dd = 0; dd < DS / KSPLIT; ++dd)
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[kb][i] = sacc[kb][i] * a.scale_log2;
+            tmax = fmaxf(tmax, x[kb][i]);
+          }
+      } else {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const int ds = part * (DS / KSPLIT) + dd;
-          sacc[kb] = mfma16(kf[dd][kb], qh[ds], sacc[kb]);
-          sacc[kb] = mfma16(kf[dd][kb], ql[ds], sacc[kb]);
-        }
-      // order: the K reads, then the S^T MFMAs with the V^T reads (two per
-      // fragment) slotted one per MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, (DS / KSPLIT) * KB, 0);
-      if (part == 0) {
+          const int vb = 16 * kb + 4 * kg;
+          const uint32_t nib_pre = (1u << min(max(lim - vb, 0), 4)) - 1u;
+          uint32_t nib_row = 0;
+          if (16 * kb < 64) nib_row = ((kb < 2 ? rlo : rhi) >> ((16 * kb & 31) + 4 * kg)) & 15u;
+          const uint32_t nib = qok ? (pre ? nib_pre : nib_row) : 0u;
 #pragma unroll
-        for (int m = 0; m < 2 * (DS / KSPLIT) * KB; ++m) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (m < 2 * KP * (DB / VSPLIT)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          for (int i = 0; i < 4; ++i) {
+            x[kb][i] = ((nib >> i) & 1u) ? sacc[kb][i] * a.scale_log2 : -INFINITY;
+            tmax = fmaxf(tmax, x[kb][i]);
+          }
         }
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * (DS / KSPLIT) * KB, 0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      // Online softmax (log2 domain) with a lazy reference: the reference m_run
+      // moves only when the tile max exceeds it by more than 8, so p <= 2^8 and
+      // the rescale of O is usually skipped.  l_run is the lane's own share.
+      tmax = rows4_max(tmax);
+      const bool up = tmax > m_run + 8.f;
+      const float alpha = up ? exp2f(m_run - tmax) : 1.f;
+      m_run = up ? tmax : m_run;
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[kb][i] = exp2f(x[kb][i] - m_use);
+          ls += x[kb][i];
+        }
+      l_run = l_run * alpha + ls;
+      if (__builtin_amdgcn_ballot_w64(up) != 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] = o[db] * alpha;
+      }
+      // O^T += V^T.(P_hi + P_lo)^T per 32 keys.  Operand slot 8*kg + t holds
+      // key 4*kg + t (t < 4) or 16 + 4*kg + t - 4 (t >= 4) of the 32, on both
+      // operands.  V^T fragments come from transposing reads: source lane s of
+      // the 16-lane group addresses tile row r0 + (s >> 2), columns
+      // 16*db + 4*(s & 3) .. +3.
+#pragma unroll
+      for (int kp = 0; kp < KP; ++kp) {
+        uint32_t ph[4], pl[4];
+#pragma unroll
+        for (int t2 = 0; t2 < 4; ++t2)
+          split_bf2(x[2 * kp + (t2 >> 1)][2 * (t2 & 1)], x[2 * kp + (t2 >> 1)][2 * (t2 & 1) + 1], ph[t2], pl[t2]);
+        const uint4 pfh = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+        const uint4 pfl = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+#pragma unroll
+        for (int part = 0; part < VSPLIT; ++part) {
+          if (part > 0) {
+#pragma unroll
+            for (int dd = 0; dd < DB / VSPLIT; ++dd) vf[kp][dd] = read_v(kp, part * (DB / VSPLIT) + dd);
+          }
+#pragma unroll
+          for (int dd = 0; dd < DB / VSPLIT; ++dd) {
+            const int db = part * (DB / VSPLIT) + dd;
+            o[db] = mfma16(vf[kp][dd], pfh, o[db]);
+            o[db] = mfma16(vf[kp][dd], pfl, o[db]);
+          }
+        }
+      }
     }
 
-    // visibility of the lane's 4 keys per block, as nibbles: a prefix tile
-    // shows its first klen - key0 keys, a row tile the ancestor-or-self rows
-    const bool pre = t < np;
-    const int key0 = (pre ? t : t - np) * KT;
-    const int lim = pre ? klen - key0 : 0;
-    const uint64_t rbits = (!pre && key0 < 64) ? (anc >> key0) : 0ull;
-    const uint32_t rlo = uint32_t(rbits), rhi = uint32_t(rbits >> 32);
-    float x[KB][4];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int vb = 16 * kb + 4 * kg;
-      const uint32_t nib_pre = (1u << min(max(lim - vb, 0), 4)) - 1u;
-      uint32_t nib_row = 0;
-      if (16 * kb < 64) nib_row = ((kb < 2 ? rlo : rhi) >> ((16 * kb & 31) + 4 * kg)) & 15u;
-      const uint32_t nib = qok ? (pre ? nib_pre : nib_row) : 0u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[kb][i] = ((nib >> i) & 1u) ? sacc[kb][i] * a.scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, x[kb][i]);
-      }
-    }
-    // Online softmax (log2 domain) with a lazy reference: the reference m_run
-    // moves only when the tile max exceeds it by more than 8, so p <= 2^8 and
-    // the rescale of O is usually skipped.  l_run is the lane's own share.
-    tmax = rows4_max(tmax);
-    const bool up = tmax > m_run + 8.f;
-    const float alpha = up ? exp2f(m_run - tmax) : 1.f;
-    m_run = up ? tmax : m_run;
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float ls = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[kb][i] = exp2f(x[kb][i] - m_use);
-        ls += x[kb][i];
-      }
-    l_run = l_run * alpha + ls;
-    if (__builtin_amdgcn_ballot_w64(up) != 0) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] = o[db] * alpha;
-    }
-    // O^T += V^T.(P_hi + P_lo)^T per 32 keys.  Operand slot 8*kg + t holds
-    // key 4*kg + t (t < 4) or 16 + 4*kg + t - 4 (t >= 4) of the 32, on both
-    // operands.  V^T fragments come from transposing reads: source lane s of
-    // the 16-lane group addresses tile row r0 + (s >> 2), columns
-    // 16*db + 4*(s & 3) .. +3.
-#pragma unroll
-    for (int kp = 0; kp < KP; ++kp) {
-      uint16_t ph[8], pl[8];
-#pragma unroll
-      for (int t8 = 0; t8 < 8; ++t8) split_bf(x[2 * kp + (t8 >> 2)][t8 & 3], ph[t8], pl[t8]);
-      const uint4 pfh = make_uint4(ph[0] | (uint32_t(ph[1]) << 16), ph[2] | (uint32_t(ph[3]) << 16),
-                                   ph[4] | (uint32_t(ph[5]) << 16), ph[6] | (uint32_t(ph[7]) << 16));
-      const uint4 pfl = make_uint4(pl[0] | (uint32_t(pl[1]) << 16), pl[2] | (uint32_t(pl[3]) << 16),
-                                   pl[4] | (uint32_t(pl[5]) << 16), pl[6] | (uint32_t(pl[7]) << 16));
-#pragma unroll
-      for (int part = 0; part < VSPLIT; ++part) {
-        if (part > 0) {
-#pragma unroll
-          for (int dd = 0; dd < DB / VSPLIT; ++dd) vf[kp][dd] = read_v(kp, part * (DB / VSPLIT) + dd);
+    // ---- the item ends with this tile: its partial results, then the next
+    // item's queries
+    if (++c_tile == c_end) {
+      const float l_all = rows4_sum(l_run);
+      if (qok) {
+        const int64_t slot = int64_t(c_slot) + mq;
+        if (kg == 0) {
+          a.part_ml[2 * slot] = m_run;
+          a.part_ml[2 * slot + 1] = l_all;
         }
+        float *po = a.part_o + slot * D + 4 * kg;
 #pragma unroll
-        for (int dd = 0; dd < DB / VSPLIT; ++dd) {
-          const int db = part * (DB / VSPLIT) + dd;
-          o[db] = mfma16(vf[kp][dd], pfh, o[db]);
-          o[db] = mfma16(vf[kp][dd], pfl, o[db]);
-        }
+        for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4 *>(po + db * 16) = o[db];
       }
+      if (s + 1 < nt) c_enter(c_item + 1);
     }
-  }
-  l_run = rows4_sum(l_run);
-
-  // ---- partial results
-  if (qok) {
-    const int64_t slot = int64_t(it.slot) + mq;
-    if (kg == 0) {
-      a.part_ml[2 * slot] = m_run;
-      a.part_ml[2 * slot + 1] = l_run;
-    }
-    float *po = a.part_o + slot * D + 4 * kg;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4 *>(po + db * 16) = o[db];
   }
 }
 
@@ -555,21 +614,21 @@ void launch_rope_f32(const float *q, const float *k, float *qo, float *ko, const
 }
 
 template <int D, int NW, int STG, int OCC>
-static void launch_attn_dd(const AttnArgs &a, int n_items, hipStream_t s) {
+static void launch_attn_dd(const AttnArgs &a, int n_runs, hipStream_t s) {
   constexpr size_t lds = attn_lds_bytes<D, STG>();
   (void)hipFuncSetAttribute(reinterpret_cast<const void *>(attn_mfma_kernel<D, NW, STG, OCC>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-  hipLaunchKernelGGL((attn_mfma_kernel<D, NW, STG, OCC>), dim3(n_items), dim3(64 * NW), lds, s, a);
+  hipLaunchKernelGGL((attn_mfma_kernel<D, NW, STG, OCC>), dim3(n_runs), dim3(64 * NW), lds, s, a);
 }
 
 // Four wavefronts (up to 64 query vectors): a 2-stage ring (64 KB of LDS)
 // so that two workgroups share a compute unit and hide each other's
 // latencies.  Eight wavefronts: a 4-stage ring, one workgroup per unit.
-void launch_attn_mfma(const AttnArgs &a, int n_items, int D, int max_qblocks, hipStream_t s) {
+void launch_attn_mfma(const AttnArgs &a, int n_runs, int D, int max_qblocks, hipStream_t s) {
   const bool eight = max_qblocks > 4;
-  if (D == 64) eight ? launch_attn_dd<64, 8, 4, 2>(a, n_items, s) : launch_attn_dd<64, 4, 2, 2>(a, n_items, s);
-  if (D == 128) eight ? launch_attn_dd<128, 8, 4, 2>(a, n_items, s) : launch_attn_dd<128, 4, 2, 2>(a, n_items, s);
-  if (D == 256) eight ? launch_attn_dd<256, 8, 4, 2>(a, n_items, s) : launch_attn_dd<256, 4, 2, 2>(a, n_items, s);
+  if (D == 64) eight ? launch_attn_dd<64, 8, 4, 2>(a, n_runs, s) : launch_attn_dd<64, 4, 2, 2>(a, n_runs, s);
+  if (D == 128) eight ? launch_attn_dd<128, 8, 4, 2>(a, n_runs, s) : launch_attn_dd<128, 4, 2, 2>(a, n_runs, s);
+  if (D == 256) eight ? launch_attn_dd<256, 8, 4, 2>(a, n_runs, s) : launch_attn_dd<256, 4, 2, 2>(a, n_runs, s);
 }
 
 void launch_attn_merge(const MergeArgs &a, int n_rows, int D, hipStream_t s) {

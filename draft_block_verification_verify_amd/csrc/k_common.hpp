@@ -57,6 +57,22 @@ __device__ __forceinline__ void split_bf(float x, uint16_t &hi, uint16_t &lo) {
   lo = f2bf(x - bf2f(hi));
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 in one word (x in the low half), round to nearest
+// even, by the gfx950 packed conversion instruction.
+__device__ __forceinline__ uint32_t cvt_bf2(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2_t));
+}
+
+// hi + lo split of two values at once: hi = bf16(v), lo = bf16(v - hi),
+// each pair packed as cvt_bf2 packs it.
+__device__ __forceinline__ void split_bf2(float x, float y, uint32_t &hi, uint32_t &lo) {
+  hi = cvt_bf2(x, y);
+  lo = cvt_bf2(x - __uint_as_float(hi << 16), y - __uint_as_float(hi & 0xFFFF0000u));
+}
+
 // 8 bf16 -> 8 fp16.  Exact for |x| in the fp16 normal range (a bf16
 // significand fits in fp16's); tiny values become fp16 subnormals.
 __device__ __forceinline__ uint4 bf8_to_h8(uint4 v) {

@@ -34,8 +34,7 @@ struct AttnArgs {
   const uint16_t *q_rot;           // [n, Hq, D] bf16 hi plane of the rotated queries
   int64_t q_lo_off;                // elements from the hi plane to the lo plane
   const AttnItem *items;
-  const int32_t *tree_start, *tree_rows, *tree_kv_len;
-  const int64_t *tree_kv_off;
+  const AttnRun *runs;             // one per workgroup
   const uint64_t *row_anc;
   float *part_o, *part_ml;         // [slots, D], [slots, 2]
   int Hq, Hkv, G;
@@ -90,7 +89,7 @@ void launch_rope_bf16(const uint16_t *q, const uint16_t *k, uint16_t *qo, uint16
                       int n, int Hq, int Hkv, int D, double base, int64_t q_lo_off, hipStream_t s);
 void launch_rope_f32(const float *q, const float *k, float *qo, float *ko, const int32_t *row_pos, int n, int Hq,
                      int Hkv, int D, double base, hipStream_t s);
-void launch_attn_mfma(const AttnArgs &a, int n_items, int D, int max_qblocks, hipStream_t s);
+void launch_attn_mfma(const AttnArgs &a, int n_runs, int D, int max_qblocks, hipStream_t s);
 void launch_attn_merge(const MergeArgs &a, int n_rows, int D, hipStream_t s);
 void launch_attn_f32(const AttnF32Args &a, int n_rows, hipStream_t s);
 

@@ -75,7 +75,7 @@ static int qg_max_of(const Dims &dm) {
   return int(ceil_div(int64_t(dm.max_tree_rows) * G, kItemQ));
 }
 
-MetaLayout meta_layout(int n, int R, int n_draft, int n_items, int n_groups) {
+MetaLayout meta_layout(int n, int R, int n_draft, int n_items, int n_runs, int n_groups) {
   MetaLayout L{};
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -96,6 +96,7 @@ MetaLayout meta_layout(int n, int R, int n_draft, int n_items, int n_groups) {
   L.tree_kv_len = take(4 * size_t(R));
   L.tree_kv_off = take(8 * size_t(R));
   L.items = take(sizeof(AttnItem) * size_t(std::max(n_items, 1)));
+  L.runs = take(sizeof(AttnRun) * size_t(std::max(n_runs, 1)));
   L.group_first = take(4 * size_t(n_groups));
   L.group_count = take(4 * size_t(n_groups));
   L.total = o;
@@ -105,8 +106,8 @@ MetaLayout meta_layout(int n, int R, int n_draft, int n_items, int n_groups) {
 size_t meta_capacity(const Dims &dm, int target_items) {
   const int qg = qg_max_of(dm);
   const int groups = dm.max_roots * dm.Hkv * qg;
-  const int items = target_items + groups + 64;
-  return meta_layout(dm.max_rows, dm.max_roots, dm.max_rows, items, groups).total;
+  const int runs = std::max(target_items, 1);
+  return meta_layout(dm.max_rows, dm.max_roots, dm.max_rows, runs + groups, runs, groups).total;
 }
 
 int build_plan(const Dims &dm, const HostInputs &in, int64_t slot_cap, int target_items,
@@ -241,18 +242,40 @@ int build_plan(const Dims &dm, const HostInputs &in, int64_t slot_cap, int targe
     mq_max = int(std::max<int64_t>(mq_max, std::min<int64_t>(mq, kItemQ)));
     total += int64_t(dm.Hkv) * ceil_div(mq, kItemQ) * tiles[r];
   }
-  // Each item writes nq partial records of (d + 2) floats; keep that below
-  // half of the item's K + V bytes (chunk >= 4 * nq keys), and aim for
-  // `target_items` items overall.
+  // Runs: the sequence of every query group's tiles (group order: tree, KV
+  // head, query group) cut into pieces of `chunk` tiles.  A run that covers a
+  // group's tiles only in part shares that group with its neighbours; each
+  // (run, group) pair is one work item.  Each item writes nq partial records
+  // of (d + 2) floats: keep the run at least 4 * nq keys long, so that the
+  // records stay below half of the K + V bytes a run reads; keep a group's
+  // items within kMaxSplits; aim for `target_items` runs.
   int64_t max_tiles = 1;
   for (int r = 0; r < P.R; ++r) max_tiles = std::max(max_tiles, tiles[r]);
   int64_t chunk = std::max<int64_t>({ceil_div(64, KT), ceil_div(4 * int64_t(mq_max), KT),
                                      ceil_div(total, std::max(target_items, 1)),
-                                     ceil_div(max_tiles, kMaxSplits)});   // in tiles
+                                     ceil_div(max_tiles, kMaxSplits - 1)});   // in tiles
+  auto for_each_item = [&](int64_t ch, auto &&fn) {
+    // fn(r, g, qg, m0, nq, tile0, tile1, run) for every work item in order
+    int64_t at = 0;   // position in the whole sequence
+    for (int r = 0; r < P.R; ++r) {
+      const int mq = P.tree_rows[r] * G;
+      for (int g = 0; g < dm.Hkv; ++g)
+        for (int qg = 0; qg * kItemQ < mq; ++qg) {
+          const int m0 = qg * kItemQ;
+          const int nq = std::min(kItemQ, mq - m0);
+          for (int64_t t0 = 0; t0 < tiles[r];) {
+            const int64_t run = at / ch;
+            const int64_t t1 = std::min(tiles[r], t0 + (run + 1) * ch - at);
+            fn(r, g, qg, m0, nq, t0, t1, run);
+            at += t1 - t0;
+            t0 = t1;
+          }
+        }
+    }
+  };
   for (;;) {
     int64_t slots = 0;
-    for (int r = 0; r < P.R; ++r)
-      slots += int64_t(dm.Hkv) * ceil_div(tiles[r], chunk) * P.tree_rows[r] * G;
+    for_each_item(chunk, [&](int, int, int, int, int nq, int64_t, int64_t, int64_t) { slots += nq; });
     if (slots <= slot_cap) break;
     if (chunk > (int64_t(1) << 30) / KT) {
       *err = "attention partial capacity exhausted";
@@ -264,36 +287,35 @@ int build_plan(const Dims &dm, const HostInputs &in, int64_t slot_cap, int targe
   const int n_groups = P.R * dm.Hkv * P.qg_max;
   P.group_first.assign(n_groups, 0);
   P.group_count.assign(n_groups, 0);
+  P.runs.assign(size_t(ceil_div(total, chunk)), AttnRun{0, 0, 0, 0});
   int64_t slot = 0;
-  for (int r = 0; r < P.R; ++r) {
-    const int mq = P.tree_rows[r] * G;
-    const int64_t splits = ceil_div(tiles[r], chunk);
-    const int64_t piece = ceil_div(tiles[r], splits);   // equal pieces, the last one ragged
-    for (int g = 0; g < dm.Hkv; ++g) {
-      for (int qg = 0; qg * kItemQ < mq; ++qg) {
-        const int m0 = qg * kItemQ;
-        const int nq = std::min(kItemQ, mq - m0);
-        const int gi = (r * dm.Hkv + g) * P.qg_max + qg;
-        P.group_first[gi] = int32_t(P.items.size());
-        for (int64_t t0 = 0; t0 < tiles[r]; t0 += piece) {
-          AttnItem it{};
-          it.tree = r;
-          it.g = g;
-          it.m0 = m0;
-          it.nq = nq;
-          it.k0 = int32_t(t0 * KT);
-          it.k1 = int32_t(std::min(tiles[r], t0 + piece) * KT);
-          it.slot = int32_t(slot);
-          slot += nq;
-          P.items.push_back(it);
-        }
-        P.group_count[gi] = int32_t(P.items.size()) - P.group_first[gi];
-      }
-    }
-  }
+  for_each_item(chunk, [&](int r, int g, int qg, int m0, int nq, int64_t t0, int64_t t1, int64_t run) {
+    const int gi = (r * dm.Hkv + g) * P.qg_max + qg;
+    if (P.group_count[gi] == 0) P.group_first[gi] = int32_t(P.items.size());
+    ++P.group_count[gi];
+    AttnRun &R = P.runs[size_t(run)];
+    if (R.count == 0) R.first = int32_t(P.items.size());
+    ++R.count;
+    R.tiles += int32_t(t1 - t0);
+    AttnItem it{};
+    it.tree = r;
+    it.g = g;
+    it.m0 = m0;
+    it.nq = nq;
+    it.k0 = int32_t(t0 * KT);
+    it.k1 = int32_t(t1 * KT);
+    it.slot = int32_t(slot);
+    it.tree_start = P.tree_start[r];
+    it.tree_rows = P.tree_rows[r];
+    it.kv_len = P.tree_kv_len[r];
+    it.kv_off = P.tree_kv_off[r];
+    slot += nq;
+    P.items.push_back(it);
+  });
   P.slots = slot;
-  const size_t cap_items = size_t(target_items) + size_t(dm.max_roots) * dm.Hkv * P.qg_max + 64;
-  if (P.items.size() > cap_items || P.slots > slot_cap) {
+  const size_t cap_runs = size_t(std::max(target_items, 1));
+  if (P.runs.size() > cap_runs || P.items.size() > cap_runs + size_t(dm.max_roots) * dm.Hkv * P.qg_max ||
+      P.slots > slot_cap) {
     *err = "attention work list exceeds the handle's capacity";
     return P_CAPACITY;
   }
@@ -302,7 +324,7 @@ int build_plan(const Dims &dm, const HostInputs &in, int64_t slot_cap, int targe
 
 void pack_plan(const Plan &p, int Hkv, void *dst, MetaLayout *lay) {
   const int n_groups = p.R * Hkv * p.qg_max;
-  MetaLayout L = meta_layout(p.n, p.R, p.n_draft, int(p.items.size()), n_groups);
+  MetaLayout L = meta_layout(p.n, p.R, p.n_draft, int(p.items.size()), int(p.runs.size()), n_groups);
   char *b = static_cast<char *>(dst);
   auto put = [&](size_t off, const void *src, size_t bytes) {
     if (bytes) std::memcpy(b + off, src, bytes);
@@ -320,6 +342,7 @@ void pack_plan(const Plan &p, int Hkv, void *dst, MetaLayout *lay) {
   put(L.tree_kv_len, p.tree_kv_len.data(), 4 * size_t(p.R));
   put(L.tree_kv_off, p.tree_kv_off.data(), 8 * size_t(p.R));
   put(L.items, p.items.data(), sizeof(AttnItem) * p.items.size());
+  put(L.runs, p.runs.data(), sizeof(AttnRun) * p.runs.size());
   put(L.group_first, p.group_first.data(), 4 * size_t(n_groups));
   put(L.group_count, p.group_count.data(), 4 * size_t(n_groups));
   *lay = L;

@@ -9,11 +9,11 @@
 
 namespace sv {
 
-// Query vectors of one attention work item: the (row, head-in-group) pairs of
-// one tree for one KV head, at most kItemQ of them per item.
+// Query vectors of one attention query group: the (row, head-in-group) pairs
+// of one tree for one KV head, at most kItemQ of them per group.
 constexpr int kItemQ = 128;
 constexpr int kMaxTreeRows = 64;   // ancestor masks are one uint64 per row
-constexpr int kMaxSplits = 1024;   // most key-range items per (tree, KV head, query group)
+constexpr int kMaxSplits = 1024;   // most work items per query group
 
 struct Dims {
   int32_t Hq, Hkv, d, hidden, vocab, dtype;
@@ -30,13 +30,30 @@ constexpr int attn_key_tile(int d) { return 8192 / d; }
 // padded), then ceil(T / KT) row tiles hold the tree's T rows in row order.
 // A tile never mixes the prefix with the rows.
 //
-// One attention work item: tiles [k0 / KT, k1 / KT) of that sequence (k0, k1
-// in keys, multiples of KT) against query vectors [m0, m0+nq) of
-// (tree, kv head g); m = local_row * G + head_in_group.
+// Query group: query vectors [m0, m0+nq) of (tree, kv head g), where
+// m = local_row * G + head_in_group.  The attention work is the sequence of
+// all query groups' tiles, group after group; it is cut into runs of equal
+// length, one workgroup each, so a run may end inside a group and the next
+// run continue it.
+//
+// One attention work item: the part of one query group that one run covers,
+// tiles [k0 / KT, k1 / KT) of the tree's sequence (k0, k1 in keys, multiples
+// of KT).  It leaves one partial (max, sum, o) record per query vector from
+// `slot` on.  The item also carries its tree's first row, row count, prefix
+// length and prefix offset.
 struct AttnItem {
-  int32_t tree, g, m0, nq, k0, k1, slot, pad;
+  int32_t tree, g, m0, nq, k0, k1, slot, tree_start;
+  int32_t tree_rows, kv_len;
+  int64_t kv_off;
 };
-static_assert(sizeof(AttnItem) == 32, "AttnItem layout");
+static_assert(sizeof(AttnItem) == 48, "AttnItem layout");
+
+// One workgroup's run: items [first, first + count) in order, `tiles` tiles
+// in all.
+struct AttnRun {
+  int32_t first, count, tiles, pad;
+};
+static_assert(sizeof(AttnRun) == 16, "AttnRun layout");
 
 struct HostInputs {
   int32_t n_rows, n_roots;
@@ -59,10 +76,11 @@ struct Plan {
   std::vector<int32_t> tree_start, tree_rows, tree_kv_len;
   std::vector<int64_t> tree_kv_off;
   // attention
-  std::vector<AttnItem> items;
+  std::vector<AttnItem> items;        // in query-group order
+  std::vector<AttnRun> runs;          // one per attention workgroup
   int32_t qg_max = 1;                 // query groups per (tree, g)
-  std::vector<int32_t> group_first, group_count;   // [R * Hkv * qg_max]
-  int32_t chunk = 0;                  // keys per work item (before ragged ends)
+  std::vector<int32_t> group_first, group_count;   // [R * Hkv * qg_max], into items
+  int32_t chunk = 0;                  // keys per run (the last run shorter)
   int64_t slots = 0;                  // partial (m, l, o) records needed
 };
 
@@ -74,7 +92,7 @@ int check_dims(const Dims &dm, std::string *err);
 
 // Validate the host inputs of one run and build its plan.  `slot_cap` bounds
 // plan->slots; the work split is coarsened until it fits.  `target_items`
-// is the work-item count to aim for (a few per compute unit).
+// is the run (workgroup) count to aim for.
 int build_plan(const Dims &dm, const HostInputs &in, int64_t slot_cap, int target_items,
                Plan *plan, std::string *err);
 
@@ -85,10 +103,10 @@ int64_t slot_capacity(const Dims &dm);
 struct MetaLayout {
   size_t row_tree, row_local, row_pos, row_parent, row_draft, row_anc, row_child, draft_row;
   size_t tree_start, tree_rows, tree_kv_len, tree_kv_off;
-  size_t items, group_first, group_count;
+  size_t items, runs, group_first, group_count;
   size_t total;
 };
-MetaLayout meta_layout(int n, int R, int n_draft, int n_items, int n_groups);
+MetaLayout meta_layout(int n, int R, int n_draft, int n_items, int n_runs, int n_groups);
 // Upper bound of the meta buffer for a handle's capacities.
 size_t meta_capacity(const Dims &dm, int target_items);
 // Serialise the plan into `dst` (at least meta_layout(...).total bytes).

@@ -1,6 +1,6 @@
 // Test-only C entry to the host planner (plan.cpp), built with g++ on a
 // machine without a GPU: validation status, error text, per-row ancestor
-// masks and the attention work list.
+// masks, the attention work items and the workgroup runs.
 #include <cstring>
 #include <string>
 
@@ -9,7 +9,7 @@
 extern "C" int svp_plan(const int *dims, int n_rows, int n_roots, const int32_t *parent, const int32_t *pos,
                         const int64_t *off, const int32_t *len, int64_t kv_tokens, int64_t slot_cap,
                         int target_items, int64_t *stats, char *err, int err_cap, uint64_t *anc_out,
-                        int32_t *items_out, int items_cap) {
+                        int32_t *items_out, int items_cap, int32_t *runs_out, int runs_cap) {
   sv::Dims dm{dims[0], dims[1], dims[2], dims[3], dims[4], dims[5], dims[6], dims[7], dims[8], dims[9]};
   std::string e;
   int st = sv::check_dims(dm, &e);
@@ -29,10 +29,14 @@ extern "C" int svp_plan(const int *dims, int n_rows, int n_roots, const int32_t 
   stats[3] = p.slots;
   stats[4] = p.chunk;
   stats[5] = p.qg_max;
-  stats[6] = int64_t(sv::meta_layout(p.n, p.R, p.n_draft, int(p.items.size()), p.R * dm.Hkv * p.qg_max).total);
+  stats[6] = int64_t(sv::meta_layout(p.n, p.R, p.n_draft, int(p.items.size()), int(p.runs.size()),
+                                          p.R * dm.Hkv * p.qg_max).total);
   stats[7] = int64_t(sv::meta_capacity(dm, target_items));
   for (int i = 0; i < p.n; ++i) anc_out[i] = p.row_anc[i];
   const int ni = int(p.items.size()) < items_cap ? int(p.items.size()) : items_cap;
   std::memcpy(items_out, p.items.data(), sizeof(sv::AttnItem) * size_t(ni));
+  stats[8] = int64_t(p.runs.size());
+  const int nr = int(p.runs.size()) < runs_cap ? int(p.runs.size()) : runs_cap;
+  std::memcpy(runs_out, p.runs.data(), sizeof(sv::AttnRun) * size_t(nr));
   return 0;
 }

@@ -108,16 +108,39 @@ def plan(L, dims, parent, pos, off, lens, kv_tokens, slot_cap=1 << 20, target=10
     lens = np.ascontiguousarray(lens, np.int32)
     n = len(parent)
     dims = np.ascontiguousarray(dims, np.int32)
-    stats = np.zeros(8, np.int64)
+    stats = np.zeros(9, np.int64)
     err = C.create_string_buffer(512)
     anc = np.zeros(max(n, 1), np.uint64)
-    items = np.zeros((8192, 8), np.int32)
+    items = np.zeros((8192, 12), np.int32)       # AttnItem: 10 int32 + one int64
+    runs = np.zeros((8192, 4), np.int32)         # AttnRun: first, count, tiles, pad
     st = L.svp_plan(dims.ctypes.data_as(C.c_void_p), n, len(lens), parent.ctypes.data_as(C.c_void_p),
                     pos.ctypes.data_as(C.c_void_p), off.ctypes.data_as(C.c_void_p),
                     lens.ctypes.data_as(C.c_void_p), C.c_int64(kv_tokens), C.c_int64(slot_cap), target,
                     stats.ctypes.data_as(C.c_void_p), err, 512, anc.ctypes.data_as(C.c_void_p),
-                    items.ctypes.data_as(C.c_void_p), 8192)
-    return st, err.value.decode(), stats, anc, items[: stats[2]] if st == 0 else None
+                    items.ctypes.data_as(C.c_void_p), 8192, runs.ctypes.data_as(C.c_void_p), 8192)
+    if st != 0:
+        return st, err.value.decode(), stats, anc, None
+    check_runs(items[: stats[2]], runs[: stats[8]], stats, 8192 // dims[2], target)
+    return st, err.value.decode(), stats, anc, items[: stats[2]]
+
+
+def check_runs(items, runs, stats, KT, target):
+    """Runs cut the item sequence in order: run j holds items
+    [first, first + count), its tiles sum to `tiles`, every run but the last
+    has chunk / KT tiles, and no more runs than asked for."""
+    assert 1 <= len(runs) <= target
+    ch = stats[4] // KT
+    nxt = 0
+    for j, (first, count, tiles, _) in enumerate(runs):
+        assert first == nxt and count >= 1
+        nxt = first + count
+        its = items[first:first + count]
+        assert tiles == sum((it[5] - it[4]) // KT for it in its)
+        assert tiles == ch or (j == len(runs) - 1 and 1 <= tiles <= ch)
+        # only a run's first item may start inside a group, only its last end inside one
+        for it in its[1:]:
+            assert it[4] == 0
+    assert nxt == len(items)
 
 
 DIMS = [32, 8, 128, 4096, 151936, 1, 512, 64, 64, 1 << 20]   # Hq Hkv d hidden V dtype rows roots tree pos
@@ -158,6 +181,9 @@ def test_plan_ancestor_masks_and_items_cover_keys(plan_lib):
                 for it in its:
                     assert it[3] == min(128, T[tree] * G - qg * 128)
                     slots.append((it[6], it[6] + it[3]))
+                    # the tree's own fields, copied into every item
+                    assert (it[7], it[8], it[9]) == (starts[tree], T[tree], lens[tree])
+                    assert int(it[10:12].view(np.int64)[0]) == off[tree]
     slots.sort()
     assert slots[0][0] == 0 and slots[-1][1] == stats[3]
     for a, b in zip(slots, slots[1:]):
@@ -171,7 +197,10 @@ def test_plan_coarsens_split_to_fit_slot_capacity(plan_lib):
                                     parent, np.arange(17) + 8192, [0], [8192], 8192, slot_cap=24 * 17 * 2)
     assert st == 0, err
     assert stats[3] <= 24 * 17 * 2
-    assert stats[2] == 4 * 2          # 2 pieces per KV head
+    # 4 KV heads x 257 tiles in runs of at least 208 tiles: at most 2 items per head
+    assert stats[4] // 32 >= 208 and len(items) <= 8
+    for g in range(4):
+        assert 1 <= sum(1 for it in items if it[1] == g) <= 2
 
 
 def test_plan_caps_splits_per_group(plan_lib):
