@@ -428,8 +428,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   const int64_t *tree_kv_off = reinterpret_cast<const int64_t *>(m + lay.tree_kv_off);
   const sv::AttnItem *items = reinterpret_cast<const sv::AttnItem *>(m + lay.items);
   const sv::AttnRun *runs = reinterpret_cast<const sv::AttnRun *>(m + lay.runs);
-  const int32_t *group_first = reinterpret_cast<const int32_t *>(m + lay.group_first);
-  const int32_t *group_count = reinterpret_cast<const int32_t *>(m + lay.group_count);
+  const sv::AttnGroup *groups = reinterpret_cast<const sv::AttnGroup *>(m + lay.groups);
 
   // ---- stage bookkeeping for profiling (events on the run's stream)
   bool recording = false;
@@ -530,9 +529,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     sv::MergeArgs ma{};
     ma.part_o = h->part_o;
     ma.part_ml = h->part_ml;
-    ma.items = items;
-    ma.group_first = group_first;
-    ma.group_count = group_count;
+    ma.groups = groups;
     ma.row_tree = row_tree;
     ma.row_local = row_local;
     ma.Hq = int(Hq);
@@ -542,7 +539,9 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     ma.lo_off = o_lo;
     ma.out = static_cast<uint16_t *>(h->o_act);
     begin("attn_merge");
-    sv::launch_attn_merge(ma, n, int(D), stream);
+    int n_groups_used = 0;
+    for (const auto &gr : plan.groups) n_groups_used += gr.count > 0;
+    sv::launch_attn_merge(ma, n, int(D), double(plan.items.size()) / std::max(n_groups_used, 1), stream);
     end();
     sv::GemmArgs g{};
     g.act = static_cast<const uint16_t *>(h->o_act);

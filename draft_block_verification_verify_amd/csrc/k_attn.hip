@@ -458,69 +458,99 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_mfma_kernel(AttnArgs a) {
   }
 }
 
-// Combine the split-KV partials of one (row, query head) and write o in the
-// projection's activation format.  The first wave reads the (max, sum)
-// records of all splits at once and leaves each split's weight
-// exp2(m_t - M) in LDS; then every thread sums its column over the splits,
-// four independent loads at a time.
-template <int D>
-__global__ __launch_bounds__(D) void attn_merge_kernel(MergeArgs a) {
-  __shared__ float wgt[kMaxSplits];
-  __shared__ int64_t slot_of[kMaxSplits];
-  __shared__ float tot_l;
-  const int i = blockIdx.x / a.Hq, h = blockIdx.x % a.Hq;
+// Combine the partial records of one (row, query head) and write o in the
+// projection's activation format.  WPP wavefronts per (row, query head): one
+// when its query group has few items (four pairs per workgroup), four when
+// it has many (the items split round robin, the four sums added in LDS).
+// Lane c owns elements [c E, c E + E) of o, E = D / 64.  Each wavefront
+// reads the (max, sum) records once (each lane folds its share into a
+// running pair) and leaves the item weights exp2(m_t - M) in its own LDS
+// row; then it sums the o records, four in flight.
+template <int D, int WPP>
+__global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a, int n_pairs) {
+  constexpr int E = D / 64;
+  typedef float fvec __attribute__((ext_vector_type(E)));
+  __shared__ float wl[4][kMaxSplits];
+  __shared__ fvec red[WPP > 1 ? WPP : 1][64];
+  const int w = threadIdx.x >> 6, c = threadIdx.x & 63;
+  const int pair = WPP > 1 ? int(blockIdx.x) : int(blockIdx.x) * 4 + w;
+  if (WPP == 1 && pair >= n_pairs) return;    // no workgroup-wide synchronisation with one wave per pair
+  const int i = pair / a.Hq, h = pair % a.Hq;
   const int G = a.Hq / a.Hkv;
-  const int r = a.row_tree[i], loc = a.row_local[i];
+  const int r = as_const(a.row_tree)[i], loc = as_const(a.row_local)[i];
   const int g = h / G, m = loc * G + h % G;
   const int qg = m / kItemQ, mi = m % kItemQ;
-  const int gi = (r * a.Hkv + g) * a.qg_max + qg;
-  const int first = a.group_first[gi], cnt = min(a.group_count[gi], kMaxSplits);   // the plan keeps it <= kMaxSplits
-  const int c = threadIdx.x;
-  if (c < 64) {
-    float M = -INFINITY;
-    for (int t = c; t < cnt; t += 64) {
-      const int64_t slot = int64_t(a.items[first + t].slot) + mi;
-      slot_of[t] = slot;
-      M = fmaxf(M, a.part_ml[2 * slot]);
+  const auto &gr = as_const(a.groups)[(r * a.Hkv + g) * a.qg_max + qg];
+  const int cnt = min(gr.count, kMaxSplits);   // the plan keeps it <= kMaxSplits
+  const int64_t base = int64_t(gr.slot) + mi, stride = gr.nq;
+
+  // (max, sum) over the items; an item that saw no key of this query has
+  // max -inf and sum 0
+  float Mi = -INFINITY, Li = 0.f;
+  for (int t = c; t < cnt; t += 64) {
+    const float2 ml = *reinterpret_cast<const float2 *>(a.part_ml + 2 * (base + t * stride));
+    wl[w][t] = ml.x;
+    if (ml.x == -INFINITY) continue;
+    if (ml.x > Mi) {
+      Li = (Mi == -INFINITY ? 0.f : Li * exp2f(Mi - ml.x)) + ml.y;
+      Mi = ml.x;
+    } else {
+      Li += ml.y * exp2f(ml.x - Mi);
     }
-    M = wave_max(M);
-    float L = 0.f;
-    for (int t = c; t < cnt; t += 64) {
-      const int64_t slot = slot_of[t];
-      const float mt = a.part_ml[2 * slot];
-      const float w = (mt == -INFINITY) ? 0.f : exp2f(mt - M);
-      wgt[t] = w;
-      L += w * a.part_ml[2 * slot + 1];
-    }
-    L = wave_sum(L);
-    if (c == 0) tot_l = L;
   }
-  __syncthreads();
-  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-  int t = 0;
-  for (; t + 4 <= cnt; t += 4) {
-    const float o0 = a.part_o[slot_of[t] * D + c], o1 = a.part_o[slot_of[t + 1] * D + c];
-    const float o2 = a.part_o[slot_of[t + 2] * D + c], o3 = a.part_o[slot_of[t + 3] * D + c];
-    acc0 += wgt[t] * o0;
-    acc1 += wgt[t + 1] * o1;
-    acc2 += wgt[t + 2] * o2;
-    acc3 += wgt[t + 3] * o3;
+  const float M = wave_max(Mi);
+  const float L = wave_sum(Mi == -INFINITY ? 0.f : Li * exp2f(Mi - M));
+  for (int t = c; t < cnt; t += 64) {         // the lane's own entries: no other lane writes them
+    const float mt = wl[w][t];
+    wl[w][t] = mt == -INFINITY ? 0.f : exp2f(mt - M);
   }
-  for (; t < cnt; ++t) acc0 += wgt[t] * a.part_o[slot_of[t] * D + c];
-  const float val = ((acc0 + acc1) + (acc2 + acc3)) / tot_l;
-  const int64_t idx = int64_t(i) * a.Hq * D + int64_t(h) * D + c;
-  if (a.mode == ACT_SPLIT) {
-    uint16_t hi, lo;
-    split_h(val, hi, lo);
-    a.out[idx] = hi;
-    a.out[a.lo_off + idx] = lo;
-  } else if (a.mode == ACT_F16_BLOCKED) {
-    // blocked fp16 layout of the tiled W_o launch (K = Hq * D)
-    const int k = h * D + c, R = i & 255, q = (k >> 3) & 3;
+  // the wavefront's LDS writes above precede its reads below in LDS order
+
+  auto orec = [&](int t) { return *reinterpret_cast<const fvec *>(a.part_o + (base + t * stride) * D + c * E); };
+  fvec acc0 = fvec(0.f), acc1 = fvec(0.f), acc2 = fvec(0.f), acc3 = fvec(0.f);
+  const int t0 = WPP > 1 ? w : 0;
+  int t = t0;
+  for (; t + 3 * WPP < cnt; t += 4 * WPP) {
+    const fvec o0 = orec(t), o1 = orec(t + WPP), o2 = orec(t + 2 * WPP), o3 = orec(t + 3 * WPP);
+    acc0 += wl[w][t] * o0;
+    acc1 += wl[w][t + WPP] * o1;
+    acc2 += wl[w][t + 2 * WPP] * o2;
+    acc3 += wl[w][t + 3 * WPP] * o3;
+  }
+  for (; t < cnt; t += WPP) acc0 += wl[w][t] * orec(t);
+  fvec val = (acc0 + acc1) + (acc2 + acc3);
+  if constexpr (WPP > 1) {
+    red[w][c] = val;
+    __syncthreads();
+    if (w != 0) return;
+    val = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
+  }
+  val = val / L;
+
+  const int64_t idx = int64_t(i) * a.Hq * D + int64_t(h) * D + c * E;
+  uint16_t hi[E], lo[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (a.mode == ACT_SPLIT)
+      split_h(val[e], hi[e], lo[e]);
+    else
+      hi[e] = f2h(val[e]);
+  }
+  if (a.mode == ACT_F16_BLOCKED) {
+    // blocked fp16 layout of the tiled W_o launch (K = Hq * D); the lane's E
+    // elements share one 16-B chunk
+    const int k = h * D + c * E, R = i & 255, q = (k >> 3) & 3;
     const int64_t b = (int64_t(i >> 8) * ((a.Hq * D) >> 5) + (k >> 5)) * 8192;
-    a.out[b + R * 32 + ((q ^ ((R >> 1) & 3)) << 3) + (k & 7)] = f2h(val);
+    uint16_t *dst = a.out + b + R * 32 + ((q ^ ((R >> 1) & 3)) << 3) + (k & 7);
+#pragma unroll
+    for (int e = 0; e < E; ++e) dst[e] = hi[e];
   } else {
-    a.out[idx] = f2h(val);
+#pragma unroll
+    for (int e = 0; e < E; ++e) a.out[idx + e] = hi[e];
+    if (a.mode == ACT_SPLIT) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) a.out[a.lo_off + idx + e] = lo[e];
+    }
   }
 }
 
@@ -631,11 +661,22 @@ void launch_attn_mfma(const AttnArgs &a, int n_runs, int D, int max_qblocks, hip
   if (D == 256) eight ? launch_attn_dd<256, 8, 4, 2>(a, n_runs, s) : launch_attn_dd<256, 4, 2, 2>(a, n_runs, s);
 }
 
-void launch_attn_merge(const MergeArgs &a, int n_rows, int D, hipStream_t s) {
-  const dim3 grid(n_rows * a.Hq);
-  if (D == 64) hipLaunchKernelGGL(attn_merge_kernel<64>, grid, dim3(64), 0, s, a);
-  if (D == 128) hipLaunchKernelGGL(attn_merge_kernel<128>, grid, dim3(128), 0, s, a);
-  if (D == 256) hipLaunchKernelGGL(attn_merge_kernel<256>, grid, dim3(256), 0, s, a);
+template <int D>
+static void launch_merge_d(const MergeArgs &a, int pairs, bool many, hipStream_t s) {
+  if (many)
+    hipLaunchKernelGGL((attn_merge_kernel<D, 4>), dim3(pairs), dim3(256), 0, s, a, pairs);
+  else
+    hipLaunchKernelGGL((attn_merge_kernel<D, 1>), dim3((pairs + 3) / 4), dim3(256), 0, s, a, pairs);
+}
+
+// Four wavefronts per (row, query head) once query groups average 16 items
+// or more.
+void launch_attn_merge(const MergeArgs &a, int n_rows, int D, double mean_items, hipStream_t s) {
+  const int pairs = n_rows * a.Hq;
+  const bool many = mean_items >= 16.0;
+  if (D == 64) launch_merge_d<64>(a, pairs, many, s);
+  if (D == 128) launch_merge_d<128>(a, pairs, many, s);
+  if (D == 256) launch_merge_d<256>(a, pairs, many, s);
 }
 
 void launch_attn_f32(const AttnF32Args &a, int n_rows, hipStream_t s) {

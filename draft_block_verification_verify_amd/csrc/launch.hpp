@@ -43,8 +43,8 @@ struct AttnArgs {
 
 struct MergeArgs {
   const float *part_o, *part_ml;
-  const AttnItem *items;
-  const int32_t *group_first, *group_count, *row_tree, *row_local;
+  const AttnGroup *groups;         // [R * Hkv * qg_max]
+  const int32_t *row_tree, *row_local;
   int Hq, Hkv, qg_max;
   int mode;                        // ACT_SPLIT: fp16 hi plane at out, lo at out + lo_off; ACT_F16; ACT_F16_BLOCKED
   int64_t lo_off;
@@ -90,7 +90,7 @@ void launch_rope_bf16(const uint16_t *q, const uint16_t *k, uint16_t *qo, uint16
 void launch_rope_f32(const float *q, const float *k, float *qo, float *ko, const int32_t *row_pos, int n, int Hq,
                      int Hkv, int D, double base, hipStream_t s);
 void launch_attn_mfma(const AttnArgs &a, int n_runs, int D, int max_qblocks, hipStream_t s);
-void launch_attn_merge(const MergeArgs &a, int n_rows, int D, hipStream_t s);
+void launch_attn_merge(const MergeArgs &a, int n_rows, int D, double mean_items, hipStream_t s);
 void launch_attn_f32(const AttnF32Args &a, int n_rows, hipStream_t s);
 
 // ---- projections ----

@@ -97,8 +97,7 @@ MetaLayout meta_layout(int n, int R, int n_draft, int n_items, int n_runs, int n
   L.tree_kv_off = take(8 * size_t(R));
   L.items = take(sizeof(AttnItem) * size_t(std::max(n_items, 1)));
   L.runs = take(sizeof(AttnRun) * size_t(std::max(n_runs, 1)));
-  L.group_first = take(4 * size_t(n_groups));
-  L.group_count = take(4 * size_t(n_groups));
+  L.groups = take(sizeof(AttnGroup) * size_t(std::max(n_groups, 1)));
   L.total = o;
   return L;
 }
@@ -285,14 +284,18 @@ int build_plan(const Dims &dm, const HostInputs &in, int64_t slot_cap, int targe
   }
   P.chunk = int32_t(chunk * KT);
   const int n_groups = P.R * dm.Hkv * P.qg_max;
-  P.group_first.assign(n_groups, 0);
-  P.group_count.assign(n_groups, 0);
+  P.groups.assign(n_groups, AttnGroup{0, 0, 0, 0});
   P.runs.assign(size_t(ceil_div(total, chunk)), AttnRun{0, 0, 0, 0});
   int64_t slot = 0;
   for_each_item(chunk, [&](int r, int g, int qg, int m0, int nq, int64_t t0, int64_t t1, int64_t run) {
     const int gi = (r * dm.Hkv + g) * P.qg_max + qg;
-    if (P.group_count[gi] == 0) P.group_first[gi] = int32_t(P.items.size());
-    ++P.group_count[gi];
+    AttnGroup &Gr = P.groups[gi];
+    if (Gr.count == 0) {
+      Gr.first = int32_t(P.items.size());
+      Gr.slot = int32_t(slot);
+      Gr.nq = nq;
+    }
+    ++Gr.count;
     AttnRun &R = P.runs[size_t(run)];
     if (R.count == 0) R.first = int32_t(P.items.size());
     ++R.count;
@@ -343,8 +346,7 @@ void pack_plan(const Plan &p, int Hkv, void *dst, MetaLayout *lay) {
   put(L.tree_kv_off, p.tree_kv_off.data(), 8 * size_t(p.R));
   put(L.items, p.items.data(), sizeof(AttnItem) * p.items.size());
   put(L.runs, p.runs.data(), sizeof(AttnRun) * p.runs.size());
-  put(L.group_first, p.group_first.data(), 4 * size_t(n_groups));
-  put(L.group_count, p.group_count.data(), 4 * size_t(n_groups));
+  put(L.groups, p.groups.data(), sizeof(AttnGroup) * size_t(n_groups));
   *lay = L;
 }
 

@@ -55,6 +55,14 @@ struct AttnRun {
 };
 static_assert(sizeof(AttnRun) == 16, "AttnRun layout");
 
+// One query group for the merge: its items [first, first + count) (in
+// order), the partial slot of its first item's first query and its query
+// count nq; item t's record for query mi sits at slot + t * nq + mi.
+struct AttnGroup {
+  int32_t first, count, slot, nq;
+};
+static_assert(sizeof(AttnGroup) == 16, "AttnGroup layout");
+
 struct HostInputs {
   int32_t n_rows, n_roots;
   const int32_t *parent, *pos;
@@ -79,7 +87,7 @@ struct Plan {
   std::vector<AttnItem> items;        // in query-group order
   std::vector<AttnRun> runs;          // one per attention workgroup
   int32_t qg_max = 1;                 // query groups per (tree, g)
-  std::vector<int32_t> group_first, group_count;   // [R * Hkv * qg_max], into items
+  std::vector<AttnGroup> groups;      // [R * Hkv * qg_max]
   int32_t chunk = 0;                  // keys per run (the last run shorter)
   int64_t slots = 0;                  // partial (m, l, o) records needed
 };
@@ -103,7 +111,7 @@ int64_t slot_capacity(const Dims &dm);
 struct MetaLayout {
   size_t row_tree, row_local, row_pos, row_parent, row_draft, row_anc, row_child, draft_row;
   size_t tree_start, tree_rows, tree_kv_len, tree_kv_off;
-  size_t items, runs, group_first, group_count;
+  size_t items, runs, groups;
   size_t total;
 };
 MetaLayout meta_layout(int n, int R, int n_draft, int n_items, int n_runs, int n_groups);
