@@ -65,8 +65,10 @@ int check_dims(const Dims &dm, std::string *err) {
   return P_OK;
 }
 
+// Up to 64 partial records per query vector, at least 16 Ki and at most
+// 384 Ki records ((d + 2) floats each).
 int64_t slot_capacity(const Dims &dm) {
-  int64_t s = int64_t(24) * dm.Hq * dm.max_rows;
+  int64_t s = int64_t(64) * dm.Hq * dm.max_rows;
   return std::min<int64_t>(393216, std::max<int64_t>(16384, s));
 }
 
@@ -246,12 +248,16 @@ int build_plan(const Dims &dm, const HostInputs &in, int64_t slot_cap, int targe
   // group's tiles only in part shares that group with its neighbours; each
   // (run, group) pair is one work item.  Each item writes nq partial records
   // of (d + 2) floats: keep the run at least 4 * nq keys long, so that the
-  // records stay below half of the K + V bytes a run reads; keep a group's
-  // items within kMaxSplits; aim for `target_items` runs.
+  // records stay below half of the K + V bytes a run reads, unless that
+  // leaves fewer than target_items / 2 runs (one per compute unit: small,
+  // latency-bound batches gain more from the parallelism than the records
+  // cost); keep a group's items within kMaxSplits; aim for `target_items`
+  // runs.
   int64_t max_tiles = 1;
   for (int r = 0; r < P.R; ++r) max_tiles = std::max(max_tiles, tiles[r]);
-  int64_t chunk = std::max<int64_t>({ceil_div(64, KT), ceil_div(4 * int64_t(mq_max), KT),
-                                     ceil_div(total, std::max(target_items, 1)),
+  const int64_t rec_chunk = std::min(ceil_div(4 * int64_t(mq_max), KT),
+                                     std::max<int64_t>(1, total / std::max(target_items / 2, 1)));
+  int64_t chunk = std::max<int64_t>({ceil_div(64, KT), rec_chunk, ceil_div(total, std::max(target_items, 1)),
                                      ceil_div(max_tiles, kMaxSplits - 1)});   // in tiles
   auto for_each_item = [&](int64_t ch, auto &&fn) {
     // fn(r, g, qg, m0, nq, tile0, tile1, run) for every work item in order
