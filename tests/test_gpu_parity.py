@@ -57,6 +57,9 @@ MINIS = {
     "c4m": mini(4, hidden=256, vocab=2048, stem=300, w_lm_std=0.08),
     "c5m": mini(5, hidden=512, vocab=4104, min_len=0, max_len=400, w_lm_std=0.06),
     "c5s": mini(5, hidden=384, vocab=3000, n_seqs=5, min_len=3, max_len=200, w_lm_std=0.06),
+    # many tiny trees: attention runs that hold several whole query groups,
+    # 768 rows (three 256-row blocks of the blocked activation layouts)
+    "c5t": mini(5, hidden=384, vocab=3000, n_seqs=96, min_len=0, max_len=60, w_lm_std=0.06),
 }
 
 
