@@ -28,6 +28,10 @@ METRIC = "verify rows/s (attn+LM-head+accept) γ=7, 27B shape; step ms; % of roo
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+# A GPU that has been idle (input generation takes seconds on the host) runs
+# the first tens of milliseconds of load below its working clocks: before the
+# warmup steps, the step runs untimed for at least this long.
+SETTLE_S = 0.5
 COUNTERS = os.path.join(ROOT, "profiles", "lm_head_counters.json")
 GEMM_SRC = [os.path.join(ROOT, "draft_block_verification_verify_amd", "csrc", f)
             for f in ("k_gemm.hip", "k_dma.hpp", "k_common.hpp")]
@@ -171,6 +175,7 @@ def bench_rounds(args, cfg) -> int:
             got.append(acc)
         return got
 
+    settle(dc.run)
     reset()
     replay()                                   # warmup
     reset()
@@ -284,6 +289,7 @@ def bench_schedule(args, cfg) -> int:
         out = dc.results()
         return ms, int(out["accept_len"].sum()), sub.st.n_rows, out["accept_len"]
 
+    settle(full.run)
     curve_g = [0, 1, 2, 3, 5, 7]
     curve = []
     for g in curve_g:
@@ -324,6 +330,18 @@ def bench_schedule(args, cfg) -> int:
     }
     print(json.dumps(res))
     return 0
+
+
+def settle(step) -> None:
+    """Run `step` untimed, one at a time, for at least SETTLE_S seconds."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < SETTLE_S:
+        step()
+        torch.cuda.synchronize()
+        n += 1
+    log(f"[bench] settled: {n} untimed steps in {time.perf_counter() - t0:.2f} s")
 
 
 def main() -> int:
@@ -390,6 +408,7 @@ def main() -> int:
         dc.set_uniforms(W.make_uniforms(inp))
     dc.refresh()
 
+    settle(dc.run)
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         dc.run()
