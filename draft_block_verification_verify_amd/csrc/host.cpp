@@ -63,6 +63,7 @@ struct sv_handle {
   void *q_rot = nullptr, *k_rot = nullptr, *o_act = nullptr, *hn = nullptr;
   float *part_o = nullptr, *part_ml = nullptr, *h_part = nullptr, *logits = nullptr;
   float *t_max = nullptr, *t_sum = nullptr, *lse_q = nullptr, *opart = nullptr;
+  uint16_t *p16 = nullptr;         // tiled LM head: fp16 tile-relative probabilities
   int32_t *t_arg = nullptr;
   float2 *dpart = nullptr;
   int64_t slot_cap = 0;
@@ -201,6 +202,7 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
   // layout of the tiled LM head (rows padded to 256)
   A(&h->hn, std::max<size_t>(size_t(R * H * 4), size_t(sv::blocked_elems(R, H) * 2)));
   A(&h->logits, size_t(R * V * 4));
+  if (dm.dtype == SV_BF16 && R > 64 && V % 8 == 0) A(&h->p16, size_t(R * V * 2));
   A(&h->t_max, size_t(R * h->n_tiles_cap * 4));
   A(&h->t_sum, size_t(R * h->n_tiles_cap * 4));
   A(&h->t_arg, size_t(R * h->n_tiles_cap * 4));
@@ -466,6 +468,12 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   va.drafter = in->drafter_logits;
   va.drafter_bf16 = bf16 ? 1 : 0;
   va.logits = logits;
+  // Without a caller logits buffer (and outside T = 1 mode, whose draw reads
+  // the logits), the tiled LM head stores each tile's probabilities relative
+  // to the tile maximum in fp16 instead of fp32 logits: half the bytes for
+  // the overlap pass, the only reader.
+  const bool use_p16 = bf16 && !fp8 && n > 64 && !out->logits && in->mode != SV_MODE_SAMPLE && h->p16 != nullptr;
+  va.p16 = use_p16 ? h->p16 : nullptr;
   va.t_max = h->t_max;
   va.t_sum = h->t_sum;
   va.t_arg = h->t_arg;
@@ -576,6 +584,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     l.t_sum = h->t_sum;
     l.t_arg = h->t_arg;
     l.n_tiles = n_tiles;
+    l.p16 = use_p16 ? h->p16 : nullptr;
     begin("lm_head");
     if (fp8) {
       l.W8 = h->w_lm8;

@@ -56,6 +56,10 @@ __device__ __forceinline__ void st_q(uint16_t *p, int64_t lo_off, double v) {
 }
 __device__ __forceinline__ void st_q(float *p, int64_t, double v) { *p = float(v); }
 
+// One thread per (row, head, pair): grid (rows, ceil(heads * d/2 / 256)).
+// Each workgroup first builds the row's sine/cosine table (d/2 <= 128
+// entries), so every thread then does one load pair, one rotation and one
+// store pair, with no chain of dependent memory accesses.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_rows_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                         T *__restrict__ q_out, T *__restrict__ k_out,
@@ -65,32 +69,32 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(const T *__restrict__ q,
   const int i = blockIdx.x;
   const int half = D / 2;
   const int heads = Hq + Hkv;
+  const int p = blockIdx.y * blockDim.x + threadIdx.x;
+  const bool active = p < heads * half;
+  const int hh = active ? p / half : 0, kk = p % half;
+  // issue this thread's loads before the table's arithmetic
+  const T *src = hh < Hq ? q + (int64_t(i) * Hq + hh) * D : k + (int64_t(i) * Hkv + (hh - Hq)) * D;
+  double a = 0.0, b = 0.0;
+  if (active) {
+    a = ld(src + kk);
+    b = ld(src + kk + half);
+  }
   const double pos = double(row_pos[i]);
-  for (int kk = threadIdx.x; kk < half; kk += blockDim.x) {
-    const double theta = pow(base, -2.0 * double(kk) / double(D));
-    sincos(pos * theta, &sn[kk], &cs[kk]);
+  if (threadIdx.x < half) {
+    const double theta = pow(base, -2.0 * double(threadIdx.x) / double(D));
+    sincos(pos * theta, &sn[threadIdx.x], &cs[threadIdx.x]);
   }
   __syncthreads();
-  for (int p = threadIdx.x; p < heads * half; p += blockDim.x) {
-    const int hh = p / half, kk = p % half;
-    const T *src;
-    T *dst;
-    if (hh < Hq) {
-      src = q + (int64_t(i) * Hq + hh) * D;
-      dst = q_out + (int64_t(i) * Hq + hh) * D;
-    } else {
-      src = k + (int64_t(i) * Hkv + (hh - Hq)) * D;
-      dst = k_out + (int64_t(i) * Hkv + (hh - Hq)) * D;
-    }
-    const double c = cs[kk], s = sn[kk];
-    const double a = ld(src + kk), b = ld(src + kk + half);
-    if (hh < Hq) {
-      st_q(dst + kk, q_lo_off, a * c - b * s);
-      st_q(dst + kk + half, q_lo_off, b * c + a * s);
-    } else {
-      st(dst + kk, a * c - b * s);
-      st(dst + kk + half, b * c + a * s);
-    }
+  if (!active) return;
+  const double c = cs[kk], s = sn[kk];
+  if (hh < Hq) {
+    T *dst = q_out + (int64_t(i) * Hq + hh) * D;
+    st_q(dst + kk, q_lo_off, a * c - b * s);
+    st_q(dst + kk + half, q_lo_off, b * c + a * s);
+  } else {
+    T *dst = k_out + (int64_t(i) * Hkv + (hh - Hq)) * D;
+    st(dst + kk, a * c - b * s);
+    st(dst + kk + half, b * c + a * s);
   }
 }
 
@@ -633,13 +637,15 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
 
 void launch_rope_bf16(const uint16_t *q, const uint16_t *k, uint16_t *qo, uint16_t *ko, const int32_t *row_pos,
                       int n, int Hq, int Hkv, int D, double base, int64_t q_lo_off, hipStream_t s) {
-  hipLaunchKernelGGL(rope_rows_kernel<uint16_t>, dim3(n), dim3(256), 0, s, q, k, qo, ko, row_pos, Hq, Hkv, D, base,
+  const dim3 grid(n, (Hq + Hkv) * (D / 2) / 256 + ((Hq + Hkv) * (D / 2) % 256 != 0));
+  hipLaunchKernelGGL(rope_rows_kernel<uint16_t>, grid, dim3(256), 0, s, q, k, qo, ko, row_pos, Hq, Hkv, D, base,
                      q_lo_off);
 }
 
 void launch_rope_f32(const float *q, const float *k, float *qo, float *ko, const int32_t *row_pos, int n, int Hq,
                      int Hkv, int D, double base, hipStream_t s) {
-  hipLaunchKernelGGL(rope_rows_kernel<float>, dim3(n), dim3(256), 0, s, q, k, qo, ko, row_pos, Hq, Hkv, D, base,
+  const dim3 grid(n, (Hq + Hkv) * (D / 2) / 256 + ((Hq + Hkv) * (D / 2) % 256 != 0));
+  hipLaunchKernelGGL(rope_rows_kernel<float>, grid, dim3(256), 0, s, q, k, qo, ko, row_pos, Hq, Hkv, D, base,
                      int64_t(0));
 }
 

@@ -69,6 +69,33 @@ __device__ __forceinline__ void store_tile(const GemmArgs &g, const f32x16 (&acc
   }
 }
 
+// fp16 exp(acc - m[t]) for the lane's values: the tile's probabilities
+// relative to the tile maximum of each token (g.N % 8 == 0, so every group of
+// four consecutive columns is whole and 8-byte aligned).
+template <int NV, int NT>
+__device__ __forceinline__ void store_tile_p16(const GemmArgs &g, const f32x16 (&acc)[NV][NT], const int (&nb)[NV],
+                                               const int (&tb)[NT], const float (&m)[NT], int lane) {
+  const int r32 = lane & 31, kg = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int tok = tb[t] + r32;
+    if (tok >= g.rows) continue;
+    uint16_t *orow = g.p16 + int64_t(tok) * g.ldo;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n0 = nb[v] + 8 * q + 4 * kg;
+        if (n0 >= g.N) continue;
+        uint32_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = f2h(__expf(acc[v][t][4 * q + e] - m[t]));
+        *reinterpret_cast<uint2 *>(orow + n0) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      }
+    }
+  }
+}
+
 // Per-lane (max, sumexp, argmax) over the lane's N values of token block t,
 // merged with the partner lane (l ^ 32) holding the other N rows.  CHECK
 // masks columns n >= N (only the last tile of a launch needs it).
@@ -421,8 +448,22 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
         g.t_sum[o] = r.s;
         g.t_arg[o] = r.i;
       }
+      if (g.p16) {
+        // tile maximum of each of the lane's two tokens (the value the merge
+        // above writes to t_max)
+        float m[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int row = wt * 64 + t * 32 + r32;
+          m[t] = fmaxf(red[0][row].m, red[1][row].m);
+        }
+        store_tile_p16<4, 2>(g, acc, nb, tb, m, lane);
+      } else {
+        store_tile<4, 2>(go, acc, nb, tb, lane);
+      }
+    } else {
+      store_tile<4, 2>(go, acc, nb, tb, lane);
     }
-    store_tile<4, 2>(go, acc, nb, tb, lane);
 
     int next = tile + gridDim.x;
     while (next < n_tiles_all && !valid(next)) next += gridDim.x;

@@ -169,7 +169,24 @@ __global__ __launch_bounds__(256) void overlap_partial_kernel(VocabArgs a) {
   const int64_t qrow = int64_t(t) * a.V;
   const int lo = c * a.ochunk, hi = min(a.V, lo + a.ochunk);
   float s = 0.f;
-  if ((a.V % 8) == 0) {
+  if (a.p16) {
+    // p_j(u) = p16(u) * exp(t_max - lse) within each 256-token tile of the
+    // LM head (the host takes this path only when V % 8 == 0)
+    const uint16_t *pp = a.p16 + int64_t(j) * a.V;
+    const float *tm = a.t_max + int64_t(j) * a.n_tiles;
+    for (int u = lo + tid * 8; u < hi; u += 256 * 8) {
+      float b[8];
+      load8(a.drafter, a.drafter_bf16, qrow + u, b);
+      const uint4 h = *reinterpret_cast<const uint4 *>(pp + u);
+      const float sc = __expf(tm[u >> 8] - A);
+      const uint32_t w[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = h2f(uint16_t((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu))) * sc;
+        s += fminf(p, __expf(b[e] - B));
+      }
+    }
+  } else if ((a.V % 8) == 0) {
     for (int u = lo + tid * 8; u < hi; u += 256 * 8) {
       float b[8];
       load8(a.drafter, a.drafter_bf16, qrow + u, b);

@@ -79,6 +79,9 @@ struct GemmArgs {
   float *t_max, *t_sum;
   int32_t *t_arg;
   int n_tiles;
+  // tiled LM head: when non-null, the tile's probabilities relative to its
+  // maximum, exp(l - t_max), as fp16 [rows, ldo], replace the fp32 logits
+  uint16_t *p16;
   // FP8 LM head: e4m3 operands in the blocked layout and their row scales
   const uint8_t *W8, *act8;
   const float *w_scale, *a_scale;
@@ -133,6 +136,8 @@ struct VocabArgs {
   const void *drafter;          // [n_draft, V] bf16 or f32
   int drafter_bf16;
   const float *logits;          // [n, V] fp32
+  // [n, V] fp16 exp(l - t_max) per 256-token tile (null: read `logits`)
+  const uint16_t *p16;
   const float *t_max, *t_sum;
   const int32_t *t_arg;
   int n_tiles;

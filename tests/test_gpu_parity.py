@@ -109,6 +109,32 @@ def test_parity_small(name, seed):
     _record(f"{name}/seed{seed}", rep)
 
 
+@pytest.mark.parametrize("name", ["c4m", "c5m", "c5t", "c2m"])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_parity_without_logits_buffer(name, seed):
+    # No caller logits buffer: above 64 rows the LM head then keeps fp16
+    # tile-relative probabilities for the overlap pass instead of fp32 logits
+    # (the path the benchmark times); every output is held to the same rules.
+    cfg = MINIS[name]
+    inp, ref, gpu = run_case(cfg, seed, with_logits=False)
+    rep = {}
+    P.check_self_consistency(inp.st.parent, inp.draft_ids, gpu)
+    P.compare(ref, gpu, inp.st.parent, inp.draft_ids, logits_ref=ref["logits"], report=rep)
+    _record(f"{name}/seed{seed}/no-logits", rep)
+
+
+@pytest.mark.parametrize("name,sigma", [("c5m", 0.6), ("c4m", 0.3)])
+def test_overlap_without_logits_buffer_correlated_drafter(name, sigma):
+    # overlaps far from zero (a drafter close to the target) on the fp16
+    # probability path
+    inp, ref, gpu = run_case(MINIS[name], 0, drafter=sigma, with_logits=False)
+    rep = {}
+    P.compare(ref, gpu, inp.st.parent, inp.draft_ids, logits_ref=ref["logits"], report=rep)
+    _record(f"{name}/drafter{sigma}/no-logits", rep)
+    rows = [i for i in range(len(inp.st.parent)) if inp.st.parent[i] >= 0]
+    assert np.mean(ref["overlap"][rows]) > 0.3
+
+
 @pytest.mark.parametrize("name,sigma", [("c2m", 0.4), ("c5m", 0.6), ("c4m", 0.3), ("c1", 0.5)])
 def test_parity_correlated_drafter(name, sigma):
     # q = target logits + noise: overlaps ~0.8, survival far from zero
@@ -355,8 +381,8 @@ def test_sample_mode_refuses_branching_and_bad_mode():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("cfg_id", [2, 3, 4, 5])
-def test_parity_full_size_sampled(cfg_id):
+@pytest.mark.parametrize("cfg_id,with_logits", [(2, True), (3, True), (4, True), (5, True), (4, False), (5, False)])
+def test_parity_full_size_sampled(cfg_id, with_logits):
     from draft_block_verification_verify_amd.runner import DeviceCase
     cfg = W.CONFIGS[cfg_id]
     _say(f"[full] generating {cfg.name}")
@@ -374,17 +400,17 @@ def test_parity_full_size_sampled(cfg_id):
         g = np.where(g < 0, 0, g)
         W.plant_chain_drafts(inp, g)
     ref = O.verify(cd, O.inp_dict(inp), trees=trees, keep_logits=True)
-    _say("[full] gpu run")
-    dc = DeviceCase(inp, with_logits=True)
+    _say(f"[full] gpu run (logits buffer: {with_logits})")
+    dc = DeviceCase(inp, with_logits=with_logits)
     dc.run()
     gpu = dc.results()
     dc.close()
     P.check_self_consistency(st.parent, inp.draft_ids, gpu)
     rows = [int(i) for i in ref["rows"]]
     rep = {}
-    P.compare(ref, gpu, st.parent, inp.draft_ids, rows=rows, logits_ref=ref["logits"], logits_gpu=gpu["logits"],
-              report=rep)
-    _record(f"{cfg.name}/full-sampled", rep)
+    P.compare(ref, gpu, st.parent, inp.draft_ids, rows=rows, logits_ref=ref["logits"],
+              logits_gpu=gpu["logits"] if with_logits else None, report=rep)
+    _record(f"{cfg.name}/full-sampled" + ("" if with_logits else "/no-logits"), rep)
 
 
 @pytest.mark.parametrize("seed", [0, 1])
