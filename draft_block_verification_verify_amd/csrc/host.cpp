@@ -505,13 +505,21 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   const int64_t h_lo = int64_t(dm.max_rows) * H;
 
   if (bf16) {
-    begin("rope");
-    sv::launch_rope_bf16(static_cast<const uint16_t *>(in->q_rows), static_cast<const uint16_t *>(in->k_rows),
-                         static_cast<uint16_t *>(h->q_rot), static_cast<uint16_t *>(h->k_rot), row_pos, n, int(Hq),
-                         int(Hkv), int(D), double(h->cfg.rope_base), q_lo, stream);
-    end();
-    begin("drafter_stats");
-    sv::launch_drafter_partial(va, stream);
+    sv::RopeArgs ra{};
+    ra.q = static_cast<const uint16_t *>(in->q_rows);
+    ra.k = static_cast<const uint16_t *>(in->k_rows);
+    ra.q_out = static_cast<uint16_t *>(h->q_rot);
+    ra.k_out = static_cast<uint16_t *>(h->k_rot);
+    ra.row_pos = row_pos;
+    ra.Hq = int(Hq);
+    ra.Hkv = int(Hkv);
+    ra.D = int(D);
+    ra.base = double(h->cfg.rope_base);
+    ra.q_lo_off = q_lo;
+    ra.n = n;
+    ra.ry = int(ceil_div(int64_t(Hq + Hkv) * (D / 2), 256));
+    begin("rope_drafter_stats");
+    sv::launch_rope_drafter_bf16(ra, va, stream);
     end();
     sv::AttnArgs aa{};
     aa.kv_k = static_cast<const uint16_t *>(in->kv_k);

@@ -22,80 +22,18 @@
 // fp32 path: one workgroup per (row, query head), plain fp32 arithmetic.
 #include "k_common.hpp"
 #include "k_dma.hpp"
+#include "k_rope.hpp"
 #include "launch.hpp"
 
 namespace sv {
 
-// ----------------------------------------------------------------------------
-// RoPE of the row queries and keys at their semantic positions: pair k couples
-// components k and k + d/2 and turns by pos * base^(-2k/d).  Angles, sines and
-// cosines in fp64; the rotated values are rounded once to the output type.
-// ----------------------------------------------------------------------------
-
-template <typename T>
-__device__ __forceinline__ double ld(const T *p);
-template <>
-__device__ __forceinline__ double ld<uint16_t>(const uint16_t *p) { return double(bf2f(*p)); }
-template <>
-__device__ __forceinline__ double ld<float>(const float *p) { return double(*p); }
-
-template <typename T>
-__device__ __forceinline__ void st(T *p, double v);
-template <>
-__device__ __forceinline__ void st<uint16_t>(uint16_t *p, double v) { *p = f2bf(float(v)); }
-template <>
-__device__ __forceinline__ void st<float>(float *p, double v) { *p = float(v); }
-
-// bf16 queries are written as a hi plane (q_out) and a lo plane
-// (q_out + q_lo_off) with hi + lo = rotated value to about 16 bits.
-__device__ __forceinline__ void st_q(uint16_t *p, int64_t lo_off, double v) {
-  uint16_t hi, lo;
-  split_bf(float(v), hi, lo);
-  p[0] = hi;
-  p[lo_off] = lo;
-}
-__device__ __forceinline__ void st_q(float *p, int64_t, double v) { *p = float(v); }
-
-// One thread per (row, head, pair): grid (rows, ceil(heads * d/2 / 256)).
-// Each workgroup first builds the row's sine/cosine table (d/2 <= 128
-// entries), so every thread then does one load pair, one rotation and one
-// store pair, with no chain of dependent memory accesses.
+// RoPE launch: grid (rows, ceil(heads * d/2 / 256)); device code in k_rope.hpp.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_rows_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                         T *__restrict__ q_out, T *__restrict__ k_out,
                                                         const int32_t *__restrict__ row_pos, int Hq,
                                                         int Hkv, int D, double base, int64_t q_lo_off) {
-  __shared__ double cs[128], sn[128];   // cos, sin of pos * theta_k, k < D/2 <= 128
-  const int i = blockIdx.x;
-  const int half = D / 2;
-  const int heads = Hq + Hkv;
-  const int p = blockIdx.y * blockDim.x + threadIdx.x;
-  const bool active = p < heads * half;
-  const int hh = active ? p / half : 0, kk = p % half;
-  // issue this thread's loads before the table's arithmetic
-  const T *src = hh < Hq ? q + (int64_t(i) * Hq + hh) * D : k + (int64_t(i) * Hkv + (hh - Hq)) * D;
-  double a = 0.0, b = 0.0;
-  if (active) {
-    a = ld(src + kk);
-    b = ld(src + kk + half);
-  }
-  const double pos = double(row_pos[i]);
-  if (threadIdx.x < half) {
-    const double theta = pow(base, -2.0 * double(threadIdx.x) / double(D));
-    sincos(pos * theta, &sn[threadIdx.x], &cs[threadIdx.x]);
-  }
-  __syncthreads();
-  if (!active) return;
-  const double c = cs[kk], s = sn[kk];
-  if (hh < Hq) {
-    T *dst = q_out + (int64_t(i) * Hq + hh) * D;
-    st_q(dst + kk, q_lo_off, a * c - b * s);
-    st_q(dst + kk + half, q_lo_off, b * c + a * s);
-  } else {
-    T *dst = k_out + (int64_t(i) * Hkv + (hh - Hq)) * D;
-    st(dst + kk, a * c - b * s);
-    st(dst + kk + half, b * c + a * s);
-  }
+  rope_rows_block<T>(q, k, q_out, k_out, row_pos, Hq, Hkv, D, base, q_lo_off, blockIdx.x, blockIdx.y);
 }
 
 // ----------------------------------------------------------------------------

@@ -1,7 +1,9 @@
 // Vocabulary-wide reductions and acceptance for the verify step (gfx950).
 //
 //  drafter_partial  (max, sum exp) of every drafter-logit row, per chunk
-//                   (coalesced 16-B streaming of the bf16 rows).
+//                   (coalesced 16-B streaming of the bf16 rows); for bf16
+//                   models in one launch with the RoPE of the rows
+//                   (rope_drafter).
 //  row_combine      per row: max, logsumexp and greedy token of the target
 //                   from the LM-head tile records; per draft row: log Z of q.
 //  overlap_partial  per draft row i with parent j and per vocabulary chunk:
@@ -17,6 +19,7 @@
 //                   per draft and the inverse-CDF draw of the bonus token.
 // Every reduction runs in a fixed order, so repeated runs are bit-identical.
 #include "k_common.hpp"
+#include "k_rope.hpp"
 #include "launch.hpp"
 
 namespace sv {
@@ -76,8 +79,9 @@ __device__ __forceinline__ float load1(const void *base, int bf16, int64_t idx) 
 
 constexpr int kDrafterChunk = 8192;   // the host's drafter-stats chunk (vocabulary values per workgroup)
 
-__global__ __launch_bounds__(256) void drafter_partial_kernel(VocabArgs a) {
-  const int c = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+// (max, sum exp) of chunk c of drafter row t, by one 256-thread workgroup
+__device__ __forceinline__ void drafter_partial_block(const VocabArgs &a, int c, int t) {
+  const int tid = threadIdx.x;
   const int lo = c * a.dchunk, hi = min(a.V, lo + a.dchunk);
   const int64_t row = int64_t(t) * a.V;
   const bool vec = (a.V % 8) == 0;
@@ -126,6 +130,26 @@ __global__ __launch_bounds__(256) void drafter_partial_kernel(VocabArgs a) {
   if (m == -INFINITY) s = 0.f;
   const MaxSum r = ms_block256(MaxSum{m, s});
   if (tid == 0) a.dpart[int64_t(t) * a.n_dch + c] = make_float2(r.m, r.s);
+}
+
+__global__ __launch_bounds__(256) void drafter_partial_kernel(VocabArgs a) {
+  drafter_partial_block(a, blockIdx.x, blockIdx.y);
+}
+
+// RoPE of the rows and the drafter statistics in one launch (independent
+// work: the first is fp64 arithmetic on little data, the second a stream of
+// the drafter logits, so they overlap).  Workgroups [0, n * ry) rotate row
+// b / ry, pairs of block b % ry; the rest take drafter chunks.
+__global__ __launch_bounds__(256) void rope_drafter_kernel(RopeArgs r, VocabArgs a) {
+  const int b = blockIdx.x;
+  const int nr = r.n * r.ry;
+  if (b < nr) {
+    rope_rows_block<uint16_t>(r.q, r.k, r.q_out, r.k_out, r.row_pos, r.Hq, r.Hkv, r.D, r.base, r.q_lo_off, b / r.ry,
+                              b % r.ry);
+  } else {
+    const int d = b - nr;
+    drafter_partial_block(a, d % a.n_dch, d / a.n_dch);
+  }
 }
 
 __global__ __launch_bounds__(256) void row_combine_kernel(VocabArgs a) {
@@ -485,6 +509,11 @@ void launch_sample(const VocabArgs &a, const SampleArgs &sa, hipStream_t s) {
   hipLaunchKernelGGL(swalk_kernel, dim3(a.R), dim3(64), 0, s, a, sa);
   hipLaunchKernelGGL(residual_partial_kernel, dim3(a.n_och, a.R), dim3(256), 0, s, a, sa);
   hipLaunchKernelGGL(sample_kernel, dim3(a.R), dim3(256), 0, s, a, sa);
+}
+
+void launch_rope_drafter_bf16(const RopeArgs &r, const VocabArgs &a, hipStream_t s) {
+  const int blocks = r.n * r.ry + a.n_dch * a.n_draft;
+  hipLaunchKernelGGL(rope_drafter_kernel, dim3(blocks), dim3(256), 0, s, r, a);
 }
 
 void launch_drafter_partial(const VocabArgs &a, hipStream_t s) {

@@ -177,6 +177,18 @@ struct CommitArgs {
 void launch_commit(const CommitArgs &a, int n_roots, hipStream_t s);
 
 void launch_drafter_partial(const VocabArgs &a, hipStream_t s);
+// bf16 RoPE of the rows (as launch_rope_bf16) and the drafter statistics (as
+// launch_drafter_partial) in one launch; ry = ceil((Hq + Hkv) * D / 2 / 256).
+struct RopeArgs {
+  const uint16_t *q, *k;
+  uint16_t *q_out, *k_out;
+  const int32_t *row_pos;
+  int Hq, Hkv, D;
+  double base;
+  int64_t q_lo_off;
+  int n, ry;
+};
+void launch_rope_drafter_bf16(const RopeArgs &r, const VocabArgs &a, hipStream_t s);
 void launch_row_combine(const VocabArgs &a, hipStream_t s);
 void launch_overlap_partial(const VocabArgs &a, hipStream_t s);
 void launch_accept(const VocabArgs &a, hipStream_t s);
