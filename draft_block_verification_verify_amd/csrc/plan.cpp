@@ -252,12 +252,16 @@ int build_plan(const Dims &dm, const HostInputs &in, int64_t slot_cap, int targe
   // leaves fewer than target_items / 2 runs (one per compute unit: small,
   // latency-bound batches gain more from the parallelism than the records
   // cost); keep a group's items within kMaxSplits; aim for `target_items`
-  // runs.
+  // runs, and no more runs than workgroups the launch keeps resident
+  // (target_items for four-wave workgroups, two per compute unit; half as
+  // many for the eight-wave launch of groups with more than 64 query vectors,
+  // one per compute unit), so that no compute unit takes a second round.
   int64_t max_tiles = 1;
   for (int r = 0; r < P.R; ++r) max_tiles = std::max(max_tiles, tiles[r]);
-  const int64_t rec_chunk = std::min(ceil_div(4 * int64_t(mq_max), KT),
-                                     std::max<int64_t>(1, total / std::max(target_items / 2, 1)));
-  int64_t chunk = std::max<int64_t>({ceil_div(64, KT), rec_chunk, ceil_div(total, std::max(target_items, 1)),
+  const int64_t per_cu = std::max(target_items / 2, 1);
+  const int64_t resident = mq_max > 64 ? per_cu : std::max(target_items, 1);
+  const int64_t rec_chunk = std::min(ceil_div(4 * int64_t(mq_max), KT), std::max<int64_t>(1, total / per_cu));
+  int64_t chunk = std::max<int64_t>({ceil_div(64, KT), rec_chunk, ceil_div(total, resident),
                                      ceil_div(max_tiles, kMaxSplits - 1)});   // in tiles
   auto for_each_item = [&](int64_t ch, auto &&fn) {
     // fn(r, g, qg, m0, nq, tile0, tile1, run) for every work item in order

@@ -203,6 +203,25 @@ def test_plan_coarsens_split_to_fit_slot_capacity(plan_lib):
         assert 1 <= sum(1 for it in items if it[1] == g) <= 2
 
 
+def test_plan_runs_fit_resident_workgroups(plan_lib):
+    # one 17-row chain at 27B shape: 102 query vectors per group take the
+    # eight-wave attention launch (one workgroup per compute unit), so the
+    # 4 x 257 tiles are cut into at most target / 2 runs (one round); 8-row
+    # chains (32 query vectors, four-wave launch) may use up to target runs
+    parent = [-1] + list(range(16))
+    dims = [24, 4, 256, 5120, 248320, 1, 17, 1, 64, 1 << 20]
+    st, err, stats, _, items = plan(plan_lib, dims, parent, np.arange(17) + 8192, [0], [8192], 8192, target=512)
+    assert st == 0, err
+    assert stats[8] <= 256
+    KT = 32
+    assert stats[8] == -(-(4 * 257) // (stats[4] // KT))
+    parent8 = [-1] + list(range(7))
+    dims8 = [32, 8, 128, 4096, 151936, 1, 8, 1, 64, 1 << 20]
+    st, err, stats8, _, _ = plan(plan_lib, dims8, parent8, np.arange(8) + 4096, [0], [4096], 4096, target=512)
+    assert st == 0, err
+    assert 256 < stats8[8] <= 512
+
+
 def test_plan_caps_splits_per_group(plan_lib):
     # one long prefix and a huge work-item target: the split count per
     # (tree, KV head, query group) stays within what the merge handles
