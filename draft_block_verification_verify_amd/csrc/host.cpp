@@ -451,7 +451,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
 
   float *logits = out->logits ? out->logits : h->logits;
   const bool fp8 = dm.weight_format == SV_WEIGHTS_FP8;
-  const int tile_w = bf16 && !fp8 ? sv::lm_tile_width(n) : 256;
+  const int tile_w = bf16 && !fp8 ? sv::lm_tile_width(n, int(V), h->n_cu) : 256;
   const int n_tiles = int(ceil_div(V, tile_w));
 
   sv::VocabArgs va{};
@@ -593,6 +593,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     l.t_arg = h->t_arg;
     l.n_tiles = n_tiles;
     l.p16 = use_p16 ? h->p16 : nullptr;
+    l.lm_narrow = tile_w == 128 ? 1 : 0;
     begin("lm_head");
     if (fp8) {
       l.W8 = h->w_lm8;

@@ -139,9 +139,9 @@ __device__ __forceinline__ uint4 lds16(const uint8_t *p) { return *reinterpret_c
 // 3-stage LDS ring by DMA: weights [NR rows][128 B] and the activation hi and
 // lo planes [TB*32 rows][128 B], row-XOR-swizzled (16-B chunk c of row R at
 // slot c ^ (R & 7)).  Two fp16 MFMAs per product (activation hi + lo).
-// BLOCKED (the LM head, NR = 256): the weights come from the blocked layout
-// of the tiled launch; one K step is two consecutive 16 KB blocks, copied to
-// LDS as they are.
+// BLOCKED (the LM head, NR = 256 or 128): the weights come from the blocked
+// layout of the tiled launch; one K step is two consecutive 16 KB blocks,
+// copied to LDS as they are (NR = 128: the workgroup's 8 KB half of each).
 // ----------------------------------------------------------------------------
 
 constexpr int kSkST = 3;
@@ -167,8 +167,13 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
   const int ks = blockIdx.y * g.k_split;
   const int nk = (min(g.K, ks + g.k_split) - ks) / 64;
   const int Kb = g.K * 2;
-  static_assert(!BLOCKED || NR == 256, "blocked weights come in 256-row tiles");
-  const i32x4 rw = BLOCKED ? make_rsrc(g.W + int64_t(blockIdx.x) * 256 * g.K, uint32_t(256 * Kb))
+  // blocked weights come in 256-row blocks of 64-byte rows; a 128-row
+  // workgroup takes one contiguous half (HB bytes) of each block
+  static_assert(!BLOCKED || NR == 256 || NR == 128, "blocked weight tiles of 256 or 128 rows");
+  // (NR == 128: two workgroups per 256-row block, taking its halves)
+  constexpr int HB = NR * 64;
+  const int half = (BLOCKED && NR == 128) ? int(blockIdx.x & 1) : 0;
+  const i32x4 rw = BLOCKED ? make_rsrc(g.W + int64_t(blockIdx.x / (256 / NR)) * 256 * g.K, uint32_t(256 * Kb))
                            : make_rsrc(g.W + int64_t(n0) * g.K, uint32_t(min(NR, g.N - n0)) * Kb);
   const i32x4 rah = make_rsrc(g.act, uint32_t(g.rows) * Kb);
   const i32x4 ral = make_rsrc(g.act_lo, uint32_t(g.rows) * Kb);
@@ -178,7 +183,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < WI; ++i) {
     const int R = (w * WI + i) * 8 + (lane >> 3);
-    woff[i] = BLOCKED ? (w * WI + i) * 1024 + lane * 16 : R * Kb + ((c8 ^ (R & 7)) << 4);
+    const int j = (w * WI + i) * 1024;   // LDS byte offset of this instruction in the stage
+    woff[i] = BLOCKED ? (j < HB ? j : 16384 + j - HB) + half * HB + lane * 16 : R * Kb + ((c8 ^ (R & 7)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
@@ -217,7 +223,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
       for (int v = 0; v < WV; ++v) {
         const int R = w * WV * 32 + v * 32 + r32;
         // blocked: chunk q of the 128-B step is chunk q & 3 of block q >> 2
-        af[v] = BLOCKED ? lds16(base + (q >> 2) * 16384 + R * 64 + (((q & 3) ^ ((R >> 1) & 3)) << 4))
+        af[v] = BLOCKED ? lds16(base + (q >> 2) * HB + R * 64 + (((q & 3) ^ ((R >> 1) & 3)) << 4))
                         : lds16(base + R * 128 + ((q ^ (R & 7)) << 4));
       }
 #pragma unroll
@@ -729,7 +735,19 @@ void launch_gemm_fp8(const GemmArgs &g, hipStream_t s) {
     hipLaunchKernelGGL((gemm_fp8_kernel<false>), dim3(grid_x), dim3(512), kTiledLds, s, g);
 }
 
-int lm_tile_width(int rows) { return rows <= 64 ? 4 * 2 * 32 : kTBN; }
+// The skinny LM head (<= 32 rows) takes 128 weight rows per workgroup (two
+// workgroups per compute unit, 72 KB of LDS each) when 256-row workgroups
+// (one per unit, 120 KB) would leave their last dispatch round less than 90 %
+// full; otherwise 256 rows, which read the activations half as often.
+int lm_tile_width(int rows, int N, int n_cu) {
+  if (rows > 64) return kTBN;
+  if (rows <= 32) {
+    const int64_t tiles = (int64_t(N) + 255) / 256, cu = std::max(n_cu, 1);
+    const int64_t rounds = (tiles + cu - 1) / cu;
+    if (10 * tiles < 9 * rounds * cu) return 4 * 32;
+  }
+  return 4 * 2 * 32;
+}
 
 // Split-K factor of a projection with `rows` rows: enough workgroups to
 // cover the chip, K pieces of at least 256.
@@ -768,7 +786,12 @@ void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s, 
   if (g.rows <= 64) {
     // WV = 2 for the LM head (256 weight rows per workgroup), 1 for split-K W_o
     if (g.rows <= 32) {
-      if (stats) launch_skinny<1, 2, true>(g, splits, s); else launch_skinny<1, 1, false>(g, splits, s);
+      if (stats && g.lm_narrow)
+        launch_skinny<1, 1, true>(g, splits, s);
+      else if (stats)
+        launch_skinny<1, 2, true>(g, splits, s);
+      else
+        launch_skinny<1, 1, false>(g, splits, s);
     } else {
       if (stats) launch_skinny<2, 2, true>(g, splits, s); else launch_skinny<2, 1, false>(g, splits, s);
     }

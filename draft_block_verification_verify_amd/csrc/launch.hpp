@@ -82,6 +82,8 @@ struct GemmArgs {
   // tiled LM head: when non-null, the tile's probabilities relative to its
   // maximum, exp(l - t_max), as fp16 [rows, ldo], replace the fp32 logits
   uint16_t *p16;
+  // skinny LM head: 128 weight rows per workgroup (lm_tile_width said 128)
+  int lm_narrow;
   // FP8 LM head: e4m3 operands in the blocked layout and their row scales
   const uint8_t *W8, *act8;
   const float *w_scale, *a_scale;
@@ -97,8 +99,9 @@ void launch_attn_merge(const MergeArgs &a, int n_rows, int D, double mean_items,
 void launch_attn_f32(const AttnF32Args &a, int n_rows, hipStream_t s);
 
 // ---- projections ----
-// Tile width (N columns per stats record) of the LM-head launch chosen for `rows`.
-int lm_tile_width(int rows);
+// Tile width (N columns per stats record) of the LM-head launch chosen for
+// `rows` rows, N columns and n_cu compute units.
+int lm_tile_width(int rows, int N, int n_cu);
 // Split-K factor (and K per split, a multiple of 64) of a projection launch.
 int gemm_splits(int rows, int N, int K, int n_cu, int *k_split);
 // `blocked`: the tiled launch reads W and act in the blocked layout (always
