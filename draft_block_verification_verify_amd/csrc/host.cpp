@@ -424,6 +424,10 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   const uint64_t *row_anc = reinterpret_cast<const uint64_t *>(m + lay.row_anc);
   const int32_t *row_child = reinterpret_cast<const int32_t *>(m + lay.row_child);
   const int32_t *draft_row = reinterpret_cast<const int32_t *>(m + lay.draft_row);
+  const int32_t *row_pack = reinterpret_cast<const int32_t *>(m + lay.row_pack);
+  const int32_t *row_plocal = reinterpret_cast<const int32_t *>(m + lay.row_plocal);
+  const int32_t *row_klen = reinterpret_cast<const int32_t *>(m + lay.row_klen);
+  const uint64_t *row_panc = reinterpret_cast<const uint64_t *>(m + lay.row_panc);
   const int32_t *tree_start = reinterpret_cast<const int32_t *>(m + lay.tree_start);
   const int32_t *tree_rows = reinterpret_cast<const int32_t *>(m + lay.tree_rows);
   const int32_t *tree_kv_len = reinterpret_cast<const int32_t *>(m + lay.tree_kv_len);
@@ -530,7 +534,8 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     aa.q_lo_off = q_lo;
     aa.items = items;
     aa.runs = runs;
-    aa.row_anc = row_anc;
+    aa.row_panc = row_panc;
+    aa.row_klen = row_klen;
     aa.part_o = h->part_o;
     aa.part_ml = h->part_ml;
     aa.Hq = int(Hq);
@@ -546,8 +551,8 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     ma.part_o = h->part_o;
     ma.part_ml = h->part_ml;
     ma.groups = groups;
-    ma.row_tree = row_tree;
-    ma.row_local = row_local;
+    ma.row_tree = row_pack;
+    ma.row_local = row_plocal;
     ma.Hq = int(Hq);
     ma.Hkv = int(Hkv);
     ma.qg_max = plan.qg_max;

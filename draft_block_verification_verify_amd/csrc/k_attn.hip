@@ -4,9 +4,12 @@
 // with RoPE at the rows' semantic positions (onedev.kr SpecOPD summary,
 // "what differs": parent map, semantic positions, ancestor-and-self mask).
 //
-// bf16 path: split-KV flash-decode.  A query group is (tree, KV head, up to
-// 128 of the tree's (row, head-in-group) pairs), so one K/V tile streamed
-// from HBM serves every row and every query head of the GQA group.  The
+// bf16 path: split-KV flash-decode.  A query group is (pack, KV head, up to
+// 128 of the pack's (row, head-in-group) pairs), so one K/V tile streamed
+// from HBM serves every row and every query head of the GQA group; a pack is
+// one tree, or (head dims up to 128) consecutive trees over one KV segment,
+// such as the branches of a proposal tree over a shared stem (each query
+// then masks the stem past its own tree's length).  The
 // tiles of all query groups, one group after another, are cut into runs of
 // equal length, one per workgroup; a work item is the part of one group that
 // one run covers.  K/V tiles reach LDS by DMA in their natural layout,
@@ -171,9 +174,17 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_mfma_kernel(AttnArgs a) {
   };
 
   // ---- compute side: the current item's query fragments (B operand of
-  // S^T = K.Q^T, hi and lo), ancestor bits and running softmax state
+  // S^T = K.Q^T, hi and lo), ancestor bits, prefix length and running
+  // softmax state.  With D <= 128 an item's rows may come from several trees
+  // of one pack (one KV segment): each query sees the first q_klen keys of
+  // the prefix (its tree's length, kept in LDS for the masked tiles; c_kmin
+  // is the item's smallest) and the pack's rows its ancestor bits (relative
+  // to the pack's first row) select.  With D = 256 (no register to spare) a
+  // pack is one tree and every query sees the item's c_kmin = kv_len keys.
+  constexpr bool PACKS = D <= 128;
+  __shared__ int q_klen[PACKS ? NW * 16 : 1];
   const int mq = w * 16 + n16;
-  int c_item = run.first, c_tile = 0, c_end = 0, c_np = 0, c_klen = 0, c_slot = 0;
+  int c_item = run.first, c_tile = 0, c_end = 0, c_np = 0, c_kmin = 0, c_slot = 0;
   bool wave_on = false, qok = false;
   uint4 qh[DS], ql[DS];
   uint64_t anc = 0;
@@ -185,11 +196,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_mfma_kernel(AttnArgs a) {
     c_tile = e.k0 / KT;
     c_end = e.k1 / KT;
     c_np = (e.kv_len + KT - 1) / KT;
-    c_klen = e.kv_len;
+    c_kmin = PACKS ? e.kv_min : e.kv_len;
     c_slot = e.slot;
     wave_on = w < (e.nq + 15) / 16;
     qok = wave_on && mq < e.nq;
     anc = 0;
+    [[maybe_unused]] int klen = 0;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) qh[ds] = ql[ds] = make_uint4(0, 0, 0, 0);
     if (qok) {
@@ -202,7 +214,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_mfma_kernel(AttnArgs a) {
         qh[ds] = *reinterpret_cast<const uint4 *>(qp + ds * 32);
         ql[ds] = *reinterpret_cast<const uint4 *>(qp + a.q_lo_off + ds * 32);
       }
-      anc = a.row_anc[row];
+      anc = a.row_panc[row];
+      if constexpr (PACKS) klen = a.row_klen[row];
     }
     // Complete these loads here: the compiler does not see the DMA, and
     // would otherwise re-wait for them (with every DMA in flight) inside the
@@ -214,6 +227,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_mfma_kernel(AttnArgs a) {
       asm volatile("" : "+v"(ql[ds].x), "+v"(ql[ds].y), "+v"(ql[ds].z), "+v"(ql[ds].w));
     }
     asm volatile("" : "+v"(anc));
+    if constexpr (PACKS) {
+      asm volatile("" : "+v"(klen));
+      if (kg == 0) q_klen[mq] = klen;   // read back by this wavefront only
+    }
     m_run = -INFINITY;
     l_run = 0.f;
 #pragma unroll
@@ -300,14 +317,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_mfma_kernel(AttnArgs a) {
       // shows its first klen - key0 keys, a row tile the ancestor-or-self rows
       const bool pre = t < c_np;
       const int key0 = (pre ? t : t - c_np) * KT;
-      const int lim = pre ? c_klen - key0 : 0;
       const uint64_t rbits = (!pre && key0 < 64) ? (anc >> key0) : 0ull;
       const uint32_t rlo = uint32_t(rbits), rhi = uint32_t(rbits >> 32);
       float x[KB][4];
       float tmax = -INFINITY;
-      if (pre && lim >= KT) {
-        // a prefix tile whose keys are all visible (every tile but a tree's
-        // last prefix tile and its row tiles): no mask.  Padding query lanes
+      if (pre && c_kmin - key0 >= KT) {
+        // a prefix tile whose keys every query of the item sees (every
+        // tile but the last prefix tiles and the row tiles): no mask.  Padding query lanes
         // (zero queries) get finite scores here that are never written out.
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -317,6 +333,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_mfma_kernel(AttnArgs a) {
             tmax = fmaxf(tmax, x[kb][i]);
           }
       } else {
+        const int lim = pre ? (PACKS ? q_klen[mq] : c_kmin) - key0 : 0;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           const int vb = 16 * kb + 4 * kg;

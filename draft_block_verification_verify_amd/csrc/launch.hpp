@@ -35,7 +35,8 @@ struct AttnArgs {
   int64_t q_lo_off;                // elements from the hi plane to the lo plane
   const AttnItem *items;
   const AttnRun *runs;             // one per workgroup
-  const uint64_t *row_anc;
+  const uint64_t *row_panc;        // [n] ancestor-or-self bits relative to the row's pack
+  const int32_t *row_klen;         // [n] prefix keys the row sees (its tree's length)
   float *part_o, *part_ml;         // [slots, D], [slots, 2]
   int Hq, Hkv, G;
   float scale_log2;                // log2(e) / sqrt(D)
@@ -43,8 +44,8 @@ struct AttnArgs {
 
 struct MergeArgs {
   const float *part_o, *part_ml;
-  const AttnGroup *groups;         // [R * Hkv * qg_max]
-  const int32_t *row_tree, *row_local;
+  const AttnGroup *groups;         // [R * Hkv * qg_max], by pack
+  const int32_t *row_tree, *row_local;   // the row's pack and its row within the pack
   int Hq, Hkv, qg_max;
   int mode;                        // ACT_SPLIT: fp16 hi plane at out, lo at out + lo_off; ACT_F16; ACT_F16_BLOCKED
   int64_t lo_off;

@@ -93,6 +93,10 @@ MetaLayout meta_layout(int n, int R, int n_draft, int n_items, int n_runs, int n
   L.row_anc = take(8 * size_t(n));
   L.row_child = take(4 * size_t(n));
   L.draft_row = take(4 * size_t(std::max(n_draft, 1)));
+  L.row_pack = take(4 * size_t(n));
+  L.row_plocal = take(4 * size_t(n));
+  L.row_klen = take(4 * size_t(n));
+  L.row_panc = take(8 * size_t(n));
   L.tree_start = take(4 * size_t(R));
   L.tree_rows = take(4 * size_t(R));
   L.tree_kv_len = take(4 * size_t(R));
@@ -228,20 +232,62 @@ int build_plan(const Dims &dm, const HostInputs &in, int64_t slot_cap, int targe
   const int G = dm.Hq / dm.Hkv;
   const int KT = attn_key_tile(dm.d);
   P.qg_max = qg_max_of(dm);
-  std::vector<int64_t> tiles(P.R);
+  // Packs: a tree joins the pack of the trees before it when it reads the
+  // same KV segment (same offset), the pack stays within 64 rows (ancestor
+  // bits) and kItemQ query vectors per KV head (one query group), and the
+  // prefix lengths stay within a factor 2 (queries of the shorter trees run
+  // over the longest prefix, masked).  Head dims above 128 keep one tree
+  // per pack (their attention kernel has no register for a per-query prefix
+  // length).
+  std::vector<int32_t> pack_first, pack_start, pack_rows, pack_len, pack_min;
+  std::vector<int64_t> pack_off;
+  for (int r = 0; r < P.R;) {
+    int rows = P.tree_rows[r], lo = P.tree_kv_len[r], hi = lo, e = r + 1;
+    while (dm.d <= 128 && e < P.R && P.tree_kv_off[e] == P.tree_kv_off[r] && rows + P.tree_rows[e] <= 64 &&
+           int64_t(rows + P.tree_rows[e]) * G <= kItemQ) {
+      const int l2 = std::min(lo, P.tree_kv_len[e]), h2 = std::max(hi, P.tree_kv_len[e]);
+      if (int64_t(h2) > 2 * int64_t(l2) + KT) break;
+      rows += P.tree_rows[e];
+      lo = l2;
+      hi = h2;
+      ++e;
+    }
+    pack_first.push_back(r);
+    pack_start.push_back(P.tree_start[r]);
+    pack_rows.push_back(rows);
+    pack_len.push_back(hi);
+    pack_min.push_back(lo);
+    pack_off.push_back(P.tree_kv_off[r]);
+    r = e;
+  }
+  const int NP = int(pack_first.size());
+  P.n_packs = NP;
+  P.row_pack.resize(n);
+  P.row_plocal.resize(n);
+  P.row_klen.resize(n);
+  P.row_panc.resize(n);
+  for (int pk = 0; pk < NP; ++pk)
+    for (int i = pack_start[pk]; i < pack_start[pk] + pack_rows[pk]; ++i) {
+      const int r = P.row_tree[i];
+      P.row_pack[i] = pk;
+      P.row_plocal[i] = i - pack_start[pk];
+      P.row_klen[i] = P.tree_kv_len[r];
+      P.row_panc[i] = P.row_anc[i] << (P.tree_start[r] - pack_start[pk]);
+    }
+  std::vector<int64_t> tiles(NP);
   int64_t total = 0;
   int mq_max = 1;
-  for (int r = 0; r < P.R; ++r) {
-    const int64_t len = P.tree_kv_len[r];
-    // per-lane byte offsets into one tree's prefix stay below 2^31
+  for (int pk = 0; pk < NP; ++pk) {
+    const int64_t len = pack_len[pk];
+    // per-lane byte offsets into one pack's prefix stay below 2^31
     if (dm.dtype == 1 && (len + KT) * dm.Hkv * dm.d * 2 >= (int64_t(1) << 31)) {
-      *err = cat("tree ", r, ": prefix length ", len, " too large for 32-bit KV offsets");
+      *err = cat("tree ", pack_first[pk], ": prefix length ", len, " too large for 32-bit KV offsets");
       return P_UNSUPPORTED;
     }
-    tiles[r] = ceil_div(len, KT) + ceil_div(P.tree_rows[r], KT);
-    const int64_t mq = int64_t(P.tree_rows[r]) * G;
+    tiles[pk] = ceil_div(len, KT) + ceil_div(pack_rows[pk], KT);
+    const int64_t mq = int64_t(pack_rows[pk]) * G;
     mq_max = int(std::max<int64_t>(mq_max, std::min<int64_t>(mq, kItemQ)));
-    total += int64_t(dm.Hkv) * ceil_div(mq, kItemQ) * tiles[r];
+    total += int64_t(dm.Hkv) * ceil_div(mq, kItemQ) * tiles[pk];
   }
   // Runs: the sequence of every query group's tiles (group order: tree, KV
   // head, query group) cut into pieces of `chunk` tiles.  A run that covers a
@@ -257,7 +303,7 @@ int build_plan(const Dims &dm, const HostInputs &in, int64_t slot_cap, int targe
   // many for the eight-wave launch of groups with more than 64 query vectors,
   // one per compute unit), so that no compute unit takes a second round.
   int64_t max_tiles = 1;
-  for (int r = 0; r < P.R; ++r) max_tiles = std::max(max_tiles, tiles[r]);
+  for (int pk = 0; pk < NP; ++pk) max_tiles = std::max(max_tiles, tiles[pk]);
   const int64_t per_cu = std::max(target_items / 2, 1);
   const int64_t resident = mq_max > 64 ? per_cu : std::max(target_items, 1);
   const int64_t rec_chunk = std::min(ceil_div(4 * int64_t(mq_max), KT), std::max<int64_t>(1, total / per_cu));
@@ -266,8 +312,8 @@ int build_plan(const Dims &dm, const HostInputs &in, int64_t slot_cap, int targe
   auto for_each_item = [&](int64_t ch, auto &&fn) {
     // fn(r, g, qg, m0, nq, tile0, tile1, run) for every work item in order
     int64_t at = 0;   // position in the whole sequence
-    for (int r = 0; r < P.R; ++r) {
-      const int mq = P.tree_rows[r] * G;
+    for (int r = 0; r < NP; ++r) {
+      const int mq = pack_rows[r] * G;
       for (int g = 0; g < dm.Hkv; ++g)
         for (int qg = 0; qg * kItemQ < mq; ++qg) {
           const int m0 = qg * kItemQ;
@@ -318,10 +364,11 @@ int build_plan(const Dims &dm, const HostInputs &in, int64_t slot_cap, int targe
     it.k0 = int32_t(t0 * KT);
     it.k1 = int32_t(t1 * KT);
     it.slot = int32_t(slot);
-    it.tree_start = P.tree_start[r];
-    it.tree_rows = P.tree_rows[r];
-    it.kv_len = P.tree_kv_len[r];
-    it.kv_off = P.tree_kv_off[r];
+    it.tree_start = pack_start[r];
+    it.tree_rows = pack_rows[r];
+    it.kv_len = pack_len[r];
+    it.kv_off = pack_off[r];
+    it.kv_min = pack_min[r];
     slot += nq;
     P.items.push_back(it);
   });
@@ -350,6 +397,10 @@ void pack_plan(const Plan &p, int Hkv, void *dst, MetaLayout *lay) {
   put(L.row_anc, p.row_anc.data(), 8 * size_t(p.n));
   put(L.row_child, p.row_child.data(), 4 * size_t(p.n));
   put(L.draft_row, p.draft_row.data(), 4 * size_t(p.n_draft));
+  put(L.row_pack, p.row_pack.data(), 4 * size_t(p.n));
+  put(L.row_plocal, p.row_plocal.data(), 4 * size_t(p.n));
+  put(L.row_klen, p.row_klen.data(), 4 * size_t(p.n));
+  put(L.row_panc, p.row_panc.data(), 8 * size_t(p.n));
   put(L.tree_start, p.tree_start.data(), 4 * size_t(p.R));
   put(L.tree_rows, p.tree_rows.data(), 4 * size_t(p.R));
   put(L.tree_kv_len, p.tree_kv_len.data(), 4 * size_t(p.R));

@@ -45,8 +45,9 @@ struct AttnItem {
   int32_t tree, g, m0, nq, k0, k1, slot, tree_start;
   int32_t tree_rows, kv_len;
   int64_t kv_off;
+  int32_t kv_min, pad;   // the smallest prefix length among the item's queries
 };
-static_assert(sizeof(AttnItem) == 48, "AttnItem layout");
+static_assert(sizeof(AttnItem) == 56, "AttnItem layout");
 
 // One workgroup's run: items [first, first + count) in order, `tiles` tiles
 // in all.
@@ -83,11 +84,20 @@ struct Plan {
   // per tree
   std::vector<int32_t> tree_start, tree_rows, tree_kv_len;
   std::vector<int64_t> tree_kv_off;
+  // attention packs: consecutive trees over one KV segment whose queries
+  // share one query group per KV head, so that each prefix tile is read once
+  // for all of them (a pack of one tree otherwise).  Per row: its pack, its
+  // row within the pack, its own prefix length (the keys of the shared
+  // segment it sees) and its ancestor-or-self bits relative to the pack's
+  // first row.
+  int32_t n_packs = 0;
+  std::vector<int32_t> row_pack, row_plocal, row_klen;
+  std::vector<uint64_t> row_panc;
   // attention
-  std::vector<AttnItem> items;        // in query-group order
+  std::vector<AttnItem> items;        // in query-group order (tree fields: the pack's)
   std::vector<AttnRun> runs;          // one per attention workgroup
   int32_t qg_max = 1;                 // query groups per (tree, g)
-  std::vector<AttnGroup> groups;      // [R * Hkv * qg_max]
+  std::vector<AttnGroup> groups;      // [R * Hkv * qg_max], indexed by pack
   int32_t chunk = 0;                  // keys per run (the last run shorter)
   int64_t slots = 0;                  // partial (m, l, o) records needed
 };
@@ -110,6 +120,7 @@ int64_t slot_capacity(const Dims &dm);
 // Byte layout of the device copy of a plan (offsets into one buffer).
 struct MetaLayout {
   size_t row_tree, row_local, row_pos, row_parent, row_draft, row_anc, row_child, draft_row;
+  size_t row_pack, row_plocal, row_klen, row_panc;
   size_t tree_start, tree_rows, tree_kv_len, tree_kv_off;
   size_t items, runs, groups;
   size_t total;

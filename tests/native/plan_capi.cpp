@@ -40,3 +40,24 @@ extern "C" int svp_plan(const int *dims, int n_rows, int n_roots, const int32_t 
   std::memcpy(runs_out, p.runs.data(), sizeof(sv::AttnRun) * size_t(nr));
   return 0;
 }
+
+// Per-row attention pack arrays of the same plan: pack index, row within the
+// pack, prefix length, pack-relative ancestor bits; returns the pack count.
+extern "C" int svp_packs(const int *dims, int n_rows, int n_roots, const int32_t *parent, const int32_t *pos,
+                         const int64_t *off, const int32_t *len, int64_t kv_tokens, int32_t *row_pack,
+                         int32_t *row_plocal, int32_t *row_klen, uint64_t *row_panc) {
+  sv::Dims dm{dims[0], dims[1], dims[2], dims[3], dims[4], dims[5], dims[6], dims[7], dims[8], dims[9]};
+  std::string e;
+  if (sv::check_dims(dm, &e) != sv::P_OK) return -100;
+  sv::Plan p;
+  sv::HostInputs hi{n_rows, n_roots, parent, pos, off, len, kv_tokens};
+  const int st = sv::build_plan(dm, hi, int64_t(1) << 20, 1024, &p, &e);
+  if (st != sv::P_OK) return st;
+  for (int i = 0; i < p.n; ++i) {
+    row_pack[i] = p.row_pack[i];
+    row_plocal[i] = p.row_plocal[i];
+    row_klen[i] = p.row_klen[i];
+    row_panc[i] = p.row_panc[i];
+  }
+  return p.n_packs;
+}

@@ -111,7 +111,7 @@ def plan(L, dims, parent, pos, off, lens, kv_tokens, slot_cap=1 << 20, target=10
     stats = np.zeros(9, np.int64)
     err = C.create_string_buffer(512)
     anc = np.zeros(max(n, 1), np.uint64)
-    items = np.zeros((8192, 12), np.int32)       # AttnItem: 10 int32 + one int64
+    items = np.zeros((8192, 14), np.int32)       # AttnItem: 10 int32, one int64, kv_min, pad
     runs = np.zeros((8192, 4), np.int32)         # AttnRun: first, count, tiles, pad
     st = L.svp_plan(dims.ctypes.data_as(C.c_void_p), n, len(lens), parent.ctypes.data_as(C.c_void_p),
                     pos.ctypes.data_as(C.c_void_p), off.ctypes.data_as(C.c_void_p),
@@ -220,6 +220,55 @@ def test_plan_runs_fit_resident_workgroups(plan_lib):
     st, err, stats8, _, _ = plan(plan_lib, dims8, parent8, np.arange(8) + 4096, [0], [4096], 4096, target=512)
     assert st == 0, err
     assert 256 < stats8[8] <= 512
+
+
+def test_plan_packs_trees_over_one_kv_segment(plan_lib):
+    # Trees that read the same KV segment (same offset) share one query group
+    # per KV head: up to 64 rows and 128 query vectors, prefix lengths within
+    # a factor 2.  Here: three 7-row chains on segment 0 (lengths 100, 120,
+    # 150: one pack), a fourth on segment 0 with length 400 (too long: its
+    # own pack), a fifth on another segment (its own pack).
+    T = 7
+    lens = [100, 120, 150, 400, 90]
+    offs = [0, 0, 0, 0, 1000]
+    parent = []
+    for t in range(5):
+        parent += [-1] + [t * T + j for j in range(T - 1)]
+    n = len(parent)
+    pos = np.concatenate([np.arange(T) + lens[t] for t in range(5)])
+    st, err, stats, anc, items = plan(plan_lib, DIMS, parent, pos, offs, lens, 1200)
+    assert st == 0, err
+    L = plan_lib
+    L.svp_packs.restype = C.c_int
+    rp, rl, rk = (np.zeros(n, np.int32) for _ in range(3))
+    ra = np.zeros(n, np.uint64)
+    args = [np.ascontiguousarray(x) for x in (np.array(DIMS, np.int32), np.array(parent, np.int32),
+                                              pos.astype(np.int32), np.array(offs, np.int64),
+                                              np.array(lens, np.int32))]
+    npk = L.svp_packs(args[0].ctypes.data_as(C.c_void_p), n, 5, args[1].ctypes.data_as(C.c_void_p),
+                      args[2].ctypes.data_as(C.c_void_p), args[3].ctypes.data_as(C.c_void_p),
+                      args[4].ctypes.data_as(C.c_void_p), C.c_int64(1200), rp.ctypes.data_as(C.c_void_p),
+                      rl.ctypes.data_as(C.c_void_p), rk.ctypes.data_as(C.c_void_p), ra.ctypes.data_as(C.c_void_p))
+    assert npk == 3
+    assert rp.tolist() == [0] * 21 + [1] * 7 + [2] * 7
+    starts = [0, 0, 0, 21, 28]
+    assert rl.tolist() == [i - starts[i // T] for i in range(n)]
+    assert rk.tolist() == sum(([lens[t]] * T for t in range(5)), [])
+    for i in range(n):
+        t = i // T
+        shift = t * T - starts[t]
+        assert int(ra[i]) == int(anc[i]) << shift, i
+    # items are per pack: the pack's first row, its rows and longest prefix,
+    # and its key range covers that prefix and the pack's rows
+    KT = 8192 // DIMS[2]
+    for pk, (start, rows, klen, off) in enumerate([(0, 21, 150, 0), (21, 7, 400, 0), (28, 7, 90, 1000)]):
+        its = [it for it in items if it[0] == pk]
+        assert its and all((it[7], it[8], it[9]) == (start, rows, klen) for it in its)
+        assert all(int(it[10:12].view(np.int64)[0]) == off for it in its)
+        for g in range(DIMS[1]):
+            gi = sorted((it for it in its if it[1] == g), key=lambda it: it[4])
+            assert gi[0][4] == 0 and gi[-1][5] == (-(-klen // KT) - (-rows // KT)) * KT
+            assert all(it[3] == rows * 4 for it in gi)
 
 
 def test_plan_caps_splits_per_group(plan_lib):
