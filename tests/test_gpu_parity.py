@@ -219,6 +219,63 @@ def test_edge_cases_forest():
     P.compare(ref, gpu, st.parent, inp.draft_ids, logits_ref=ref["logits"], logits_gpu=gpu["logits"])
 
 
+def test_edge_cases_shared_segment():
+    # Trees that read one KV segment (the same offset) become attention packs
+    # when their lengths are close: here segment A holds a pack of four trees
+    # (lengths 130, 129, 200, 290: branching, chains, lone rows), then a pack
+    # of a 10-token tree and a root with an empty prefix (lengths not tile
+    # multiples, one zero), a tree on segment B, and a last tree back on A
+    # (not consecutive with the first pack: its own).  Head dim 128.
+    cfg = mini(2, hidden=256, vocab=1003, w_lm_std=0.08)
+    rng = np.random.default_rng(11)
+    parent, pos, offs, lens = [], [], [], []
+
+    def add_tree(par_local, off, L):
+        s = len(parent)
+        for k, pl in enumerate(par_local):
+            parent.append(-1 if pl < 0 else s + pl)
+            pos.append(L + k)
+        offs.append(off)
+        lens.append(L)
+
+    add_tree([-1, 0, 0, 1, 1, 2, 5], 0, 130)
+    add_tree([-1, 0, 1, 2], 0, 129)
+    add_tree([-1] + list(range(6)), 0, 200)
+    add_tree([-1, 0, 0], 0, 290)
+    add_tree([-1, 0, 1, 2, 3], 0, 10)
+    add_tree([-1], 0, 0)
+    add_tree([-1, 0, 1, 2, 3, 4], 300, 50)
+    add_tree([-1, 0, 0, 2, 2, 4, 4], 0, 140)
+    tok = 350
+    st = W.Structure(np.array(parent, np.int32), np.array(pos, np.int32), np.array(offs, np.int64),
+                     np.array(lens, np.int32), tok)
+    inp = W.make_inputs(cfg, 0)
+    n, nd = st.n_rows, int((st.parent >= 0).sum())
+    inp.st = st
+    Hq, Hkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    assert d == 128
+    bf = lambda shape, s=1.0: W.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32) * s)
+    inp.kv_k, inp.kv_v = bf((tok, Hkv, d)), bf((tok, Hkv, d))
+    inp.q_rows, inp.k_rows, inp.v_rows = bf((n, Hq, d)), bf((n, Hkv, d)), bf((n, Hkv, d))
+    inp.drafter_logits = bf((nd, cfg.vocab), 2.0)
+    inp.draft_ids = rng.integers(0, cfg.vocab, n).astype(np.int32)
+    cd = O.cfg_dict(cfg)
+    g = O.target_greedy(cd, O.inp_dict(inp))
+    for i in range(n):
+        if parent[i] >= 0 and rng.random() < 0.8:
+            inp.draft_ids[i] = g[parent[i]]
+    ref = O.verify(cd, O.inp_dict(inp), keep_logits=True)
+    from draft_block_verification_verify_amd.runner import DeviceCase
+    dc = DeviceCase(inp, with_logits=True)
+    dc.run()
+    gpu = dc.results()
+    dc.close()
+    P.check_self_consistency(st.parent, inp.draft_ids, gpu)
+    rep = {}
+    P.compare(ref, gpu, st.parent, inp.draft_ids, logits_ref=ref["logits"], logits_gpu=gpu["logits"], report=rep)
+    _record("shared-segment", rep)
+
+
 def test_no_draft_rows_and_f32_path():
     # roots only: no drafter logits at all
     cfg = W.CONFIGS[1]
