@@ -472,11 +472,11 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   va.drafter = in->drafter_logits;
   va.drafter_bf16 = bf16 ? 1 : 0;
   va.logits = logits;
-  // Without a caller logits buffer (and outside T = 1 mode, whose draw reads
-  // the logits), the tiled LM head stores each tile's probabilities relative
-  // to the tile maximum in fp16 instead of fp32 logits: half the bytes for
-  // the overlap pass, the only reader.
-  const bool use_p16 = bf16 && !fp8 && n > 64 && !out->logits && in->mode != SV_MODE_SAMPLE && h->p16 != nullptr;
+  // Without a caller logits buffer, the tiled LM head stores each tile's
+  // probabilities relative to the tile maximum in fp16 instead of fp32
+  // logits: half the bytes for their readers (the overlap pass, and in T = 1
+  // mode the accept tests and the bonus draw).
+  const bool use_p16 = bf16 && !fp8 && n > 64 && !out->logits && h->p16 != nullptr;
   va.p16 = use_p16 ? h->p16 : nullptr;
   va.t_max = h->t_max;
   va.t_sum = h->t_sum;

@@ -299,6 +299,14 @@ __device__ __forceinline__ float drafter_at(const VocabArgs &a, int draft, int u
   return load1(a.drafter, a.drafter_bf16, int64_t(draft) * a.V + u);
 }
 
+// target probability p_row(u): from the fp32 logits, or from the tiled LM
+// head's fp16 probabilities relative to their 256-token tile's maximum
+__device__ __forceinline__ float p_at(const VocabArgs &a, int row, int u) {
+  if (a.p16)
+    return h2f(a.p16[int64_t(row) * a.V + u]) * __expf(a.t_max[int64_t(row) * a.n_tiles + (u >> 8)] - a.row_lse[row]);
+  return __expf(a.logits[int64_t(row) * a.V + u] - a.row_lse[row]);
+}
+
 __global__ __launch_bounds__(64) void swalk_kernel(VocabArgs a, SampleArgs sa) {
   const int r = blockIdx.x;
   if (threadIdx.x != 0) return;
@@ -306,7 +314,7 @@ __global__ __launch_bounds__(64) void swalk_kernel(VocabArgs a, SampleArgs sa) {
   int c;
   while ((c = sa.row_child[cur]) >= 0) {
     const int d = a.draft_ids[c];
-    const float pd = __expf(a.logits[int64_t(cur) * a.V + d] - a.row_lse[cur]);
+    const float pd = p_at(a, cur, d);
     const int dr = a.row_draft[c];
     const float qd = __expf(drafter_at(a, dr, d) - a.lse_q[dr]);
     if (!(sa.u_accept[c] * qd < pd)) break;
@@ -322,6 +330,8 @@ __global__ __launch_bounds__(64) void swalk_kernel(VocabArgs a, SampleArgs sa) {
 // after the rejection of child c (rej = c; -1 after a leaf).
 struct BonusRow {
   const float *lp;      // logits of the stop row
+  const uint16_t *pp;   // or its fp16 tile-relative probabilities (a.p16)
+  const float *tm;      // and their tile maxima
   const void *lq;       // drafter logits of the rejected child (resid only)
   float lse_p, lse_q;
   bool resid;
@@ -330,6 +340,8 @@ struct BonusRow {
 __device__ __forceinline__ BonusRow bonus_row(const VocabArgs &a, int stop, int rej) {
   BonusRow b;
   b.lp = a.logits + int64_t(stop) * a.V;
+  b.pp = a.p16 ? a.p16 + int64_t(stop) * a.V : nullptr;
+  b.tm = a.t_max + int64_t(stop) * a.n_tiles;
   b.lse_p = a.row_lse[stop];
   b.resid = rej >= 0;
   const int dr = b.resid ? a.row_draft[rej] : 0;
@@ -345,11 +357,29 @@ constexpr int kSampPer = kSampChunk / 256;   // tokens per thread in a chunk
 // every load is issued before the arithmetic
 __device__ __forceinline__ void chunk_weights(const VocabArgs &a, const BonusRow &b, int base,
                                               float (&w)[kSampPer]) {
-  float lg[kSampPer];
+  float pr[kSampPer];   // p of the stop row
+  if (b.pp) {
+    // token u = base + thread + 256 j lies in 256-token tile base / 256 + j
+    uint16_t h[kSampPer];
 #pragma unroll
-  for (int j = 0; j < kSampPer; ++j) {
-    const int u = base + int(threadIdx.x) + 256 * j;
-    lg[j] = u < a.V ? b.lp[u] : -INFINITY;
+    for (int j = 0; j < kSampPer; ++j) {
+      const int u = base + int(threadIdx.x) + 256 * j;
+      h[j] = u < a.V ? b.pp[u] : uint16_t(0);
+    }
+#pragma unroll
+    for (int j = 0; j < kSampPer; ++j) {
+      const int tile = min((base >> 8) + j, a.n_tiles - 1);
+      pr[j] = h2f(h[j]) * __expf(b.tm[tile] - b.lse_p);
+    }
+  } else {
+    float lg[kSampPer];
+#pragma unroll
+    for (int j = 0; j < kSampPer; ++j) {
+      const int u = base + int(threadIdx.x) + 256 * j;
+      lg[j] = u < a.V ? b.lp[u] : -INFINITY;
+    }
+#pragma unroll
+    for (int j = 0; j < kSampPer; ++j) pr[j] = __expf(lg[j] - b.lse_p);
   }
   if (b.resid) {
     float lq[kSampPer];
@@ -359,11 +389,10 @@ __device__ __forceinline__ void chunk_weights(const VocabArgs &a, const BonusRow
       lq[j] = load1(b.lq, a.drafter_bf16, u);
     }
 #pragma unroll
-    for (int j = 0; j < kSampPer; ++j)
-      w[j] = fmaxf(__expf(lg[j] - b.lse_p) - __expf(lq[j] - b.lse_q), 0.f);
+    for (int j = 0; j < kSampPer; ++j) w[j] = fmaxf(pr[j] - __expf(lq[j] - b.lse_q), 0.f);
   } else {
 #pragma unroll
-    for (int j = 0; j < kSampPer; ++j) w[j] = __expf(lg[j] - b.lse_p);
+    for (int j = 0; j < kSampPer; ++j) w[j] = pr[j];
   }
 }
 

@@ -363,7 +363,7 @@ def test_error_paths_enqueue_nothing():
 # ----------------------------------------------------------------------------
 
 
-def run_sample_case(cfg, seed, sigma=None):
+def run_sample_case(cfg, seed, sigma=None, with_logits=True):
     """Drafts drawn from the drafter (optionally a drafter correlated with the
     target: its logits = the target's + N(0, sigma)), seeded uniforms."""
     from draft_block_verification_verify_amd.runner import DeviceCase
@@ -382,7 +382,7 @@ def run_sample_case(cfg, seed, sigma=None):
     d = dict(O.inp_dict(inp))
     d.update(mode=1, u_accept=ua, u_bonus=ub)
     ref = O.verify(cd, d, keep_logits=True)
-    dc = DeviceCase(inp, with_logits=True, uniforms=(ua, ub))
+    dc = DeviceCase(inp, with_logits=with_logits, uniforms=(ua, ub))
     dc.run()
     gpu = dc.results()
     dc.close()
@@ -406,6 +406,22 @@ def test_parity_sample_mode(name, sigma):
     rep.update(rs)
     rep["same_as_oracle"] = same / st.n_roots
     _record(f"{name}/sample{sigma}", rep)
+
+
+@pytest.mark.parametrize("name,sigma", [("c5m", 0.5), ("c4m", 0.3), ("c5t", 0.4), ("c5m", None)])
+def test_parity_sample_mode_without_logits_buffer(name, sigma):
+    # above 64 rows without a caller logits buffer the accept tests and the
+    # bonus draw read the LM head's fp16 tile-relative probabilities
+    cfg = MINIS[name]
+    inp, ref, gpu, ua, ub = run_sample_case(cfg, 1, sigma, with_logits=False)
+    st = inp.st
+    P.check_self_consistency(st.parent, inp.draft_ids, gpu, greedy=False)
+    rep = {}
+    P.compare(ref, gpu, st.parent, inp.draft_ids, logits_ref=ref["logits"], report=rep, greedy=False)
+    dl = O.decode(inp.drafter_logits, cfg.dtype)
+    rs = P.check_sample(st.parent, inp.draft_ids, ua, ub, ref["logits"], dl, gpu)
+    rep.update(rs)
+    _record(f"{name}/sample{sigma}/no-logits", rep)
 
 
 def test_sample_mode_refuses_branching_and_bad_mode():
