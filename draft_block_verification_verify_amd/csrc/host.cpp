@@ -651,12 +651,20 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     sv::launch_stats_from_logits(logits, n, int(V), 256, h->t_max, h->t_sum, h->t_arg, n_tiles, stream);
     end();
   }
-  begin("row_combine");
-  sv::launch_row_combine(va, stream);
-  end();
-  begin("overlap");
-  sv::launch_overlap_partial(va, stream);
-  end();
+  if (n <= 64) {
+    // few rows: few tile records per row, so the overlap workgroups merge
+    // their own logsumexps and the two passes share one launch
+    begin("combine_overlap");
+    sv::launch_combine_overlap(va, stream);
+    end();
+  } else {
+    begin("row_combine");
+    sv::launch_row_combine(va, stream);
+    end();
+    begin("overlap");
+    sv::launch_overlap_partial(va, stream);
+    end();
+  }
   begin("accept");
   sv::launch_accept(va, stream);
   end();

@@ -152,10 +152,11 @@ __global__ __launch_bounds__(256) void rope_drafter_kernel(RopeArgs r, VocabArgs
   }
 }
 
-__global__ __launch_bounds__(256) void row_combine_kernel(VocabArgs a) {
-  const int i = blockIdx.x, tid = threadIdx.x;
-  // target tiles of row i: each thread merges its strided tiles in order, then
-  // a fixed-shape tree over the block
+// Target (max, sum exp, argmax) of row i from its LM-head tile records:
+// each thread merges its strided tiles in order, then a fixed-shape tree
+// over the block; every thread gets the result.
+__device__ __forceinline__ MaxSumArg row_stats_block(const VocabArgs &a, int i) {
+  const int tid = threadIdx.x;
   MaxSumArg r = msa_empty();
   for (int c = tid; c < a.n_tiles; c += 256) {
     const int64_t o = int64_t(i) * a.n_tiles + c;
@@ -164,31 +165,42 @@ __global__ __launch_bounds__(256) void row_combine_kernel(VocabArgs a) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) r = msa_shfl_xor(r, o);
   __shared__ MaxSumArg red[4];
+  __syncthreads();
   if ((tid & 63) == 0) red[tid >> 6] = r;
   __syncthreads();
-  if (tid == 0) {
-    r = msa_merge(msa_merge(red[0], red[1]), msa_merge(red[2], red[3]));
+  return msa_merge(msa_merge(red[0], red[1]), msa_merge(red[2], red[3]));
+}
+
+// (max, sum exp) of drafter row t from its chunk records, every thread
+__device__ __forceinline__ MaxSum drafter_stats_block(const VocabArgs &a, int t) {
+  MaxSum q{-INFINITY, 0.f};
+  for (int c = threadIdx.x; c < a.n_dch; c += 256) {
+    const float2 d = a.dpart[int64_t(t) * a.n_dch + c];
+    q = ms_merge(q, MaxSum{d.x, d.y});
+  }
+  return ms_block256(q);
+}
+
+__device__ __forceinline__ void row_combine_block(const VocabArgs &a, int i) {
+  const MaxSumArg r = row_stats_block(a, i);
+  if (threadIdx.x == 0) {
     a.row_max[i] = r.m;
     a.row_lse[i] = r.m + logf(r.s);
     a.argmax[i] = r.i;
   }
   const int t = a.row_draft[i];
   if (t >= 0) {
-    MaxSum q{-INFINITY, 0.f};
-    for (int c = tid; c < a.n_dch; c += 256) {
-      const float2 d = a.dpart[int64_t(t) * a.n_dch + c];
-      q = ms_merge(q, MaxSum{d.x, d.y});
-    }
-    q = ms_block256(q);
-    if (tid == 0) a.lse_q[t] = q.m + logf(q.s);
+    const MaxSum q = drafter_stats_block(a, t);
+    if (threadIdx.x == 0) a.lse_q[t] = q.m + logf(q.s);
   }
 }
 
-__global__ __launch_bounds__(256) void overlap_partial_kernel(VocabArgs a) {
-  const int c = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
-  const int i = a.draft_row[t];
-  const int j = a.row_parent[i];
-  const float A = a.row_lse[j], B = a.lse_q[t];
+__global__ __launch_bounds__(256) void row_combine_kernel(VocabArgs a) { row_combine_block(a, blockIdx.x); }
+
+// chunk c of draft row t's overlap with its parent j: A = lse of p_j, B =
+// lse of q_t
+__device__ __forceinline__ void overlap_block(const VocabArgs &a, int c, int t, int j, float A, float B) {
+  const int tid = threadIdx.x;
   const float *lp = a.logits + int64_t(j) * a.V;
   const int64_t qrow = int64_t(t) * a.V;
   const int lo = c * a.ochunk, hi = min(a.V, lo + a.ochunk);
@@ -226,6 +238,29 @@ __global__ __launch_bounds__(256) void overlap_partial_kernel(VocabArgs a) {
   }
   s = sum_block256(s);
   if (tid == 0) a.opart[int64_t(t) * a.n_och + c] = s;
+}
+
+__global__ __launch_bounds__(256) void overlap_partial_kernel(VocabArgs a) {
+  const int t = blockIdx.y;
+  const int j = a.row_parent[a.draft_row[t]];
+  overlap_block(a, blockIdx.x, t, j, a.row_lse[j], a.lse_q[t]);
+}
+
+// Small batches: the row statistics and the overlap sums in one launch.
+// Workgroups [0, n) combine row b; the rest take overlap chunks, each
+// merging its parent's and its drafter row's records itself with the same
+// code and order as the combining workgroups (so with the same values).
+__global__ __launch_bounds__(256) void combine_overlap_kernel(VocabArgs a) {
+  const int b = blockIdx.x;
+  if (b < a.n) {
+    row_combine_block(a, b);
+    return;
+  }
+  const int d = b - a.n, c = d % a.n_och, t = d / a.n_och;
+  const int j = a.row_parent[a.draft_row[t]];
+  const MaxSumArg r = row_stats_block(a, j);
+  const MaxSum q = drafter_stats_block(a, t);
+  overlap_block(a, c, t, j, r.m + logf(r.s), q.m + logf(q.s));
 }
 
 // One wavefront per tree (at most 64 rows).
@@ -551,6 +586,9 @@ void launch_drafter_partial(const VocabArgs &a, hipStream_t s) {
 }
 void launch_row_combine(const VocabArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(row_combine_kernel, dim3(a.n), dim3(256), 0, s, a);
+}
+void launch_combine_overlap(const VocabArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(combine_overlap_kernel, dim3(a.n + a.n_och * a.n_draft), dim3(256), 0, s, a);
 }
 void launch_overlap_partial(const VocabArgs &a, hipStream_t s) {
   if (a.n_draft == 0) return;

@@ -193,6 +193,9 @@ struct RopeArgs {
   int n, ry;
 };
 void launch_rope_drafter_bf16(const RopeArgs &r, const VocabArgs &a, hipStream_t s);
+// row_combine and overlap_partial in one launch (small batches: each
+// overlap workgroup recomputes its two logsumexps from the tile records)
+void launch_combine_overlap(const VocabArgs &a, hipStream_t s);
 void launch_row_combine(const VocabArgs &a, hipStream_t s);
 void launch_overlap_partial(const VocabArgs &a, hipStream_t s);
 void launch_accept(const VocabArgs &a, hipStream_t s);
