@@ -366,8 +366,8 @@ def main() -> int:
                          "lengths each step) instead of the single verify step")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the verify step is not "
-              "sharded across GPUs in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the verify step here is "
+              "a single-GPU implementation with no sharding across GPUs", file=sys.stderr)
         return 2
     import torch
     if args.copy_calibration:
