@@ -274,9 +274,18 @@ __global__ __launch_bounds__(64) void accept_kernel(VocabArgs a) {
     const int p = a.row_parent[i];
     float o = 1.f;
     if (p >= 0) {
-      const int t = a.row_draft[i];
+      // the chunk sums in chunk order; loads issued eight at a time ahead of
+      // the adds (a runtime-bounded loop of loads would wait on each one)
+      const float *op = a.opart + int64_t(a.row_draft[i]) * a.n_och;
       o = 0.f;
-      for (int c = 0; c < a.n_och; ++c) o += a.opart[int64_t(t) * a.n_och + c];
+      for (int c0 = 0; c0 < a.n_och; c0 += 8) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = c0 + e < a.n_och ? op[c0 + e] : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (c0 + e < a.n_och) o += x[e];
+      }
     }
     ov[lane] = o;
     par[lane] = p < 0 ? -1 : p - s0;
