@@ -158,9 +158,19 @@ __global__ __launch_bounds__(256) void rope_drafter_kernel(RopeArgs r, VocabArgs
 __device__ __forceinline__ MaxSumArg row_stats_block(const VocabArgs &a, int i) {
   const int tid = threadIdx.x;
   MaxSumArg r = msa_empty();
-  for (int c = tid; c < a.n_tiles; c += 256) {
-    const int64_t o = int64_t(i) * a.n_tiles + c;
-    r = msa_merge(r, MaxSumArg{a.t_max[o], a.t_sum[o], a.t_arg[o]});
+  // the thread's tiles tid, tid + 256, ... in order, their records loaded four
+  // at a time ahead of the merges
+  const int64_t row0 = int64_t(i) * a.n_tiles;
+  for (int c0 = tid; c0 < a.n_tiles; c0 += 4 * 256) {
+    MaxSumArg v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = c0 + 256 * e;
+      v[e] = c < a.n_tiles ? MaxSumArg{a.t_max[row0 + c], a.t_sum[row0 + c], a.t_arg[row0 + c]} : msa_empty();
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (c0 + 256 * e < a.n_tiles) r = msa_merge(r, v[e]);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) r = msa_shfl_xor(r, o);
