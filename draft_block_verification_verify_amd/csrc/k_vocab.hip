@@ -207,6 +207,8 @@ __device__ __forceinline__ void row_combine_block(const VocabArgs &a, int i) {
 
 __global__ __launch_bounds__(256) void row_combine_kernel(VocabArgs a) { row_combine_block(a, blockIdx.x); }
 
+constexpr int kOverlapChunk = 8192;   // the host's overlap chunk (vocabulary values per workgroup)
+
 // chunk c of draft row t's overlap with its parent j: A = lse of p_j, B =
 // lse of q_t
 __device__ __forceinline__ void overlap_block(const VocabArgs &a, int c, int t, int j, float A, float B) {
@@ -220,6 +222,35 @@ __device__ __forceinline__ void overlap_block(const VocabArgs &a, int c, int t, 
     // LM head (the host takes this path only when V % 8 == 0)
     const uint16_t *pp = a.p16 + int64_t(j) * a.V;
     const float *tm = a.t_max + int64_t(j) * a.n_tiles;
+    constexpr int NG = kOverlapChunk / 2048;   // groups of 8 per thread in a full chunk
+    if (a.ochunk == kOverlapChunk && a.drafter_bf16) {
+      // every group's loads issued before the arithmetic (one pass over HBM);
+      // groups past the vocabulary contribute nothing
+      uint4 hq[NG], hb[NG];
+      float sc[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int u = lo + tid * 8 + g * 2048;
+        const bool in = u < hi;
+        hq[g] = in ? *reinterpret_cast<const uint4 *>(pp + u) : make_uint4(0, 0, 0, 0);
+        hb[g] = in ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.drafter) + qrow + u)
+                   : make_uint4(0, 0, 0, 0);
+        sc[g] = in ? tm[u >> 8] : -INFINITY;
+      }
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        if (lo + tid * 8 + g * 2048 >= hi) continue;
+        const float scale = __expf(sc[g] - A);
+        const uint32_t w[4] = {hq[g].x, hq[g].y, hq[g].z, hq[g].w};
+        const uint32_t d[4] = {hb[g].x, hb[g].y, hb[g].z, hb[g].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = h2f(uint16_t((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu))) * scale;
+          const float b = __uint_as_float((e & 1) ? (d[e >> 1] & 0xFFFF0000u) : (d[e >> 1] << 16));
+          s += fminf(p, __expf(b - B));
+        }
+      }
+    } else {
     for (int u = lo + tid * 8; u < hi; u += 256 * 8) {
       float b[8];
       load8(a.drafter, a.drafter_bf16, qrow + u, b);
@@ -231,6 +262,7 @@ __device__ __forceinline__ void overlap_block(const VocabArgs &a, int c, int t, 
         const float p = h2f(uint16_t((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu))) * sc;
         s += fminf(p, __expf(b[e] - B));
       }
+    }
     }
   } else if ((a.V % 8) == 0) {
     for (int u = lo + tid * 8; u < hi; u += 256 * 8) {
