@@ -265,14 +265,37 @@ __device__ __forceinline__ void overlap_block(const VocabArgs &a, int c, int t, 
     }
     }
   } else if ((a.V % 8) == 0) {
-    for (int u = lo + tid * 8; u < hi; u += 256 * 8) {
-      float b[8];
-      load8(a.drafter, a.drafter_bf16, qrow + u, b);
-      const float4 l0 = *reinterpret_cast<const float4 *>(lp + u);
-      const float4 l1 = *reinterpret_cast<const float4 *>(lp + u + 4);
-      const float l[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+    constexpr int NG = kOverlapChunk / 2048;
+    if (a.ochunk == kOverlapChunk) {
+      // every group's loads issued before the arithmetic (same order of adds)
+      float b[NG][8];
+      float4 l0[NG], l1[NG];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += __expf(fminf(l[e] - A, b[e] - B));
+      for (int g = 0; g < NG; ++g) {
+        const int u = lo + tid * 8 + g * 2048;
+        if (u < hi) {
+          load8(a.drafter, a.drafter_bf16, qrow + u, b[g]);
+          l0[g] = *reinterpret_cast<const float4 *>(lp + u);
+          l1[g] = *reinterpret_cast<const float4 *>(lp + u + 4);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        if (lo + tid * 8 + g * 2048 >= hi) continue;
+        const float l[8] = {l0[g].x, l0[g].y, l0[g].z, l0[g].w, l1[g].x, l1[g].y, l1[g].z, l1[g].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += __expf(fminf(l[e] - A, b[g][e] - B));
+      }
+    } else {
+      for (int u = lo + tid * 8; u < hi; u += 256 * 8) {
+        float b[8];
+        load8(a.drafter, a.drafter_bf16, qrow + u, b);
+        const float4 l0 = *reinterpret_cast<const float4 *>(lp + u);
+        const float4 l1 = *reinterpret_cast<const float4 *>(lp + u + 4);
+        const float l[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += __expf(fminf(l[e] - A, b[e] - B));
+      }
     }
   } else {
     for (int u = lo + tid; u < hi; u += 256)
