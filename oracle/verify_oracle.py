@@ -51,7 +51,10 @@ from their fp32 / bf16 bits):
    walk reaches a leaf it is drawn from p_cur, both by the inverse CDF at
    u_bonus (the smallest token whose running weight exceeds u_bonus times
    the total; a residual without mass falls back to p_cur).  The uniforms
-   are inputs.  Trees with branching nodes are not taken in this mode.
+   are inputs.  Trees with branching nodes are not taken in this mode.  A
+   draft id outside the vocabulary is a token neither model can emit
+   (p = q = 0 there), so the test 0 < 0 fails and it is rejected, as it is
+   in greedy mode, where it never equals a greedy token.
 10. Commit (the step after verify: sionic.ai page, section 1, generation
    resumes after the matching leading drafts; section 6, committing accepted
    tokens follows verify).  Each tree's accepted path, its root and then
@@ -66,8 +69,9 @@ from their fp32 / bf16 bits):
    bits, bias 7, 3 mantissa bits, largest finite 448, subnormal step 2^-9,
    no infinities), values rounded to nearest, ties to even.  Each LM-head
    row n gets the power-of-two scale s_n = 2^e, e the smallest integer with
-   max_k |W[n, k]| <= 448 * 2^e (1 for a zero row); each normalised hidden
-   row t likewise a_t from max |h_t|.  q = e4m3(value / scale) (an exact
+   max_k |W[n, k]| <= 448 * 2^e (1 for a zero row), and at least -126, so
+   that every scale is a normal fp32 number; each normalised hidden row t
+   likewise a_t from max |h_t|.  q = e4m3(value / scale) (an exact
    division), and logits[t, n] = a_t s_n sum_k q_h[t, k] q_w[n, k].
 """
 from __future__ import annotations
@@ -279,8 +283,10 @@ def stochastic_walk(forest: Forest, root: int, p_of, q_of, draft_ids, u_accept, 
         c = ch[0]
         d = int(draft_ids[c])
         q = q_of(c)
-        lhs, rhs = float(u_accept[c]) * float(q[d]), float(p[d])
-        margin = min(margin, abs(lhs - rhs) / max(float(p[d]), float(q[d]), 1e-300))
+        inside = 0 <= d < len(p)
+        lhs = float(u_accept[c]) * float(q[d]) if inside else 0.0
+        rhs = float(p[d]) if inside else 0.0
+        margin = min(margin, abs(lhs - rhs) / max(rhs, lhs, 1e-300))
         if lhs < rhs:
             cur, acc = c, acc + 1
             continue
@@ -351,7 +357,7 @@ def e4m3(x) -> np.ndarray:
 
 
 def pow2_scale(amax: float) -> float:
-    """Smallest 2^e with amax <= 448 * 2^e (1 when amax is 0)."""
+    """Smallest 2^e, e >= -126, with amax <= 448 * 2^e (1 when amax is 0)."""
     if amax == 0.0:
         return 1.0
     e = int(np.ceil(np.log2(amax / 448.0)))
@@ -359,7 +365,7 @@ def pow2_scale(amax: float) -> float:
         e += 1
     while amax <= 448.0 * 2.0 ** (e - 1):
         e -= 1
-    return 2.0 ** e
+    return 2.0 ** max(e, -126)
 
 
 def pow2_scales(amax) -> np.ndarray:
@@ -369,7 +375,7 @@ def pow2_scales(amax) -> np.ndarray:
     e = np.ceil(np.log2(np.where(pos, amax, 448.0) / 448.0))
     e = np.where(amax > 448.0 * np.exp2(e), e + 1, e)
     e = np.where(amax <= 448.0 * np.exp2(e - 1), e - 1, e)
-    return np.where(pos, np.exp2(e), 1.0)
+    return np.where(pos, np.exp2(np.maximum(e, -126.0)), 1.0)
 
 
 def lm_head_fp8(cfg, w_lm, hs: np.ndarray, chunk: int = 8192, scales=None) -> np.ndarray:

@@ -121,3 +121,58 @@ def test_fp8_verify_step():
     # sanity only (the bounds are pinned above): the FP8 head tracks the bf16 one
     a8, ab = res8["logits"].ravel(), ref["logits"].ravel()
     assert np.abs(a8 - ab).max() > 0 and np.corrcoef(a8, ab)[0, 1] > 0.99
+
+
+def test_forced_scales_hand_values():
+    # lm_head_fp8(scales=...) quantises a row at a given power of two instead
+    # of its own.  Row h = (1.75, 0.5, -1.7, 0...): its own scale is 2^-8
+    # (1.75 = 448 * 2^-8 sits on the boundary).  The LM head has one-hot rows
+    # W[n] = e_n, so logit n is the dequantised h[n] (W's own scale 2^-8,
+    # code 256, dequantised 1 exactly).
+    h = np.zeros((1, 64))
+    h[0, :3] = [1.75, 0.5, -1.7]
+    w = np.eye(3, 64)
+    cfg = {"dtype": "f64"}
+    # own scale 2^-8: codes 448, 128, -435.2 -> -448 (step 32 above 256;
+    # 435.2 / 32 = 13.6 rounds to 14); dequantised 1.75, 0.5, -1.75
+    np.testing.assert_array_equal(O.lm_head_fp8(cfg, w, h), [[1.75, 0.5, -1.75]])
+    # the next higher scale 2^-7: 224, 64, -217.6 -> -224 (step 16: 13.6 -> 14);
+    # the same values
+    np.testing.assert_array_equal(O.lm_head_fp8(cfg, w, h, scales=[2.0 ** -7]), [[1.75, 0.5, -1.75]])
+    # the next lower scale 2^-9: 896 and -870.4 lie past 448 and are held at
+    # +-448 (0.875 after dequantisation); 0.5 -> 256 exactly
+    np.testing.assert_array_equal(O.lm_head_fp8(cfg, w, h, scales=[2.0 ** -9]), [[0.875, 0.5, -0.875]])
+    # a row far below its scale: 2^-2 makes 0.5 -> 2, 1.75 -> 7, -1.7 -> -6.8
+    # (step 0.5 in [4, 8): 13.6 -> 14 halves: -7); all exact
+    np.testing.assert_array_equal(O.lm_head_fp8(cfg, w, h, scales=[0.25]), [[1.75, 0.5, -1.75]])
+    # a scale so large the values fall below e4m3's subnormal steps: 2^3 makes
+    # 0.5 -> 2^-4 (code 32 * 2^-9), 1.75 -> 0.21875, -1.7 -> -0.2125, step 2^-6
+    # below 2^-2 but 2^-5 in [2^-3, 2^-2): 0.2125 / 2^-5 = 6.8 -> 7
+    np.testing.assert_array_equal(O.lm_head_fp8(cfg, w, h, scales=[8.0]), [[1.75, 0.5, -1.75]])
+
+
+def test_forced_scale_saturation_differs_from_the_own_scale():
+    # a row with several values past 448 at the forced lower scale: each is
+    # held at +-448, the rest quantised normally
+    h = np.zeros((2, 64))
+    h[0, :4] = [3.0, -2.9, 2.0, 0.75]          # own scale 2^-7 (448 * 2^-7 = 3.5)
+    h[1, :4] = [0.0, 0.0, 0.0, 1.0]            # own scale 2^-8
+    w = np.eye(4, 64)
+    got = O.lm_head_fp8({"dtype": "f64"}, w, h, scales=[2.0 ** -8, 2.0 ** -8])
+    # row 0 at 2^-8: 768 -> 448, -742.4 -> -448, 512 -> 448, 192 -> 192
+    np.testing.assert_array_equal(got[0], [1.75, -1.75, 1.75, 0.75])
+    np.testing.assert_array_equal(got[1], [0.0, 0.0, 0.0, 1.0])
+    own = O.lm_head_fp8({"dtype": "f64"}, w, h)
+    np.testing.assert_array_equal(own[0], [3.0, -3.0, 2.0, 0.75])   # -371.2 at 2^-7 -> -384 (step 32 above 256)
+
+
+def test_scale_floor_keeps_scales_normal():
+    # the smallest exponent is -126: tiny rows use 2^-126 and stay exact when
+    # representable at that scale
+    assert O.pow2_scale(1e-40) == 2.0 ** -126 and O.pow2_scale(448.0 * 2.0 ** -126) == 2.0 ** -126
+    assert O.pow2_scale(448.0 * 2.0 ** -126 * 1.001) == 2.0 ** -125
+    np.testing.assert_array_equal(O.pow2_scales([1e-40, 0.0, 448.0 * 2.0 ** -130]), [2.0 ** -126, 1.0, 2.0 ** -126])
+    w = np.zeros((1, 64))
+    w[0, 0] = 2.0 ** -130                       # 2^-4 at the floor scale: an e4m3 value
+    h = np.ones((1, 64)) * 448.0
+    np.testing.assert_array_equal(O.lm_head_fp8({"dtype": "f64"}, w, h), [[448.0 * 2.0 ** -130]])
