@@ -239,7 +239,7 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
                                          nullptr);
         if (fp8)
           sv::launch_quant_fp8_blocked(static_cast<const uint16_t *>(w_lm), h->w_lm8, h->w_scale, int(V), int(H),
-                                       nullptr);
+                                       h->d_bad, nullptr);
         else
           sv::launch_bf16_to_f16_blocked(static_cast<const uint16_t *>(w_lm), wlm16, int(V), int(H), h->d_bad,
                                          nullptr);
@@ -253,7 +253,9 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
       }
       if (bad != 0) {
         release(h);
-        return fail(SV_ERR_UNSUPPORTED, std::to_string(bad) + " weight values exceed the fp16 range (|w| > 65504)");
+        return fail(SV_ERR_UNSUPPORTED,
+                    std::to_string(bad) + (fp8 ? " weight values are not finite, or W_o values exceed the fp16 range"
+                                               : " weight values exceed the fp16 range (|w| > 65504) or are not finite"));
       }
       h->w_o = wo16;
       h->w_o_blk = wo_blk;
@@ -381,6 +383,17 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   if (!out->accept_len || !out->bonus || !out->last_row || !out->surv_sum || !out->argmax || !out->row_max ||
       !out->row_lse || !out->overlap || !out->survival)
     return fail(SV_ERR_INVALID_ARG, "every output except logits must be a non-null device pointer");
+  {
+    const bool samp = in->mode == SV_MODE_SAMPLE;
+    const sv::RunPointers rp{{in->kv_tokens > 0 ? in->kv_k : nullptr, in->kv_tokens > 0 ? in->kv_v : nullptr,
+                              in->q_rows, in->k_rows, in->v_rows, plan.n_draft > 0 ? in->drafter_logits : nullptr,
+                              out->logits},
+                             {in->draft_ids, samp ? in->u_accept : nullptr, samp ? in->u_bonus : nullptr,
+                              out->accept_len, out->bonus, out->last_row, out->surv_sum, out->argmax, out->row_max,
+                              out->row_lse, out->overlap, out->survival}};
+    const int ac = sv::check_alignment(rp, &err);
+    if (ac != sv::P_OK) return fail(sv_status(ac), err);
+  }
   const sv::MetaLayout lay =
       sv::meta_layout(plan.n, plan.R, plan.n_draft, int(plan.items.size()), int(plan.runs.size()),
                       plan.R * dm.Hkv * plan.qg_max);

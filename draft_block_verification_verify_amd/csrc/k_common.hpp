@@ -73,18 +73,23 @@ __device__ __forceinline__ void split_bf2(float x, float y, uint32_t &hi, uint32
   lo = cvt_bf2(x - __uint_as_float(hi << 16), y - __uint_as_float(hi & 0xFFFF0000u));
 }
 
-// 8 bf16 -> 8 fp16.  Exact for |x| in the fp16 normal range (a bf16
-// significand fits in fp16's); tiny values become fp16 subnormals.
+// 8 bf16 -> 8 fp16, round to nearest even.  Exact for 0 and for 2^-17 <=
+// |x| <= 65504 (a bf16 significand has 8 bits, so its last bit is at least
+// 2^-24, fp16's subnormal step, from 2^-17 up); smaller magnitudes become the
+// nearest multiple of 2^-24.
 __device__ __forceinline__ uint4 bf8_to_h8(uint4 v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   uint32_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xFFFF0000u);
-    o[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+    o[i] = uint32_t(f2h(lo)) | (uint32_t(f2h(hi)) << 16);
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
+
+// A weight the fp16 copy cannot hold: |w| > 65504, infinite or NaN.
+__device__ __forceinline__ int not_f16(float w) { return !(fabsf(w) <= 65504.f); }
 
 // D(32x32) += A(32x16) * B(16x32).  Lane l supplies A[l%32][8*(l/32)+0..7],
 // B[8*(l/32)+0..7][l%32]; acc element j of lane l is

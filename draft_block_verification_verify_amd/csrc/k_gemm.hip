@@ -31,6 +31,7 @@
 
 #include "k_common.hpp"
 #include "k_dma.hpp"
+#include "k_fp8.hpp"
 #include "launch.hpp"
 
 namespace sv {
@@ -882,35 +883,8 @@ void launch_stats_from_logits(const float *logits, int rows, int V, int tile, fl
 // partials of 4 columns (16-B loads, splits unrolled by 4), keeps h in LDS,
 // then scales.
 // ----------------------------------------------------------------------------
-// FP8 (OCP e4m3) encoding: 4 exponent bits (bias 7), 3 mantissa bits, largest
-// finite 448, subnormal step 2^-9; rounded to nearest, ties to even.
+// FP8 (OCP e4m3) operands: e4m3_code and fp8_exponent come from k_fp8.hpp.
 // ----------------------------------------------------------------------------
-
-// code of x, |x| <= 448
-__device__ __forceinline__ uint32_t e4m3_code(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float a = fabsf(x);
-  uint32_t code;
-  if (a < 0.015625f) {                      // below 2^-6: multiples of 2^-9
-    code = uint32_t(rintf(a * 512.0f));     // exact product; rintf rounds half to even
-  } else {
-    const uint32_t b = __float_as_uint(a);
-    const uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) & ~0xFFFFFu;   // 3 mantissa bits, half to even
-    const int e = int(r >> 23) - 127;
-    code = (uint32_t(e + 7) << 3) | ((r >> 20) & 7u);
-  }
-  return sign | code;
-}
-
-// smallest e with amax <= 448 * 2^e (0 for amax == 0)
-__device__ __forceinline__ int fp8_exponent(float amax) {
-  if (!(amax > 0.0f)) return 0;
-  int e = int(ceilf(log2f(amax / 448.0f)));
-  while (amax > ldexpf(448.0f, e)) ++e;
-  while (amax <= ldexpf(448.0f, e - 1)) --e;
-  return e;
-}
 
 // 16 consecutive values (already divided by the row scale) -> 16 codes
 __device__ __forceinline__ uint4 e4m3_pack16(const float (&v)[16]) {
@@ -928,15 +902,25 @@ __device__ __forceinline__ int64_t fp8_blocked_off(int64_t row, int c16, int K) 
   return ((row >> 8) * (K >> 6) + kb) * 16384 + R * 64 + ((q ^ ((R >> 1) & 3)) << 4);
 }
 
+// Counts weights that are not finite into *bad (such a row cannot be
+// scaled); its codes are still written, from a bounded scale.
 __global__ __launch_bounds__(256) void quant_fp8_blocked_kernel(const uint16_t *__restrict__ src,
                                                                uint8_t *__restrict__ dst, float *__restrict__ scale,
-                                                               int rows, int K) {
+                                                               int rows, int K, int32_t *__restrict__ bad) {
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   const bool live = row < rows;
   float m = 0.f;
+  int n_bad = 0;
   if (live)
-    for (int k = tid; k < K; k += 256) m = fmaxf(m, fabsf(bf2f(src[row * K + k])));
+    for (int k = tid; k < K; k += 256) {
+      const float w = bf2f(src[row * K + k]);
+      if (fp8_weight_ok(w))
+        m = fmaxf(m, fabsf(w));
+      else
+        ++n_bad;
+    }
+  if (n_bad) atomicAdd(bad, n_bad);
   m = wave_max(m);
   __shared__ float red[4];
   if ((tid & 63) == 0) red[tid >> 6] = m;
@@ -951,9 +935,10 @@ __global__ __launch_bounds__(256) void quant_fp8_blocked_kernel(const uint16_t *
   if (tid == 0) scale[row] = ldexpf(1.0f, e);
 }
 
-void launch_quant_fp8_blocked(const uint16_t *src, uint8_t *dst, float *scale, int rows, int K, hipStream_t s) {
+void launch_quant_fp8_blocked(const uint16_t *src, uint8_t *dst, float *scale, int rows, int K, int32_t *bad,
+                              hipStream_t s) {
   const int padded = (rows + 255) / 256 * 256;
-  hipLaunchKernelGGL(quant_fp8_blocked_kernel, dim3(padded), dim3(256), 0, s, src, dst, scale, rows, K);
+  hipLaunchKernelGGL(quant_fp8_blocked_kernel, dim3(padded), dim3(256), 0, s, src, dst, scale, rows, K, bad);
 }
 
 __global__ __launch_bounds__(1024) void norm_kernel(const float *part, int splits, int64_t split_stride, int hidden,
@@ -1040,9 +1025,9 @@ void launch_norm(const float *part, int splits, int64_t split_stride, int rows, 
 
 
 // ----------------------------------------------------------------------------
-// weight preparation (once, at handle creation): bf16 -> fp16.  Exact for
-// values in the fp16 normal range; tiny values become fp16 subnormals.
-// Counts values outside the fp16 range (they would become infinities).
+// weight preparation (once, at handle creation): bf16 -> fp16, round to
+// nearest even (exact for 0 and 2^-17 <= |w| <= 65504; see bf8_to_h8).
+// Counts values the copy cannot hold (|w| > 65504, infinities, NaN).
 // ----------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint16_t *__restrict__ src, uint16_t *__restrict__ dst,
@@ -1054,7 +1039,7 @@ __global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint16_t *__rest
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float lo = __uint_as_float(w[k] << 16), hi = __uint_as_float(w[k] & 0xFFFF0000u);
-      local_bad += (fabsf(lo) > 65504.f) + (fabsf(hi) > 65504.f);
+      local_bad += not_f16(lo) + not_f16(hi);
     }
     reinterpret_cast<uint4 *>(dst)[i] = bf8_to_h8(v);
   }
@@ -1078,7 +1063,7 @@ __global__ __launch_bounds__(256) void bf16_to_f16_blocked_kernel(const uint16_t
       const uint32_t w[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        local_bad += (fabsf(__uint_as_float(w[k] << 16)) > 65504.f) + (fabsf(__uint_as_float(w[k] & 0xFFFF0000u)) > 65504.f);
+        local_bad += not_f16(__uint_as_float(w[k] << 16)) + not_f16(__uint_as_float(w[k] & 0xFFFF0000u));
       v = bf8_to_h8(b);
     }
     reinterpret_cast<uint4 *>(dst)[i] = v;

@@ -423,6 +423,9 @@ __global__ __launch_bounds__(64) void swalk_kernel(VocabArgs a, SampleArgs sa) {
   int c;
   while ((c = sa.row_child[cur]) >= 0) {
     const int d = a.draft_ids[c];
+    // a token outside the vocabulary has target probability 0: rejected,
+    // and nothing is loaded for it
+    if (d < 0 || d >= a.V) break;
     const float pd = p_at(a, cur, d);
     const int dr = a.row_draft[c];
     const float qd = __expf(drafter_at(a, dr, d) - a.lse_q[dr]);

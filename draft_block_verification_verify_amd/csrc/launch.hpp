@@ -121,8 +121,9 @@ void launch_norm(const float *part, int splits, int64_t split_stride, int rows, 
 void launch_gemm_fp8(const GemmArgs &g, hipStream_t s);
 // bf16 [rows, K] row-major -> e4m3 blocked layout (blocked_elems(rows, K)
 // bytes, K % 64 == 0) and scale[] (rows padded to 256; padding rows: codes 0,
-// scale 1).
-void launch_quant_fp8_blocked(const uint16_t *src, uint8_t *dst, float *scale, int rows, int K, hipStream_t s);
+// scale 1).  Adds the count of weights that are not finite to *bad.
+void launch_quant_fp8_blocked(const uint16_t *src, uint8_t *dst, float *scale, int rows, int K, int32_t *bad,
+                              hipStream_t s);
 
 // bf16 -> fp16 copy of n values (n % 8 == 0); adds the count of values
 // outside the fp16 range to *bad (device int).

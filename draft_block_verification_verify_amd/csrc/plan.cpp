@@ -65,6 +65,26 @@ int check_dims(const Dims &dm, std::string *err) {
   return P_OK;
 }
 
+const char *const kWideNames[RunPointers::kWide] = {"kv_k", "kv_v", "q_rows", "k_rows",
+                                                    "v_rows", "drafter_logits", "logits"};
+const char *const kNarrowNames[RunPointers::kNarrow] = {"draft_ids", "u_accept", "u_bonus", "accept_len",
+                                                        "bonus",     "last_row", "surv_sum", "argmax",
+                                                        "row_max",   "row_lse",  "overlap",  "survival"};
+
+int check_alignment(const RunPointers &p, std::string *err) {
+  for (int i = 0; i < RunPointers::kWide; ++i)
+    if (reinterpret_cast<uintptr_t>(p.wide[i]) % 16 != 0) {
+      *err = cat(kWideNames[i], " must be 16-byte aligned");
+      return P_INVALID;
+    }
+  for (int i = 0; i < RunPointers::kNarrow; ++i)
+    if (reinterpret_cast<uintptr_t>(p.narrow[i]) % 4 != 0) {
+      *err = cat(kNarrowNames[i], " must be 4-byte aligned");
+      return P_INVALID;
+    }
+  return P_OK;
+}
+
 // Up to 64 partial records per query vector, at least 16 Ki and at most
 // 384 Ki records ((d + 2) floats each).
 int64_t slot_capacity(const Dims &dm) {

@@ -108,6 +108,23 @@ enum PlanStatus { P_OK = 0, P_INVALID = -1, P_BAD_TREE = -2, P_CAPACITY = -3, P_
 // Check the model description and capacities.
 int check_dims(const Dims &dm, std::string *err);
 
+// Device buffers of one run.  The kernels move the large ones (`wide`: KV
+// cache, row q/k/v, drafter logits, caller logits) with 16-byte vector
+// accesses and the small per-row and per-tree arrays (`narrow`: draft ids,
+// uniforms, the outputs) with 4-byte ones.  Null entries are not checked
+// here.
+struct RunPointers {
+  static constexpr int kWide = 7, kNarrow = 12;
+  const void *wide[kWide];
+  const void *narrow[kNarrow];
+};
+extern const char *const kWideNames[RunPointers::kWide];
+extern const char *const kNarrowNames[RunPointers::kNarrow];
+
+// P_INVALID, naming the first buffer that is not 16-byte (wide) or 4-byte
+// (narrow) aligned; P_OK otherwise.
+int check_alignment(const RunPointers &p, std::string *err);
+
 // Validate the host inputs of one run and build its plan.  `slot_cap` bounds
 // plan->slots; the work split is coarsened until it fits.  `target_items`
 // is the run (workgroup) count to aim for.

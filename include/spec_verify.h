@@ -69,8 +69,9 @@ typedef enum sv_mode { SV_MODE_GREEDY = 0, SV_MODE_SAMPLE = 1 } sv_mode;
  * and each normalised hidden row t is divided by a power of two, s_n = 2^e
  * with e the smallest integer such that max |row| <= 448 * 2^e (1 for a zero
  * row), and rounded to the nearest e4m3 value (ties to even); logits[t, n] =
- * a_t s_n sum_k q_h[t, k] q_w[n, k], accumulated in fp32.  W_o stays in the
- * native format. */
+ * a_t s_n sum_k q_h[t, k] q_w[n, k], accumulated in fp32.  Exponents below
+ * -126 are raised to -126, so that every scale is a normal fp32 number.  W_o
+ * stays in the native format. */
 typedef enum sv_weights { SV_WEIGHTS_NATIVE = 0, SV_WEIGHTS_FP8 = 1 } sv_weights;
 
 /* Model shape and capacities, fixed for the handle's lifetime. */
@@ -96,7 +97,14 @@ typedef struct sv_handle sv_handle;
  * root (parent -1); for a non-root row i of the tree starting at s,
  * s <= parent[i] < i.  Roots are numbered in row order and index the
  * root_kv_* arrays.  Non-root ("draft") rows are numbered in row order and
- * index drafter_logits. */
+ * index drafter_logits.
+ *
+ * Device buffers: kv_k, kv_v, q_rows, k_rows, v_rows, drafter_logits (and
+ * the outputs' logits) must be 16-byte aligned, the other device arrays
+ * 4-byte aligned (SV_ERR_INVALID_ARG otherwise, before anything is
+ * enqueued).  A draft id may be any int32: one outside [0, V) is a token
+ * neither model can emit, so it is never accepted (in SV_MODE_SAMPLE its
+ * target probability is 0), and nothing is read for it. */
 typedef struct sv_inputs {
   int32_t n_rows;              /* 1 .. max_rows                                 */
   int32_t n_roots;             /* number of trees (rows with parent -1)         */
@@ -110,7 +118,7 @@ typedef struct sv_inputs {
   const void *q_rows;          /* DEVICE [n_rows, Hq, d]  queries before RoPE   */
   const void *k_rows;          /* DEVICE [n_rows, Hkv, d] keys before RoPE      */
   const void *v_rows;          /* DEVICE [n_rows, Hkv, d]                       */
-  const int32_t *draft_ids;    /* DEVICE [n_rows] token at each row; roots ignored */
+  const int32_t *draft_ids;    /* DEVICE [n_rows] token at each row; roots ignored; see above for ids outside [0, V) */
   const void *drafter_logits;  /* DEVICE [n_rows - n_roots, V]                  */
   int32_t mode;                /* sv_mode; 0 (greedy) when zero-initialised     */
   const float *u_accept;       /* DEVICE [n_rows] uniforms in [0, 1), SV_MODE_SAMPLE only; roots ignored */
@@ -134,14 +142,16 @@ typedef struct sv_outputs {
 
 /* Create a handle on the current device.  w_o is DEVICE [hidden, Hq*d] and
  * w_lm is DEVICE [vocab, hidden], both row-major in cfg->dtype.  For SV_BF16
- * the handle converts them once into fp16 copies it owns (exact for bf16
- * values of magnitude up to 65504; larger weights fail with
- * SV_ERR_UNSUPPORTED), or with SV_WEIGHTS_FP8 W_lm into e4m3 codes and row
- * scales, and the caller's buffers are not used afterwards; for SV_F32 they
- * are borrowed for the handle's lifetime.  Allocates the handle's
- * device scratch (sized from the capacities) and pinned host staging;
- * synchronises the device.  Fails with SV_ERR_UNSUPPORTED unless the device
- * is gfx950. */
+ * the handle converts them once into fp16 copies it owns, rounding to
+ * nearest even: exact for 0 and every bf16 value with 2^-17 <= |w| <=
+ * 65504, smaller magnitudes become the nearest multiple of 2^-24; a weight
+ * above 65504 in magnitude, infinite or NaN fails with SV_ERR_UNSUPPORTED.
+ * With SV_WEIGHTS_FP8, W_lm becomes e4m3 codes and row scales instead (a
+ * weight that is not finite fails with SV_ERR_UNSUPPORTED).  The caller's
+ * bf16 buffers are not used after create returns; for SV_F32 they are
+ * borrowed for the handle's lifetime.  Allocates the handle's device scratch
+ * (sized from the capacities) and pinned host staging; synchronises the
+ * device.  Fails with SV_ERR_UNSUPPORTED unless the device is gfx950. */
 sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *w_lm,
                              sv_handle **out);
 
@@ -150,11 +160,16 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
  * u_accept and u_bonus and fails with SV_ERR_UNSUPPORTED when a row has
  * more than one child.
  * Host arrays are read and copied before the call returns; device inputs and
- * outputs must stay valid until the stream passes the enqueued work.  Never
- * synchronises the host with the device.  Every argument, tree and capacity
- * check happens before anything is enqueued: on error nothing was enqueued
- * and the outputs are untouched.  A handle runs one step at a time: steps on
- * one handle must be ordered by the caller (same stream, or events). */
+ * outputs must stay valid until the stream passes the enqueued work.  The
+ * step's metadata goes through one of 4 pinned staging slots of the handle,
+ * used in turn: the call waits on the host only until the device has
+ * finished the metadata copy of the run 4 calls back on this handle, whose
+ * slot it reuses (so at most 4 runs of a handle are queued ahead of the
+ * device; with fewer queued the call never waits).  Every
+ * argument, tree, alignment and capacity check happens before anything is
+ * enqueued: on error nothing was enqueued and the outputs are untouched.  A
+ * handle runs one step at a time: steps on one handle must be ordered by the
+ * caller (same stream, or events). */
 sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *out, void *stream);
 
 /* Commit of the handle's most recent step: the step after verify, which keeps

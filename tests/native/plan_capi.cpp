@@ -61,3 +61,19 @@ extern "C" int svp_packs(const int *dims, int n_rows, int n_roots, const int32_t
   }
   return p.n_packs;
 }
+
+// Alignment check of a run's device buffers (the check spec_verify_run makes
+// before anything is enqueued): 7 wide and 12 narrow pointers, in the order
+// of sv::RunPointers.
+extern "C" int svp_check_alignment(const void *const *wide, const void *const *narrow, char *err, int err_cap) {
+  sv::RunPointers p{};
+  for (int i = 0; i < sv::RunPointers::kWide; ++i) p.wide[i] = wide[i];
+  for (int i = 0; i < sv::RunPointers::kNarrow; ++i) p.narrow[i] = narrow[i];
+  std::string e;
+  const int st = sv::check_alignment(p, &e);
+  if (err && err_cap > 0) {
+    std::strncpy(err, e.c_str(), size_t(err_cap - 1));
+    err[err_cap - 1] = 0;
+  }
+  return st;
+}
