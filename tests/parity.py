@@ -6,7 +6,12 @@ Tolerances (bf16 inputs, fp32 accumulation):
     below that the GPU choice must be a near-maximal token of the oracle
     logits and the GPU walk must agree with the GPU's own greedy tokens;
   * logits: |d| <= 2e-2 * max(|ref|, rms(ref row));
-  * probabilities p = softmax(logits): 1e-3 absolute;
+  * probabilities p = softmax(logits): 1e-3 absolute.  Without a logits
+    buffer this is checked on the top token from the row statistics alone:
+    p_max = exp(row_max - row_lse) moves by p_max * |d(row_max - row_lse)|,
+    held to 1e-3; row_lse itself is held to 1e-2 absolute (a common shift
+    of every logit moves lse but no probability, so lse gets the looser
+    bound);
   * overlaps and survival products: 2e-3 absolute.
 
 FP8 LM head (e4m3 W8A8): the activations are quantised from each side's own
@@ -17,8 +22,10 @@ midpoint may take the neighbouring code on the GPU, one e4m3 step away.  Per log
 differ by B[t, n] = a_t * sum over such elements k of step_k * |s_n q_w[n, k]|
 (fp8_bounds, from the oracle's own hidden state and weights); the logits are
 held to B plus 1e-3 * max(|ref|, rms) (fp32 accumulation), decisions are
-exact where the oracle's top-2 gap exceeds 2 max_n B[t, n] + 1e-2,
-probabilities to 2e-3.  A row whose largest value sits within 1e-2 of a
+exact where the oracle's top-2 gap exceeds 2 max_n B[t, n] + 1e-2.  Since
+lse moves by at most max_n B[t, n], the log-sum-exp is held to 1e-2 + max B
+and each probability p_n to 1e-3 + p_n (exp(B[t, n] + max B) - 1) (the
+top token's likewise, from the row statistics).  A row whose largest value sits within 1e-2 of a
 scale boundary (448 * 2^e) may take the other power of two: it is held to
 the nearer of the two references (fp8_alternatives).  Overlaps and survival
 keep 2e-3.
@@ -32,7 +39,8 @@ LOGIT_REL = 2e-2
 PROB_ABS = 1e-3
 OV_ABS = 2e-3
 EPS_H = 2e-3
-FP8_TOL = {"prob_abs": 2e-3}
+LSE_ABS = 1e-2
+FP8_TOL = {}
 
 
 def walk(parent, start, end, greedy, drafts):
@@ -109,6 +117,62 @@ def fp8_bounds(cfg, inp, rows, eps=EPS_H, chunk=8192):
     return {i: B[r] for r, i in enumerate(rows)}
 
 
+def _near_scale_boundary(h, rel):
+    from oracle import verify_oracle as O
+    amax = float(np.abs(h).max())
+    s = O.pow2_scale(amax)
+    return amax >= 448.0 * s * (1 - rel) or amax <= 448.0 * s / 2 * (1 + rel)
+
+
+def plant_fp8_margins(cfg, inp, rows, margin=1.5, seed=0, rel=1e-2):
+    """Give each listed row a clear FP8 decision.
+
+    First, a row whose hidden state has its largest |value| within `rel` of a
+    scale boundary (see fp8_alternatives) gets a fresh query vector (a row's
+    query enters only its own attention output), up to 8 draws.  Then row i
+    gets a token u_i (distinct per row) whose LM-head row moves along column
+    i of the pseudo-inverse of the rows' hidden states H (the oracle's, fp64),
+    so that logit u_i of row i rises to the row's largest logit + `margin`
+    and the other listed rows' logits of u_i keep their values (H G = I;
+    needs no more rows than the hidden width).  Writes inp.q_rows and
+    inp.w_lm (bf16 bits) in place and returns the tokens.  The margin is in
+    logit units, several times the FP8 flip bound (about 0.2 of the logits'
+    rms)."""
+    from oracle import verify_oracle as O
+    from draft_block_verification_verify_amd import workloads as W
+    cd = {"dtype": cfg["dtype"], "n_q_heads": cfg["n_q_heads"], "n_kv_heads": cfg["n_kv_heads"],
+          "head_dim": cfg["head_dim"], "rope_base": cfg["rope_base"], "norm_eps": cfg["norm_eps"]}
+    rows = list(rows)
+    hs = O.hidden_states(cd, O.inp_dict(inp), rows)
+    rq = np.random.default_rng([seed, 778])
+    for _ in range(8):
+        redo = [i for i in rows if _near_scale_boundary(hs[i], rel)]
+        if not redo:
+            break
+        for i in redo:
+            q = rq.standard_normal(inp.q_rows[i].shape).astype(np.float32)
+            inp.q_rows[i] = W.f32_to_bf16_bits(q) if cd["dtype"] == "bf16" else q
+        hs.update(O.hidden_states(cd, O.inp_dict(inp), redo))
+    H = np.stack([hs[i] for i in rows])
+    assert H.shape[0] <= H.shape[1], "more rows than the hidden width"
+    lg = O.lm_head(cd, inp.w_lm, H)
+    G = np.linalg.pinv(H)
+    toks = np.random.default_rng([seed, 777]).choice(inp.w_lm.shape[0], size=len(rows), replace=False)
+    w = O.decode(inp.w_lm[toks], cd["dtype"])
+    delta = lg.max(axis=1) + margin - lg[np.arange(len(rows)), toks]
+    w_new = w + (G * delta[None, :]).T
+    inp.w_lm[toks] = W.f32_to_bf16_bits(w_new.astype(np.float32))
+    return toks
+
+
+def fp8_clear_fraction(ref, rows, bound, alt, gap=GAP):
+    """Fraction of the listed rows whose FP8 decision is held exactly by
+    compare(): oracle top-2 gap above 2 max B + gap and no second valid
+    scale."""
+    clear = [i for i in rows if i not in alt and ref["gap"][i] > gap + 2 * float(bound[i].max())]
+    return len(clear) / max(1, len(rows))
+
+
 def fp8_alternatives(cfg, inp, rows, rel=1e-2):
     """Rows whose oracle hidden state has its largest |value| within `rel`
     of a scale boundary (448 * 2^e): the GPU's own hidden state may take the
@@ -151,8 +215,9 @@ def compare(ref, gpu, parent, drafts, rows=None, logits_ref=None, logits_gpu=Non
     parent = list(np.asarray(parent))
     n = len(parent)
     rows = list(range(n)) if rows is None else list(rows)
+    lse_t = tol.get("lse_abs", LSE_ABS)
     worst = {"argmax_mismatch_clear": 0, "near_ties": 0, "ov": 0.0, "surv": 0.0, "lse": 0.0,
-             "logit": 0.0, "prob": 0.0}
+             "top_prob": 0.0, "logit": 0.0, "prob": 0.0}
     gap = ref["gap"]
 
     def lse_max(x):
@@ -181,13 +246,19 @@ def compare(ref, gpu, parent, drafts, rows=None, logits_ref=None, logits_gpu=Non
         worst["ov"] = max(worst["ov"], abs(float(gpu["overlap"][i]) - ref["overlap"][i]))
         worst["surv"] = max(worst["surv"], abs(float(gpu["survival"][i]) - ref["survival"][i]))
         refs = [(ref["row_lse"][i], ref["row_max"][i])] + ([lse_max(alt[i])] if i in alt else [])
-        e_lse = min(max(abs(float(gpu["row_lse"][i]) - l) / max(1.0, abs(l)),
-                        abs(float(gpu["row_max"][i]) - m) / max(1.0, abs(l))) for l, m in refs)
+        gl, gm = float(gpu["row_lse"][i]), float(gpu["row_max"][i])
+        bmax = float(bound[i].max()) if i in bound else 0.0
+        # (with a flip bound: the excess over what code flips can move)
+        e_lse = min(abs(gl - l) for l, m in refs) - bmax
+        # the top token's probability from the row statistics alone
+        e_top = min(abs(np.exp(gm - gl) - np.exp(m - l)) - np.exp(m - l) * np.expm1(2 * bmax) for l, m in refs)
         worst["lse"] = max(worst["lse"], e_lse)
+        worst["top_prob"] = max(worst["top_prob"], e_top)
     assert worst["argmax_mismatch_clear"] == 0, worst
     assert worst["ov"] <= OV_ABS, worst
     assert worst["surv"] <= OV_ABS, worst
-    assert worst["lse"] <= logit_t, worst
+    assert worst["lse"] <= lse_t, worst
+    assert worst["top_prob"] <= prob_t, worst
     if logits_ref is not None and logits_gpu is not None:
         for i in rows:
             lg = logits_gpu[i].astype(np.float64)
@@ -195,13 +266,15 @@ def compare(ref, gpu, parent, drafts, rows=None, logits_ref=None, logits_gpu=Non
             e_logit, e_prob = np.inf, np.inf
             for lr in [logits_ref[i]] + ([alt[i]] if i in alt else []):
                 rms = np.sqrt(np.mean(lr * lr))
+                pr = np.exp(lr - lse_max(lr)[0])
                 if i in bound:   # excess over the flip bound
                     err = np.maximum(np.abs(lg - lr) - bound[i], 0.0) / np.maximum(np.abs(lr), rms)
+                    perr = np.abs(pr - pg) - pr * np.expm1(bound[i] + float(bound[i].max()))
                 else:
                     err = np.abs(lg - lr) / np.maximum(np.abs(lr), rms)
-                pr = np.exp(lr - lse_max(lr)[0])
+                    perr = np.abs(pr - pg)
                 if float(err.max()) < e_logit:
-                    e_logit, e_prob = float(err.max()), float(np.abs(pr - pg).max())
+                    e_logit, e_prob = float(err.max()), float(perr.max())
             key = "logit_over_bound" if i in bound else "logit"
             worst[key] = max(worst.get(key, 0.0), e_logit)
             worst["prob"] = max(worst["prob"], e_prob)
@@ -231,6 +304,38 @@ def compare(ref, gpu, parent, drafts, rows=None, logits_ref=None, logits_gpu=Non
     if report is not None:
         report.update(worst)
     return worst
+
+
+def sampled_trees(st, k=8):
+    """k trees of a full-size batch for the oracle to score: the first, middle
+    and last, the longest and the shortest prefix, and seeded others."""
+    R = st.n_roots
+    lens = np.asarray(st.root_kv_len)
+    want = {0, R // 2, R - 1, int(np.argmax(lens)), int(np.argmin(lens))}
+    r = np.random.default_rng(R)
+    while len(want) < min(k, R):
+        want.add(int(r.integers(0, R)))
+    return sorted(want)
+
+
+def walk_decisions(ref, gpu, parent, gap=GAP):
+    """Per tree (accept_len, bonus, last_row): the oracle's where every row
+    its walk consults has a top-2 gap above `gap` (compare() has asserted the
+    GPU equal there), the GPU's at a near tie (where either choice is
+    valid).  Returns the dict and the number of trees taken from the GPU."""
+    parent = list(np.asarray(parent))
+    out = {k: np.array(ref[k], copy=True) for k in ("accept_len", "bonus", "last_row")}
+    from_gpu = 0
+    for t, (s, e) in enumerate(tree_ranges(parent)):
+        j, clear = int(ref["last_row"][t]), True
+        while j >= 0:
+            clear = clear and ref["gap"][j] > gap
+            j = parent[j]
+        if not clear:
+            from_gpu += 1
+            for k in out:
+                out[k][t] = gpu[k][t]
+    return out, from_gpu
 
 
 def _softmax64(x):
@@ -273,6 +378,8 @@ def check_sample(parent, drafts, u_accept, u_bonus, logits_ref, drafter_ref, gpu
         def decision(cur, c):
             lc = np.asarray(logits_ref[cur], np.float64)
             d = int(drafts[c])
+            if not 0 <= d < len(lc):
+                return False, True            # a token outside the vocabulary: rejected
             p = _softmax64(lc)[d]
             q = _softmax64(drafter_ref[draft_index[c]])[d]
             lhs, rhs = float(u_accept[c]) * q, p

@@ -55,21 +55,21 @@ def run_steps(name, seed, steps):
     n, nd = st.n_rows, int((st.parent >= 0).sum())
     dc = DeviceCase(inp, with_logits=True, max_pos=int(st.pos.max()) + 1 + steps * (gamma + 1))
     kk_o, vv_o = a["kv_k"], a["kv_v"]
-    rep = {}
-    gpu = None
+    rep = {"walks_from_gpu": 0}
+    gpu = dec = None
     try:
         for r in range(steps):
             if r > 0:
                 rows = W.round_rows(cfg, seed, r, n, nd)
                 dc.next_step(gpu["accept_len"], rows)
-                parent, pos, off, ln = O.advance(a, gpu, gamma)
+                # the oracle's layout follows its own walk (the GPU's only at a near tie)
+                parent, pos, off, ln = O.advance(a, dec, gamma)
                 assert (dc.inp.st.pos == pos).all() and (dc.inp.st.root_kv_len == ln).all()
                 assert (dc.inp.st.parent == parent).all() and (dc.inp.st.root_kv_off == off).all()
                 a = dict(a, parent=parent, pos=pos, root_kv_off=off, root_kv_len=ln, **rows)
             a["kv_k"], a["kv_v"] = kk_o, vv_o
-            # plant from the GPU's own greedy tokens (a first run of the step)
-            dc.run()
-            W.plant_chain_drafts(dc.inp, dc.results()["argmax"], rnd=r)
+            # plant on the oracle's greedy tokens
+            W.plant_chain_drafts(dc.inp, O.target_greedy(c, a), rnd=r)
             dc.refresh()
             a["draft_ids"] = dc.inp.draft_ids.copy()
             dc.run()
@@ -78,8 +78,10 @@ def run_steps(name, seed, steps):
             P.check_self_consistency(a["parent"], a["draft_ids"], gpu)
             P.compare(ref, gpu, a["parent"], a["draft_ids"], logits_ref=ref["logits"], logits_gpu=gpu["logits"],
                       report=rep)
+            dec, from_gpu = P.walk_decisions(ref, gpu, a["parent"])
+            rep["walks_from_gpu"] += from_gpu
             dc.commit()
-            kk_o, vv_o = O.commit(c, a, gpu, kk_o, vv_o)
+            kk_o, vv_o = O.commit(c, a, dec, kk_o, vv_o)
             _compare_caches(dc, kk_o, vv_o, cfg.dtype, rep)
             rep[f"accept_mean_step{r}"] = float(np.mean(gpu["accept_len"]))
     finally:

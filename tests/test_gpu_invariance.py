@@ -1,0 +1,167 @@
+"""Invariances of the HIP verify step, GPU against GPU (needs an MI355X).
+
+* Branch alone: each row sees only its own tree's prefix and its ancestors
+  (onedev.kr SpecOPD summary, "what differs": ancestor-and-self mask, parent
+  map), so a proposal-tree branch scored inside a shared-stem batch, where it
+  shares attention packs with other branches, must score as it does alone
+  on stem[0:a_b].
+* Tree order: permuting the trees of a batch (which regroups the attention
+  packs and the work split) permutes the outputs and changes nothing else.
+
+Both runs of a comparison take the same projection path when their row
+counts are on the same side of 64, so their results differ only by fp32
+summation order in the attention merge: logits are held to 2e-4 of
+max(|l|, rms of the row), overlaps and survival to 1e-5, and every greedy
+token, accept length, bonus and last row exactly where the first run's
+top-2 gap exceeds 1e-3.  A 448-row batch against its 7-row branches changes
+path (fp16 activations above 64 rows, an fp16 hi + lo pair below), and is
+held to the parity tolerances instead (logits 2e-2 of max(|l|, rms),
+overlaps 2e-3, decisions exact where the gap exceeds 1e-2).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from draft_block_verification_verify_amd import workloads as W
+from tests import parity as P
+from tests.test_gpu_parity import MINIS, _record, _say
+
+pytestmark = pytest.mark.gpu
+
+SAME_PATH = {"logit": 2e-4, "ov": 1e-5, "gap": 1e-3}
+CROSS_PATH = {"logit": 2e-2, "ov": 2e-3, "gap": 1e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from draft_block_verification_verify_amd import binding
+    binding.lib()
+    yield
+
+
+def _run(inp):
+    from draft_block_verification_verify_amd.runner import DeviceCase
+    dc = DeviceCase(inp, with_logits=True)
+    try:
+        dc.run()
+        return dc.results()
+    finally:
+        dc.close()
+
+
+def _tree_rows(st):
+    roots = list(np.nonzero(np.asarray(st.parent) < 0)[0]) + [st.n_rows]
+    return [list(range(roots[t], roots[t + 1])) for t in range(st.n_roots)]
+
+
+def sub_forest(inp, order):
+    """The trees `order` of `inp` (in that order) as a batch of their own:
+    same prefixes (offset, length) in the same cache, same rows."""
+    st = inp.st
+    trs = _tree_rows(st)
+    draft_of = np.cumsum(st.parent >= 0) - 1
+    idx, parent = [], []
+    for t in order:
+        s0 = len(idx)
+        base = trs[t][0]
+        for i in trs[t]:
+            idx.append(i)
+            parent.append(-1 if st.parent[i] < 0 else s0 + int(st.parent[i]) - base)
+    idx = np.array(idx)
+    sub_st = W.Structure(np.array(parent, np.int32), st.pos[idx].astype(np.int32),
+                         st.root_kv_off[list(order)].copy(), st.root_kv_len[list(order)].copy(), st.kv_tokens)
+    drows = [int(draft_of[i]) for i in idx if st.parent[i] >= 0]
+    return dataclasses.replace(inp, st=sub_st, q_rows=inp.q_rows[idx], k_rows=inp.k_rows[idx],
+                               v_rows=inp.v_rows[idx], drafter_logits=inp.drafter_logits[drows],
+                               draft_ids=inp.draft_ids[idx].copy()), idx
+
+
+def _plant_on(inp, greedy, seed):
+    """Drafts: the parent's greedy token (from a first run) with probability
+    0.7, else a random token, so the walks go deep."""
+    r = np.random.default_rng(seed)
+    for i, p in enumerate(inp.st.parent):
+        if p >= 0:
+            inp.draft_ids[i] = int(greedy[p]) if r.random() < 0.7 else int(r.integers(0, inp.cfg.vocab))
+
+
+def _gap(logits):
+    top2 = np.partition(logits, -2, axis=1)[:, -2:]
+    return top2[:, 1] - top2[:, 0]
+
+
+def compare_runs(a, b, rows_a, rows_b, trees, tol, rep):
+    """Outputs of run a's rows rows_a against run b's rows rows_b (same rows
+    in both batches), and per tree (index in a, index in b, its rows in a,
+    its first row in b) the walk's outcome."""
+    la, lb = a["logits"][rows_a].astype(np.float64), b["logits"][rows_b].astype(np.float64)
+    rms = np.sqrt(np.mean(la * la, axis=1, keepdims=True))
+    e = np.abs(la - lb) / np.maximum(np.abs(la), rms)
+    rep["logit"] = max(rep.get("logit", 0.0), float(e.max()))
+    assert e.max() <= tol["logit"], e.max()
+    for k in ("overlap", "survival"):
+        d = float(np.abs(a[k][rows_a].astype(np.float64) - b[k][rows_b]).max())
+        rep[k] = max(rep.get(k, 0.0), d)
+        assert d <= tol["ov"], (k, d)
+    d = float(np.abs(a["row_lse"][rows_a].astype(np.float64) - b["row_lse"][rows_b]).max())
+    rep["lse"] = max(rep.get("lse", 0.0), d)
+    assert d <= tol["logit"] * 10, d
+    gap = _gap(la)
+    clear = gap > tol["gap"]
+    rep["near"] = rep.get("near", 0) + int((~clear).sum())
+    assert (a["argmax"][rows_a][clear] == b["argmax"][rows_b][clear]).all()
+    # per tree: the walk is decided identically where every row of the tree is clear
+    clear_row = {int(r): bool(c) for r, c in zip(rows_a, clear)}
+    for ta, tb, rows, start_b in trees:
+        if all(clear_row[int(r)] for r in rows):
+            # the last accepted row, as an offset into its tree
+            wa = (int(a["accept_len"][ta]), int(a["bonus"][ta]), int(a["last_row"][ta]) - int(rows[0]))
+            wb = (int(b["accept_len"][tb]), int(b["bonus"][tb]), int(b["last_row"][tb]) - int(start_b))
+            rep["walks_checked"] = rep.get("walks_checked", 0) + 1
+            assert wa == wb, (ta, tb, wa, wb)
+
+
+@pytest.mark.parametrize("n_trees,seed", [(9, 0), (9, 1), (64, 0)])
+def test_branch_alone_equals_branch_in_pack(n_trees, seed):
+    cfg = MINIS["c4m"]
+    if n_trees != cfg.anchors:
+        cfg = dataclasses.replace(cfg, cfg_id=cfg.cfg_id + 20, anchors=n_trees)
+    inp = W.make_inputs(cfg, seed)
+    W.sample_tree_drafts(inp)
+    first = _run(inp)
+    _plant_on(inp, first["argmax"], seed)
+    full = _run(inp)
+    trs = _tree_rows(inp.st)
+    tol = SAME_PATH if inp.st.n_rows <= 64 else CROSS_PATH
+    rep = {}
+    picks = sorted({0, 1, n_trees // 2, n_trees - 1})
+    for t in picks:
+        alone, idx = sub_forest(inp, [t])
+        _say(f"[branch alone] trees={n_trees} seed={seed} tree={t} anchor={int(inp.st.root_kv_len[t])}")
+        b = _run(alone)
+        compare_runs(full, b, np.array(trs[t]), np.arange(len(idx)), [(t, 0, trs[t], 0)], tol, rep)
+    _record(f"c4m/branch-alone/trees{n_trees}/seed{seed}", rep)
+
+
+@pytest.mark.parametrize("name,n_trees", [("c4m", 9), ("c4m", 64), ("c5m", 32), ("c5t", 96)])
+def test_tree_permutation(name, n_trees):
+    cfg = MINIS[name]
+    if cfg.kind == "tree" and n_trees != cfg.anchors:
+        cfg = dataclasses.replace(cfg, cfg_id=cfg.cfg_id + 20, anchors=n_trees)
+    inp = W.make_inputs(cfg, 3)
+    first = _run(inp)
+    _plant_on(inp, first["argmax"], 3)
+    a = _run(inp)
+    perm = np.random.default_rng(n_trees).permutation(inp.st.n_roots)
+    pinp, idx = sub_forest(inp, perm)
+    _say(f"[permutation] {name} trees={inp.st.n_roots} rows={inp.st.n_rows}")
+    b = _run(pinp)
+    rep = {}
+    trs, trs_b = _tree_rows(inp.st), _tree_rows(pinp.st)
+    compare_runs(a, b, idx, np.arange(len(idx)), [(int(t), k, trs[t], trs_b[k][0]) for k, t in enumerate(perm)],
+                 SAME_PATH, rep)
+    _record(f"{name}/tree-permutation", rep)
