@@ -128,7 +128,191 @@ void release(sv_handle *h) {
   delete h;
 }
 
+// Scratch buffers of the vocabulary stages of one run.
+struct VocabBufs {
+  float *logits;
+  uint16_t *p16;
+  float *t_max, *t_sum;
+  int32_t *t_arg;
+  int n_tiles;
+  float2 *dpart;
+  int n_dch;
+  float *lse_q, *opart;
+  int n_och;
+};
+
+// Arguments of the vocabulary stages (statistics, overlaps, acceptance, the
+// T = 1 draw) of one run, from its plan, its device metadata and buffers.
+sv::VocabArgs vocab_args(const sv::Plan &plan, const char *m, const sv::MetaLayout &lay, int V, bool bf16,
+                         const sv_inputs *in, const sv_outputs *out, const VocabBufs &b) {
+  sv::VocabArgs va{};
+  va.n = plan.n;
+  va.n_draft = plan.n_draft;
+  va.R = plan.R;
+  va.V = V;
+  va.row_parent = reinterpret_cast<const int32_t *>(m + lay.row_parent);
+  va.row_draft = reinterpret_cast<const int32_t *>(m + lay.row_draft);
+  va.draft_row = reinterpret_cast<const int32_t *>(m + lay.draft_row);
+  va.tree_start = reinterpret_cast<const int32_t *>(m + lay.tree_start);
+  va.tree_rows = reinterpret_cast<const int32_t *>(m + lay.tree_rows);
+  va.draft_ids = in->draft_ids;
+  va.drafter = in->drafter_logits;
+  va.drafter_bf16 = bf16 ? 1 : 0;
+  va.logits = b.logits;
+  va.p16 = b.p16;
+  va.t_max = b.t_max;
+  va.t_sum = b.t_sum;
+  va.t_arg = b.t_arg;
+  va.n_tiles = b.n_tiles;
+  va.dpart = b.dpart;
+  va.n_dch = b.n_dch;
+  va.dchunk = kDChunk;
+  va.lse_q = b.lse_q;
+  va.opart = b.opart;
+  va.n_och = b.n_och;
+  va.ochunk = kOChunk;
+  va.argmax = out->argmax;
+  va.accept_len = out->accept_len;
+  va.bonus = out->bonus;
+  va.last_row = out->last_row;
+  va.row_max = out->row_max;
+  va.row_lse = out->row_lse;
+  va.overlap = out->overlap;
+  va.survival = out->survival;
+  va.surv_sum = out->surv_sum;
+  return va;
+}
+
+// Device buffers of the fp32 path of one run.
+struct F32Bufs {
+  float *q_rot, *k_rot, *o_act, *h_part, *hn;
+  float *t_max, *t_sum;   // the LM head's tile statistics
+  int32_t *t_arg;
+};
+
+// fp32 models: RoPE, drafter statistics, attention, W_o, final norm, and the
+// LM head with its tile statistics, as plain fp32 kernels.  `begin(name)` /
+// `end()` bracket each stage (profiling events, or nothing).
+template <class Begin, class End>
+void enqueue_f32(const sv::Dims &dm, const sv_config &cfg, const char *m, const sv::MetaLayout &lay, const F32Bufs &b,
+                 const void *w_o, const void *w_lm, const sv_inputs *in, const sv::VocabArgs &va, hipStream_t stream,
+                 Begin &&begin, End &&end) {
+  const int n = va.n, Hq = dm.Hq, Hkv = dm.Hkv, D = dm.d, H = dm.hidden, V = dm.vocab;
+  begin("rope");
+  sv::launch_rope_f32(static_cast<const float *>(in->q_rows), static_cast<const float *>(in->k_rows), b.q_rot,
+                      b.k_rot, reinterpret_cast<const int32_t *>(m + lay.row_pos), n, Hq, Hkv, D,
+                      double(cfg.rope_base), stream);
+  end();
+  begin("drafter_stats");
+  sv::launch_drafter_partial(va, stream);
+  end();
+  sv::AttnF32Args af{};
+  af.kv_k = static_cast<const float *>(in->kv_k);
+  af.kv_v = static_cast<const float *>(in->kv_v);
+  af.k_rot = b.k_rot;
+  af.v_rows = static_cast<const float *>(in->v_rows);
+  af.q_rot = b.q_rot;
+  af.row_tree = reinterpret_cast<const int32_t *>(m + lay.row_tree);
+  af.tree_start = reinterpret_cast<const int32_t *>(m + lay.tree_start);
+  af.tree_rows = reinterpret_cast<const int32_t *>(m + lay.tree_rows);
+  af.tree_kv_len = reinterpret_cast<const int32_t *>(m + lay.tree_kv_len);
+  af.tree_kv_off = reinterpret_cast<const int64_t *>(m + lay.tree_kv_off);
+  af.row_anc = reinterpret_cast<const uint64_t *>(m + lay.row_anc);
+  af.out = b.o_act;
+  af.Hq = Hq;
+  af.Hkv = Hkv;
+  af.D = D;
+  begin("attention");
+  sv::launch_attn_f32(af, n, stream);
+  end();
+  begin("w_o");
+  sv::launch_gemm_f32(b.o_act, n, static_cast<const float *>(w_o), H, Hq * D, b.h_part, stream);
+  end();
+  begin("final_norm");
+  sv::launch_norm(b.h_part, 1, 0, n, H, cfg.norm_eps, sv::ACT_F32, b.hn, 0, nullptr, stream);
+  end();
+  begin("lm_head");
+  sv::launch_gemm_f32(b.hn, n, static_cast<const float *>(w_lm), V, H, va.logits, stream);
+  sv::launch_stats_from_logits(va.logits, n, V, 256, b.t_max, b.t_sum, b.t_arg, va.n_tiles, stream);
+  end();
+}
+
+// After the LM head: row statistics, overlaps, acceptance, and in T = 1 mode
+// the stochastic walk and the bonus draw.
+template <class Begin, class End>
+void enqueue_tail(const sv::VocabArgs &va, const sv_inputs *in, const char *m, const sv::MetaLayout &lay,
+                  int32_t *rej_child, float *rpart, hipStream_t stream, Begin &&begin, End &&end) {
+  if (va.n <= 64) {
+    // few rows: few tile records per row, so the overlap workgroups merge
+    // their own logsumexps and the two passes share one launch
+    begin("combine_overlap");
+    sv::launch_combine_overlap(va, stream);
+    end();
+  } else {
+    begin("row_combine");
+    sv::launch_row_combine(va, stream);
+    end();
+    begin("overlap");
+    sv::launch_overlap_partial(va, stream);
+    end();
+  }
+  begin("accept");
+  sv::launch_accept(va, stream);
+  end();
+  if (in->mode == SV_MODE_SAMPLE) {
+    sv::SampleArgs sa{};
+    sa.row_child = reinterpret_cast<const int32_t *>(m + lay.row_child);
+    sa.u_accept = in->u_accept;
+    sa.u_bonus = in->u_bonus;
+    sa.rej_child = rej_child;
+    sa.rpart = rpart;
+    begin("sample");
+    sv::launch_sample(va, sa, stream);
+    end();
+  }
+}
+
+// Validation of one run's arguments and its plan (shared by spec_verify_run
+// and spec_verify_run_static): nothing may be enqueued before this passes.
+sv_status check_run(const sv::Dims &dm, const sv_inputs *in, const sv_outputs *out, int64_t slot_cap,
+                    int target_items, int n_och, sv::Plan *plan, sv::MetaLayout *lay) {
+  sv::HostInputs hi{in->n_rows, in->n_roots, in->parent, in->pos, in->root_kv_off, in->root_kv_len, in->kv_tokens};
+  std::string err;
+  const int pc = sv::build_plan(dm, hi, slot_cap, target_items, plan, &err);
+  if (pc != sv::P_OK) return fail(sv_status(pc), err);
+  if (!in->q_rows || !in->k_rows || !in->v_rows || !in->draft_ids)
+    return fail(SV_ERR_INVALID_ARG, "q_rows, k_rows, v_rows and draft_ids must be non-null device pointers");
+  if (plan->n_draft > 0 && !in->drafter_logits)
+    return fail(SV_ERR_INVALID_ARG, "drafter_logits must be non-null when the block has draft rows");
+  if (in->mode != SV_MODE_GREEDY && in->mode != SV_MODE_SAMPLE)
+    return fail(SV_ERR_INVALID_ARG, "mode must be SV_MODE_GREEDY or SV_MODE_SAMPLE");
+  if (in->mode == SV_MODE_SAMPLE) {
+    if (!in->u_accept || !in->u_bonus) return fail(SV_ERR_INVALID_ARG, "SV_MODE_SAMPLE needs u_accept and u_bonus");
+    if (!plan->chains_only)
+      return fail(SV_ERR_UNSUPPORTED, "SV_MODE_SAMPLE takes chains: a row has more than one child");
+    if (n_och > 1024) return fail(SV_ERR_UNSUPPORTED, "SV_MODE_SAMPLE supports vocabularies up to 8388608 tokens");
+  }
+  if (in->kv_tokens > 0 && (!in->kv_k || !in->kv_v))
+    return fail(SV_ERR_INVALID_ARG, "kv_k and kv_v must be non-null when kv_tokens > 0");
+  if (!out->accept_len || !out->bonus || !out->last_row || !out->surv_sum || !out->argmax || !out->row_max ||
+      !out->row_lse || !out->overlap || !out->survival)
+    return fail(SV_ERR_INVALID_ARG, "every output except logits must be a non-null device pointer");
+  const bool samp = in->mode == SV_MODE_SAMPLE;
+  const sv::RunPointers rp{{in->kv_tokens > 0 ? in->kv_k : nullptr, in->kv_tokens > 0 ? in->kv_v : nullptr,
+                            in->q_rows, in->k_rows, in->v_rows, plan->n_draft > 0 ? in->drafter_logits : nullptr,
+                            out->logits},
+                           {in->draft_ids, samp ? in->u_accept : nullptr, samp ? in->u_bonus : nullptr,
+                            out->accept_len, out->bonus, out->last_row, out->surv_sum, out->argmax, out->row_max,
+                            out->row_lse, out->overlap, out->survival}};
+  const int ac = sv::check_alignment(rp, &err);
+  if (ac != sv::P_OK) return fail(sv_status(ac), err);
+  *lay = sv::meta_layout(plan->n, plan->R, plan->n_draft, int(plan->items.size()), int(plan->runs.size()),
+                         plan->R * dm.Hkv * plan->qg_max);
+  return SV_OK;
+}
+
 }  // namespace
+
 
 extern "C" {
 
@@ -190,17 +374,19 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
   };
   A(&h->d_meta, h->meta_cap);
   A(&h->q_rot, size_t(R * Hq * D * 4));       // bf16: hi + lo planes; fp32: one plane
-  A(&h->k_rot, size_t(R * Hkv * D * E));
+  A(&h->k_rot, size_t(R * Hkv * D * 4));      // bf16: hi + lo planes; fp32: one plane
   if (dm.dtype == SV_BF16) {
     A(&h->part_o, size_t(h->slot_cap * D * 4));
     A(&h->part_ml, size_t(h->slot_cap * 2 * 4));
   }
   // attention output: fp16 hi + lo planes, blocked fp16 (rows padded to 256), or fp32
-  A(&h->o_act, std::max<size_t>(size_t(R * Hq * D * 4), size_t(sv::blocked_elems(R, Hq * D) * 2)));
+  // (hi plane, then the lo plane one blocked capacity further)
+  A(&h->o_act, std::max<size_t>(size_t(R * Hq * D * 4), size_t(2 * sv::blocked_elems(R, Hq * D) * 2)));
   A(&h->h_part, h->h_part_floats * 4);
   // normalised rows: fp16 hi + lo planes (<= 64 rows) or the blocked fp16
-  // layout of the tiled LM head (rows padded to 256)
-  A(&h->hn, std::max<size_t>(size_t(R * H * 4), size_t(sv::blocked_elems(R, H) * 2)));
+  // layout of the tiled LM head (rows padded to 256) and a row-major fp16 lo
+  // plane, one blocked capacity further in both cases
+  A(&h->hn, std::max<size_t>(size_t(R * H * 4), size_t((sv::blocked_elems(R, H) + R * H) * 2)));
   A(&h->logits, size_t(R * V * 4));
   if (dm.dtype == SV_BF16 && R > 64 && V % 8 == 0) A(&h->p16, size_t(R * V * 2));
   A(&h->t_max, size_t(R * h->n_tiles_cap * 4));
@@ -231,7 +417,9 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
       e = hipMemsetAsync(h->d_bad, 0, 4, nullptr);
       // padding rows of the blocked activations are read by the LM head:
       // start them at zero
-      if (e == hipSuccess) e = hipMemsetAsync(h->hn, 0, std::max<size_t>(size_t(R * H * 4), size_t(sv::blocked_elems(R, H) * 2)), nullptr);
+      if (e == hipSuccess)
+        e = hipMemsetAsync(h->hn, 0, std::max<size_t>(size_t(R * H * 4), size_t((sv::blocked_elems(R, H) + R * H) * 2)),
+                           nullptr);
       if (e == hipSuccess) {
         sv::launch_bf16_to_f16(static_cast<const uint16_t *>(w_o), wo16, H * Hq * D, h->d_bad, nullptr);
         if (tiled)
@@ -359,44 +547,12 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   const hipStream_t stream = static_cast<hipStream_t>(stream_v);
 
   // ---- host-side validation and plan (nothing is enqueued before this passes)
-  sv::HostInputs hi{in->n_rows, in->n_roots, in->parent, in->pos, in->root_kv_off, in->root_kv_len, in->kv_tokens};
   sv::Plan plan;
-  std::string err;
-  const int pc = sv::build_plan(dm, hi, h->slot_cap, h->target_items, &plan, &err);
-  if (pc != sv::P_OK) return fail(sv_status(pc), err);
-  if (!in->q_rows || !in->k_rows || !in->v_rows || !in->draft_ids)
-    return fail(SV_ERR_INVALID_ARG, "q_rows, k_rows, v_rows and draft_ids must be non-null device pointers");
-  if (plan.n_draft > 0 && !in->drafter_logits)
-    return fail(SV_ERR_INVALID_ARG, "drafter_logits must be non-null when the block has draft rows");
-  if (in->mode != SV_MODE_GREEDY && in->mode != SV_MODE_SAMPLE)
-    return fail(SV_ERR_INVALID_ARG, "mode must be SV_MODE_GREEDY or SV_MODE_SAMPLE");
-  if (in->mode == SV_MODE_SAMPLE) {
-    if (!in->u_accept || !in->u_bonus)
-      return fail(SV_ERR_INVALID_ARG, "SV_MODE_SAMPLE needs u_accept and u_bonus");
-    if (!plan.chains_only)
-      return fail(SV_ERR_UNSUPPORTED, "SV_MODE_SAMPLE takes chains: a row has more than one child");
-    if (h->n_och > 1024)
-      return fail(SV_ERR_UNSUPPORTED, "SV_MODE_SAMPLE supports vocabularies up to 8388608 tokens");
-  }
-  if (in->kv_tokens > 0 && (!in->kv_k || !in->kv_v))
-    return fail(SV_ERR_INVALID_ARG, "kv_k and kv_v must be non-null when kv_tokens > 0");
-  if (!out->accept_len || !out->bonus || !out->last_row || !out->surv_sum || !out->argmax || !out->row_max ||
-      !out->row_lse || !out->overlap || !out->survival)
-    return fail(SV_ERR_INVALID_ARG, "every output except logits must be a non-null device pointer");
+  sv::MetaLayout lay{};
   {
-    const bool samp = in->mode == SV_MODE_SAMPLE;
-    const sv::RunPointers rp{{in->kv_tokens > 0 ? in->kv_k : nullptr, in->kv_tokens > 0 ? in->kv_v : nullptr,
-                              in->q_rows, in->k_rows, in->v_rows, plan.n_draft > 0 ? in->drafter_logits : nullptr,
-                              out->logits},
-                             {in->draft_ids, samp ? in->u_accept : nullptr, samp ? in->u_bonus : nullptr,
-                              out->accept_len, out->bonus, out->last_row, out->surv_sum, out->argmax, out->row_max,
-                              out->row_lse, out->overlap, out->survival}};
-    const int ac = sv::check_alignment(rp, &err);
-    if (ac != sv::P_OK) return fail(sv_status(ac), err);
+    const sv_status vs = check_run(dm, in, out, h->slot_cap, h->target_items, h->n_och, &plan, &lay);
+    if (vs != SV_OK) return vs;
   }
-  const sv::MetaLayout lay =
-      sv::meta_layout(plan.n, plan.R, plan.n_draft, int(plan.items.size()), int(plan.runs.size()),
-                      plan.R * dm.Hkv * plan.qg_max);
   if (lay.total > h->meta_cap) return fail(SV_ERR_CAPACITY, "metadata exceeds the handle's staging capacity");
 
   const int n = plan.n;
@@ -429,22 +585,11 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   h->meta_used[slot] = true;
 
   const char *m = h->d_meta;
-  const int32_t *row_tree = reinterpret_cast<const int32_t *>(m + lay.row_tree);
-  const int32_t *row_local = reinterpret_cast<const int32_t *>(m + lay.row_local);
   const int32_t *row_pos = reinterpret_cast<const int32_t *>(m + lay.row_pos);
-  const int32_t *row_parent = reinterpret_cast<const int32_t *>(m + lay.row_parent);
-  const int32_t *row_draft = reinterpret_cast<const int32_t *>(m + lay.row_draft);
-  const uint64_t *row_anc = reinterpret_cast<const uint64_t *>(m + lay.row_anc);
-  const int32_t *row_child = reinterpret_cast<const int32_t *>(m + lay.row_child);
-  const int32_t *draft_row = reinterpret_cast<const int32_t *>(m + lay.draft_row);
   const int32_t *row_pack = reinterpret_cast<const int32_t *>(m + lay.row_pack);
   const int32_t *row_plocal = reinterpret_cast<const int32_t *>(m + lay.row_plocal);
   const int32_t *row_klen = reinterpret_cast<const int32_t *>(m + lay.row_klen);
   const uint64_t *row_panc = reinterpret_cast<const uint64_t *>(m + lay.row_panc);
-  const int32_t *tree_start = reinterpret_cast<const int32_t *>(m + lay.tree_start);
-  const int32_t *tree_rows = reinterpret_cast<const int32_t *>(m + lay.tree_rows);
-  const int32_t *tree_kv_len = reinterpret_cast<const int32_t *>(m + lay.tree_kv_len);
-  const int64_t *tree_kv_off = reinterpret_cast<const int64_t *>(m + lay.tree_kv_off);
   const sv::AttnItem *items = reinterpret_cast<const sv::AttnItem *>(m + lay.items);
   const sv::AttnRun *runs = reinterpret_cast<const sv::AttnRun *>(m + lay.runs);
   const sv::AttnGroup *groups = reinterpret_cast<const sv::AttnGroup *>(m + lay.groups);
@@ -471,46 +616,14 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   const int tile_w = bf16 && !fp8 ? sv::lm_tile_width(n, int(V), h->n_cu) : 256;
   const int n_tiles = int(ceil_div(V, tile_w));
 
-  sv::VocabArgs va{};
-  va.n = n;
-  va.n_draft = plan.n_draft;
-  va.R = plan.R;
-  va.V = int(V);
-  va.row_parent = row_parent;
-  va.row_draft = row_draft;
-  va.draft_row = draft_row;
-  va.tree_start = tree_start;
-  va.tree_rows = tree_rows;
-  va.draft_ids = in->draft_ids;
-  va.drafter = in->drafter_logits;
-  va.drafter_bf16 = bf16 ? 1 : 0;
-  va.logits = logits;
   // Without a caller logits buffer, the tiled LM head stores each tile's
   // probabilities relative to the tile maximum in fp16 instead of fp32
   // logits: half the bytes for their readers (the overlap pass, and in T = 1
   // mode the accept tests and the bonus draw).
   const bool use_p16 = bf16 && !fp8 && n > 64 && !out->logits && h->p16 != nullptr;
-  va.p16 = use_p16 ? h->p16 : nullptr;
-  va.t_max = h->t_max;
-  va.t_sum = h->t_sum;
-  va.t_arg = h->t_arg;
-  va.n_tiles = n_tiles;
-  va.dpart = h->dpart;
-  va.n_dch = h->n_dch;
-  va.dchunk = kDChunk;
-  va.lse_q = h->lse_q;
-  va.opart = h->opart;
-  va.n_och = h->n_och;
-  va.ochunk = kOChunk;
-  va.argmax = out->argmax;
-  va.accept_len = out->accept_len;
-  va.bonus = out->bonus;
-  va.last_row = out->last_row;
-  va.row_max = out->row_max;
-  va.row_lse = out->row_lse;
-  va.overlap = out->overlap;
-  va.survival = out->survival;
-  va.surv_sum = out->surv_sum;
+  sv::VocabArgs va = vocab_args(plan, m, lay, int(V), bf16, in, out,
+                                VocabBufs{logits, use_p16 ? h->p16 : nullptr, h->t_max, h->t_sum, h->t_arg,
+                                          n_tiles, h->dpart, h->n_dch, h->lse_q, h->opart, h->n_och});
 
   int k_split = 0;
   const int splits = bf16 ? sv::gemm_splits(n, int(H), int(Hq * D), h->n_cu, &k_split) : 1;
@@ -518,8 +631,17 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   // skinny launch, blocked fp16 for the tiled one (e4m3 for the FP8 LM head)
   const int lm_act_mode = fp8 ? sv::ACT_FP8_BLOCKED : n <= 64 ? sv::ACT_SPLIT : sv::ACT_F16_BLOCKED;
   const int64_t q_lo = int64_t(dm.max_rows) * Hq * D;   // lo planes start one capacity further
-  const int64_t o_lo = int64_t(dm.max_rows) * Hq * D;
-  const int64_t h_lo = int64_t(dm.max_rows) * H;
+  const int64_t k_lo = int64_t(dm.max_rows) * Hkv * D;
+  const int64_t o_lo = sv::blocked_elems(dm.max_rows, Hq * D);
+  const int64_t h_lo = sv::blocked_elems(dm.max_rows, H);
+  if (bf16 && !fp8 && n > 64) {
+    // the tiled LM head's plain fp16 activations: its high-probability
+    // logits are recomputed from the hi + lo pair with the row statistics
+    va.rf_w = static_cast<const uint16_t *>(h->w_lm);
+    va.rf_hi = static_cast<const uint16_t *>(h->hn);
+    va.rf_lo = va.rf_hi + h_lo;
+    va.rf_K = int(H);
+  }
 
   if (bf16) {
     sv::RopeArgs ra{};
@@ -533,6 +655,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     ra.D = int(D);
     ra.base = double(h->cfg.rope_base);
     ra.q_lo_off = q_lo;
+    ra.k_lo_off = k_lo;
     ra.n = n;
     ra.ry = int(ceil_div(int64_t(Hq + Hkv) * (D / 2), 256));
     begin("rope_drafter_stats");
@@ -569,9 +692,18 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     ma.Hq = int(Hq);
     ma.Hkv = int(Hkv);
     ma.qg_max = plan.qg_max;
-    ma.mode = n <= 64 ? sv::ACT_SPLIT : sv::ACT_F16_BLOCKED;
+    ma.mode = n <= 64 ? sv::ACT_SPLIT : sv::ACT_SPLIT_BLOCKED;
     ma.lo_off = o_lo;
     ma.out = static_cast<uint16_t *>(h->o_act);
+    ma.row_anc = reinterpret_cast<const uint64_t *>(m + lay.row_anc);
+    ma.row_tree_real = reinterpret_cast<const int32_t *>(m + lay.row_tree);
+    ma.tree_start = reinterpret_cast<const int32_t *>(m + lay.tree_start);
+    ma.q_rot = aa.q_rot;
+    ma.k_rot = aa.k_rot;
+    ma.v_rows = aa.v_rows;
+    ma.q_lo_off = q_lo;
+    ma.k_lo_off = k_lo;
+    ma.scale_log2 = aa.scale_log2;
     begin("attn_merge");
     int n_groups_used = 0;
     for (const auto &gr : plan.groups) n_groups_used += gr.count > 0;
@@ -589,7 +721,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     g.ldo = H;
     g.split_stride = int64_t(n) * H;
     begin("w_o");
-    sv::launch_gemm_bf16(g, false, splits, stream, n > 64);
+    sv::launch_gemm_bf16(g, false, splits, stream, n > 64, n > 64);
     end();
     begin("final_norm");
     sv::launch_norm(h->h_part, splits, int64_t(n) * H, n, int(H), h->cfg.norm_eps, lm_act_mode, h->hn, h_lo,
@@ -624,74 +756,12 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     }
     end();
   } else {
-    begin("rope");
-    sv::launch_rope_f32(static_cast<const float *>(in->q_rows), static_cast<const float *>(in->k_rows),
-                        static_cast<float *>(h->q_rot), static_cast<float *>(h->k_rot), row_pos, n, int(Hq), int(Hkv),
-                        int(D), double(h->cfg.rope_base), stream);
-    end();
-    begin("drafter_stats");
-    sv::launch_drafter_partial(va, stream);
-    end();
-    sv::AttnF32Args af{};
-    af.kv_k = static_cast<const float *>(in->kv_k);
-    af.kv_v = static_cast<const float *>(in->kv_v);
-    af.k_rot = static_cast<const float *>(h->k_rot);
-    af.v_rows = static_cast<const float *>(in->v_rows);
-    af.q_rot = static_cast<const float *>(h->q_rot);
-    af.row_tree = row_tree;
-    af.tree_start = tree_start;
-    af.tree_rows = tree_rows;
-    af.tree_kv_len = tree_kv_len;
-    af.tree_kv_off = tree_kv_off;
-    af.row_anc = row_anc;
-    af.out = static_cast<float *>(h->o_act);
-    af.Hq = int(Hq);
-    af.Hkv = int(Hkv);
-    af.D = int(D);
-    begin("attention");
-    sv::launch_attn_f32(af, n, stream);
-    end();
-    begin("w_o");
-    sv::launch_gemm_f32(static_cast<const float *>(h->o_act), n, static_cast<const float *>(h->w_o), int(H),
-                        int(Hq * D), h->h_part, stream);
-    end();
-    begin("final_norm");
-    sv::launch_norm(h->h_part, 1, 0, n, int(H), h->cfg.norm_eps, sv::ACT_F32, h->hn, 0, nullptr, stream);
-    end();
-    begin("lm_head");
-    sv::launch_gemm_f32(static_cast<const float *>(h->hn), n, static_cast<const float *>(h->w_lm), int(V), int(H),
-                        logits, stream);
-    sv::launch_stats_from_logits(logits, n, int(V), 256, h->t_max, h->t_sum, h->t_arg, n_tiles, stream);
-    end();
+    enqueue_f32(dm, h->cfg, m, lay,
+                F32Bufs{static_cast<float *>(h->q_rot), static_cast<float *>(h->k_rot), static_cast<float *>(h->o_act),
+                        h->h_part, static_cast<float *>(h->hn), h->t_max, h->t_sum, h->t_arg},
+                h->w_o, h->w_lm, in, va, stream, begin, end);
   }
-  if (n <= 64) {
-    // few rows: few tile records per row, so the overlap workgroups merge
-    // their own logsumexps and the two passes share one launch
-    begin("combine_overlap");
-    sv::launch_combine_overlap(va, stream);
-    end();
-  } else {
-    begin("row_combine");
-    sv::launch_row_combine(va, stream);
-    end();
-    begin("overlap");
-    sv::launch_overlap_partial(va, stream);
-    end();
-  }
-  begin("accept");
-  sv::launch_accept(va, stream);
-  end();
-  if (in->mode == SV_MODE_SAMPLE) {
-    sv::SampleArgs sa{};
-    sa.row_child = row_child;
-    sa.u_accept = in->u_accept;
-    sa.u_bonus = in->u_bonus;
-    sa.rej_child = h->rej_child;
-    sa.rpart = h->rpart;
-    begin("sample");
-    sv::launch_sample(va, sa, stream);
-    end();
-  }
+  enqueue_tail(va, in, m, lay, h->rej_child, h->rpart, stream, begin, end);
   if (h->profile == 1) (void)hipEventRecord(h->stages[step_stage].b, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail("kernel launch", e);

@@ -17,8 +17,10 @@
 // O^T += V^T.P^T run on 16x16x32 bf16 MFMA, the online softmax is per
 // wavefront in fp32 (log2 domain).  The rotated queries and the
 // probabilities are each carried as a bf16 pair hi + lo (two MFMAs per
-// product), so the only bf16 rounding left in the scores is the one of the
-// cached keys themselves.  Each item leaves (max, sum, unnormalised o) per
+// product), so the scores of the cached keys (exact bf16 inputs) are exact
+// to about 16 bits; the keys rotated in this step (the row tiles) enter the
+// tiles rounded to bf16, and the merge replaces their weights with exact
+// ones.  Each item leaves (max, sum, unnormalised o) per
 // query; a merge kernel combines the items of a query and writes o in the
 // format the W_o projection reads.
 //
@@ -35,8 +37,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void rope_rows_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                         T *__restrict__ q_out, T *__restrict__ k_out,
                                                         const int32_t *__restrict__ row_pos, int Hq,
-                                                        int Hkv, int D, double base, int64_t q_lo_off) {
-  rope_rows_block<T>(q, k, q_out, k_out, row_pos, Hq, Hkv, D, base, q_lo_off, blockIdx.x, blockIdx.y);
+                                                        int Hkv, int D, double base) {
+  rope_rows_block<T>(q, k, q_out, k_out, row_pos, Hq, Hkv, D, base, 0, 0, blockIdx.x, blockIdx.y);
 }
 
 // ----------------------------------------------------------------------------
@@ -484,25 +486,63 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a, int n_pair
     if (w != 0) return;
     val = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
   }
-  val = val / L;
+  // The keys rotated in this step (the row's ancestors and itself) reached
+  // the attention tiles rounded to bf16.  Each contributed 2^(x~ - M) v to
+  // val and 2^(x~ - M) to L, x~ the log2-scaled score against the rounded key;
+  // swap in 2^(x - M), x the score against the key's hi + lo pair (about 16
+  // bits).  x~ is recomputed in fp32 from the same bf16 operands the tiles
+  // multiplied.  Lane c holds elements [c E, c E + E) of the query and keys.
+  float Lx = L;
+  if (a.row_anc) {
+    const int64_t qoff = (int64_t(i) * a.Hq + h) * D + c * E;
+    float qv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) qv[e] = bf2f(a.q_rot[qoff + e]) + bf2f(a.q_rot[a.q_lo_off + qoff + e]);
+    const int ts = as_const(a.tree_start)[as_const(a.row_tree_real)[i]];
+    uint64_t bits = a.row_anc[i];
+    while (bits) {
+      const int j = __builtin_ctzll(bits);
+      bits &= bits - 1;
+      const int64_t koff = (int64_t(ts + j) * a.Hkv + g) * D + c * E;
+      float st = 0.f, sx = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float kh = bf2f(a.k_rot[koff + e]), kl = bf2f(a.k_rot[a.k_lo_off + koff + e]);
+        st = fmaf(kh, qv[e], st);
+        sx = fmaf(kh + kl, qv[e], sx);
+      }
+      st = wave_sum(st);
+      sx = wave_sum(sx);
+      const float dp = exp2f(sx * a.scale_log2 - M) - exp2f(st * a.scale_log2 - M);
+      Lx += dp;
+#pragma unroll
+      for (int e = 0; e < E; ++e) val[e] = fmaf(dp, bf2f(a.v_rows[koff + e]), val[e]);
+    }
+  }
+  val = val / Lx;
 
   const int64_t idx = int64_t(i) * a.Hq * D + int64_t(h) * D + c * E;
   uint16_t hi[E], lo[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    if (a.mode == ACT_SPLIT)
+    if (a.mode == ACT_SPLIT || a.mode == ACT_SPLIT_BLOCKED)
       split_h(val[e], hi[e], lo[e]);
     else
       hi[e] = f2h(val[e]);
   }
-  if (a.mode == ACT_F16_BLOCKED) {
+  if (a.mode == ACT_F16_BLOCKED || a.mode == ACT_SPLIT_BLOCKED) {
     // blocked fp16 layout of the tiled W_o launch (K = Hq * D); the lane's E
-    // elements share one 16-B chunk
+    // elements share one 16-B chunk; the lo plane (ACT_SPLIT_BLOCKED) in the
+    // same layout lo_off elements on
     const int k = h * D + c * E, R = i & 255, q = (k >> 3) & 3;
     const int64_t b = (int64_t(i >> 8) * ((a.Hq * D) >> 5) + (k >> 5)) * 8192;
     uint16_t *dst = a.out + b + R * 32 + ((q ^ ((R >> 1) & 3)) << 3) + (k & 7);
 #pragma unroll
     for (int e = 0; e < E; ++e) dst[e] = hi[e];
+    if (a.mode == ACT_SPLIT_BLOCKED) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) dst[a.lo_off + e] = lo[e];
+    }
   } else {
 #pragma unroll
     for (int e = 0; e < E; ++e) a.out[idx + e] = hi[e];
@@ -590,18 +630,10 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
 // launchers
 // ----------------------------------------------------------------------------
 
-void launch_rope_bf16(const uint16_t *q, const uint16_t *k, uint16_t *qo, uint16_t *ko, const int32_t *row_pos,
-                      int n, int Hq, int Hkv, int D, double base, int64_t q_lo_off, hipStream_t s) {
-  const dim3 grid(n, (Hq + Hkv) * (D / 2) / 256 + ((Hq + Hkv) * (D / 2) % 256 != 0));
-  hipLaunchKernelGGL(rope_rows_kernel<uint16_t>, grid, dim3(256), 0, s, q, k, qo, ko, row_pos, Hq, Hkv, D, base,
-                     q_lo_off);
-}
-
 void launch_rope_f32(const float *q, const float *k, float *qo, float *ko, const int32_t *row_pos, int n, int Hq,
                      int Hkv, int D, double base, hipStream_t s) {
   const dim3 grid(n, (Hq + Hkv) * (D / 2) / 256 + ((Hq + Hkv) * (D / 2) % 256 != 0));
-  hipLaunchKernelGGL(rope_rows_kernel<float>, grid, dim3(256), 0, s, q, k, qo, ko, row_pos, Hq, Hkv, D, base,
-                     int64_t(0));
+  hipLaunchKernelGGL(rope_rows_kernel<float>, grid, dim3(256), 0, s, q, k, qo, ko, row_pos, Hq, Hkv, D, base);
 }
 
 template <int D, int NW, int STG, int OCC>

@@ -303,10 +303,19 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 
 constexpr int kTBN = 256, kTBT = 256, kTST = 4, kTSST = (kTBN + kTBT) * 64;
 constexpr size_t kTiledLds = size_t(kTST) * kTSST;
+// LO (W_o above 64 rows): the activation is an fp16 pair hi + lo, both
+// planes blocked, two MFMAs per product; a stage holds the weights and both
+// planes (48 KB), in a 3-stage ring.
+constexpr int kTSTLo = 3, kTSSTLo = (kTBN + 2 * kTBT) * 64;
+constexpr size_t kTiledLdsLo = size_t(kTSTLo) * kTSSTLo;
 
-template <bool STATS, bool BLOCKED>
+template <bool STATS, bool BLOCKED, bool LO = false>
 __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
-  constexpr int PER = 4;     // DMA instructions per wave per stage (2 weight + 2 activation)
+  static_assert(!LO || (BLOCKED && !STATS), "the hi + lo activation pair is for the blocked W_o launch");
+  // DMA instructions per wave per stage: 2 weight + 2 activation (+ 2 lo)
+  constexpr int PER = LO ? 6 : 4;
+  constexpr int ST = LO ? kTSTLo : kTST;        // ring stages
+  constexpr int SST = LO ? kTSSTLo : kTSST;     // bytes per stage
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r32 = lane & 31, kg = lane >> 5;
@@ -332,7 +341,7 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
     t_tile = rem / 8;
   };
   struct Src {
-    i32x4 rw, ra;
+    i32x4 rw, ra, rl;
   };
   auto src_of = [&](int n_tile, int t_tile) {
     const int n0 = n_tile * kTBN, t0 = t_tile * kTBT;
@@ -343,19 +352,26 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
       const int64_t tb = int64_t(g.K) * 256;
       r.rw = make_rsrc(g.W + int64_t(n_tile) * tb, uint32_t(tb * 2));
       r.ra = make_rsrc(g.act + int64_t(t_tile) * tb, uint32_t(tb * 2));
+      r.rl = LO ? make_rsrc(g.act_lo + int64_t(t_tile) * tb, uint32_t(tb * 2)) : r.ra;
     } else {
       r.rw = make_rsrc(g.W + int64_t(n0) * g.K, uint32_t(min(kTBN, g.N - n0)) * Kb);
       r.ra = make_rsrc(g.act + int64_t(t0) * g.K, uint32_t(min(kTBT, g.rows - t0)) * Kb);
+      r.rl = r.ra;
     }
     return r;
   };
   auto issue = [&](const Src &sr, int s) {
-    const uint32_t base = lds0 + (s % kTST) * kTSST;
+    const uint32_t base = lds0 + (s % ST) * SST;
     const int soff = BLOCKED ? (ks / 32 + s) * 16384 : (ks + s * 32) * 2;
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16(sr.rw, base + (w * 32 + i * 16) * 64, off[i], soff);
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16(sr.ra, base + kTBN * 64 + (w * 32 + i * 16) * 64, off[i], soff);
+    if constexpr (LO) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        dma16(sr.rl, base + (kTBN + kTBT) * 64 + (w * 32 + i * 16) * 64, off[i], soff);
+    }
   };
 
   int tile = blockIdx.x;
@@ -372,7 +388,7 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
   tile_of(tile, n_tile, t_tile);
   Src cur = src_of(n_tile, t_tile);
 #pragma unroll
-  for (int p = 0; p < kTST - 1; ++p)
+  for (int p = 0; p < ST - 1; ++p)
     if (p < nk) issue(cur, p);
 
   for (;;) {
@@ -385,16 +401,16 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
         for (int j = 0; j < 16; ++j) acc[v][t][j] = 0.f;
 
     for (int s = 0; s < nk; ++s) {
-      const int younger = min(kTST - 2, nk - 1 - s);
+      const int younger = min(ST - 2, nk - 1 - s);
       if (younger >= 2)
         wait_and_barrier<2 * PER>();
       else if (younger == 1)
         wait_and_barrier<PER>();
       else
         wait_and_barrier<0>();
-      if (s + kTST - 1 < nk) issue(cur, s + kTST - 1);
-      const uint8_t *base = smem + (s % kTST) * kTSST;
-      uint4 af[2][4], bf[2][2];
+      if (s + ST - 1 < nk) issue(cur, s + ST - 1);
+      const uint8_t *base = smem + (s % ST) * SST;
+      uint4 af[2][4], bf[2][2], bl[2][2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int q = j * 2 + kg;
@@ -407,6 +423,7 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
         for (int t = 0; t < 2; ++t) {
           const int R = wt * 64 + t * 32 + r32;
           bf[j][t] = lds16(base + kTBN * 64 + R * 64 + ((q ^ ((R >> 1) & 3)) << 4));
+          if constexpr (LO) bl[j][t] = lds16(base + (kTBN + kTBT) * 64 + R * 64 + ((q ^ ((R >> 1) & 3)) << 4));
         }
       }
 #pragma unroll
@@ -414,7 +431,10 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
 #pragma unroll
         for (int v = 0; v < 4; ++v)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) acc[v][t] = mfma32h(af[j][v], bf[j][t], acc[v][t]);
+          for (int t = 0; t < 2; ++t) {
+            acc[v][t] = mfma32h(af[j][v], bf[j][t], acc[v][t]);
+            if constexpr (LO) acc[v][t] = mfma32h(af[j][v], bl[j][t], acc[v][t]);
+          }
     }
 
     // epilogue of this tile (vector-memory waits count stores too, so the
@@ -481,7 +501,7 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
       tile_of(next, nn_tile, nt_tile);
       nsrc = src_of(nn_tile, nt_tile);
 #pragma unroll
-      for (int p = 0; p < kTST - 1; ++p)
+      for (int p = 0; p < ST - 1; ++p)
         if (p < nk) issue(nsrc, p);
     }
     if (!more) break;
@@ -783,7 +803,7 @@ static void launch_skinny(const GemmArgs &g, int splits, hipStream_t s) {
   hipLaunchKernelGGL((gemm_skinny_kernel<TB, WV, ST, BL>), grid, dim3(256), lds, s, g);
 }
 
-void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s, bool blocked) {
+void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s, bool blocked, bool lo) {
   if (g.rows <= 64) {
     // WV = 2 for the LM head (256 weight rows per workgroup), 1 for split-K W_o
     if (g.rows <= 32) {
@@ -807,6 +827,8 @@ void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s, 
                               hipFuncAttributeMaxDynamicSharedMemorySize, int(kTiledLds));
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_tiled_kernel<false, true>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, int(kTiledLds));
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_tiled_kernel<false, true, true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(kTiledLdsLo));
     int dev = 0;
     if (hipGetDevice(&dev) == hipSuccess) {
       int cu = 0;
@@ -823,6 +845,8 @@ void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s, 
   // the LM head (stats) reads both operands in the blocked layout
   if (stats)
     hipLaunchKernelGGL((gemm_tiled_kernel<true, true>), grid, dim3(512), kTiledLds, s, g);
+  else if (blocked && lo)
+    hipLaunchKernelGGL((gemm_tiled_kernel<false, true, true>), grid, dim3(512), kTiledLdsLo, s, g);
   else if (blocked)
     hipLaunchKernelGGL((gemm_tiled_kernel<false, true>), grid, dim3(512), kTiledLds, s, g);
   else
@@ -1008,9 +1032,14 @@ __global__ __launch_bounds__(1024) void norm_kernel(const float *part, int split
     } else if (mode == ACT_F16) {
       static_cast<uint16_t *>(out)[idx] = f2h(y);
     } else if (mode == ACT_F16_BLOCKED) {
+      // the blocked hi plane of the tiled LM head, and the residual y - hi as
+      // a row-major fp16 plane at lo_off (the logit refinement reads it)
+      uint16_t hi, lo;
+      split_h(y, hi, lo);
       const int R = row & 255, q = (c >> 3) & 3;
       const int64_t b = (int64_t(row >> 8) * (hidden >> 5) + (c >> 5)) * 8192;
-      static_cast<uint16_t *>(out)[b + R * 32 + ((q ^ ((R >> 1) & 3)) << 3) + (c & 7)] = f2h(y);
+      static_cast<uint16_t *>(out)[b + R * 32 + ((q ^ ((R >> 1) & 3)) << 3) + (c & 7)] = hi;
+      static_cast<uint16_t *>(out)[lo_off + idx] = lo;
     } else {
       static_cast<float *>(out)[idx] = y;
     }

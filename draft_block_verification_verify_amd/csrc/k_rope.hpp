@@ -18,15 +18,9 @@ __device__ __forceinline__ double ld<uint16_t>(const uint16_t *p) { return doubl
 template <>
 __device__ __forceinline__ double ld<float>(const float *p) { return double(*p); }
 
-template <typename T>
-__device__ __forceinline__ void st(T *p, double v);
-template <>
-__device__ __forceinline__ void st<uint16_t>(uint16_t *p, double v) { *p = f2bf(float(v)); }
-template <>
-__device__ __forceinline__ void st<float>(float *p, double v) { *p = float(v); }
-
-// bf16 queries are written as a hi plane (q_out) and a lo plane
-// (q_out + q_lo_off) with hi + lo = rotated value to about 16 bits.
+// bf16 queries (and keys) are written as a hi plane (q_out) and a lo plane
+// (q_out + lo_off) with hi + lo = rotated value to about 16 bits.  The key's
+// hi plane is the key rounded to bf16 once, as a cache entry holds it.
 __device__ __forceinline__ void st_q(uint16_t *p, int64_t lo_off, double v) {
   uint16_t hi, lo;
   split_bf(float(v), hi, lo);
@@ -43,7 +37,7 @@ template <typename T>
 __device__ __forceinline__ void rope_rows_block(const T *__restrict__ q, const T *__restrict__ k,
                                                 T *__restrict__ q_out, T *__restrict__ k_out,
                                                 const int32_t *__restrict__ row_pos, int Hq, int Hkv, int D,
-                                                double base, int64_t q_lo_off, int i, int by) {
+                                                double base, int64_t q_lo_off, int64_t k_lo_off, int i, int by) {
   __shared__ double cs[128], sn[128];   // cos, sin of pos * theta_k, k < D/2 <= 128
   const int half = D / 2;
   const int heads = Hq + Hkv;
@@ -71,8 +65,8 @@ __device__ __forceinline__ void rope_rows_block(const T *__restrict__ q, const T
     st_q(dst + kk + half, q_lo_off, b * c + a * s);
   } else {
     T *dst = k_out + (int64_t(i) * Hkv + (hh - Hq)) * D;
-    st(dst + kk, a * c - b * s);
-    st(dst + kk + half, b * c + a * s);
+    st_q(dst + kk, k_lo_off, a * c - b * s);
+    st_q(dst + kk + half, k_lo_off, b * c + a * s);
   }
 }
 

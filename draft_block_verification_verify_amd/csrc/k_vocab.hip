@@ -144,7 +144,8 @@ __global__ __launch_bounds__(256) void rope_drafter_kernel(RopeArgs r, VocabArgs
   const int b = blockIdx.x;
   const int nr = r.n * r.ry;
   if (b < nr) {
-    rope_rows_block<uint16_t>(r.q, r.k, r.q_out, r.k_out, r.row_pos, r.Hq, r.Hkv, r.D, r.base, r.q_lo_off, b / r.ry,
+    rope_rows_block<uint16_t>(r.q, r.k, r.q_out, r.k_out, r.row_pos, r.Hq, r.Hkv, r.D, r.base, r.q_lo_off, r.k_lo_off,
+                              b / r.ry,
                               b % r.ry);
   } else {
     const int d = b - nr;
@@ -191,11 +192,185 @@ __device__ __forceinline__ MaxSum drafter_stats_block(const VocabArgs &a, int t)
   return ms_block256(q);
 }
 
+// ----------------------------------------------------------------------------
+// Logit refinement of the tiled LM head.  That launch multiplies plain fp16
+// activations (11 significant bits); on a peaked target distribution the
+// rounding moves the largest probabilities by about 1e-3.  The tokens that can
+// carry such an error -- first-pass probability >= 1/64, so at most 64 of
+// them -- are recomputed here in fp32 from the fp16 hi + lo activation pair
+// (about 22 bits), and the row's max, greedy token and logsumexp are
+// corrected: with the candidates' first-pass probabilities p_c,
+// lse' = lse + log((1 - sum_c p_c) + sum_c exp(l'_c - lse)).  The new logits
+// replace the first-pass values in the logits buffer (or in the fp16 tile
+// probabilities), so the overlap pass and the T = 1 walk and draw read them.
+// Rows without a candidate (flat distributions) keep the first pass.
+// ----------------------------------------------------------------------------
+
+constexpr int kRefineMax = 64;
+constexpr float kRefineLogTau = -4.1588830833596715f;   // log(1/64)
+
+// first-pass logit of token u of row `row` (tiles of 256 tokens)
+__device__ __forceinline__ float tile_logit(const VocabArgs &a, int row, int u) {
+  if (a.p16) {
+    const float p = h2f(a.p16[int64_t(row) * a.V + u]);
+    return p > 0.f ? a.t_max[int64_t(row) * a.n_tiles + (u >> 8)] + logf(p) : -INFINITY;
+  }
+  return a.logits[int64_t(row) * a.V + u];
+}
+
+// element offset of the 8-element chunk holding (r, k) (k % 8 == 0) in the
+// blocked fp16 layout of the tiled LM head
+__device__ __forceinline__ int64_t blocked_chunk(int64_t r, int k, int K) {
+  const int R = int(r & 255), q = (k >> 3) & 3;
+  return ((r >> 8) * (K >> 5) + (k >> 5)) * 8192 + R * 32 + ((q ^ ((R >> 1) & 3)) << 3);
+}
+
+__device__ __forceinline__ float dot8h(uint4 x, uint4 y) {
+  const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    s = fmaf(h2f(uint16_t(xs[e] & 0xFFFFu)), h2f(uint16_t(ys[e] & 0xFFFFu)), s);
+    s = fmaf(h2f(uint16_t(xs[e] >> 16)), h2f(uint16_t(ys[e] >> 16)), s);
+  }
+  return s;
+}
+
+// (max, lowest index on ties) over the block; every thread gets it
+__device__ __forceinline__ void max_arg_block256(float &m, int &i) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o);
+    const int i2 = __shfl_xor(i, o);
+    if (m2 > m || (m2 == m && i2 < i)) {
+      m = m2;
+      i = i2;
+    }
+  }
+  __shared__ float rm[4];
+  __shared__ int ri[4];
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    rm[threadIdx.x >> 6] = m;
+    ri[threadIdx.x >> 6] = i;
+  }
+  __syncthreads();
+  m = rm[0];
+  i = ri[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w)
+    if (rm[w] > m || (rm[w] == m && ri[w] < i)) {
+      m = rm[w];
+      i = ri[w];
+    }
+}
+
+// Refines row `row`: on return thread 0's r (max, argmax) and lse hold the
+// corrected values.  Called by the whole workgroup.
+__device__ void refine_row(const VocabArgs &a, int row, MaxSumArg &r, float &lse) {
+  __shared__ int s_tile[kRefineMax], s_cand[kRefineMax];
+  __shared__ float s_old[kRefineMax], s_new[kRefineMax];
+  __shared__ int s_nt, s_nc;
+  const int tid = threadIdx.x;
+  const float thr = lse + kRefineLogTau;
+  if (tid == 0) s_nt = s_nc = 0;
+  __syncthreads();
+  // candidate tiles (a token of probability >= 1/64); the best token of the
+  // other tiles
+  float ncm = -INFINITY;
+  int nci = 0x7fffffff;
+  const int64_t rt = int64_t(row) * a.n_tiles;
+  for (int c = tid; c < a.n_tiles; c += 256) {
+    const float m = a.t_max[rt + c];
+    if (m >= thr) {
+      const int k = atomicAdd(&s_nt, 1);
+      if (k < kRefineMax) s_tile[k] = c;
+    } else if (m > ncm || (m == ncm && a.t_arg[rt + c] < nci)) {
+      ncm = m;
+      nci = a.t_arg[rt + c];
+    }
+  }
+  __syncthreads();
+  const int nt = s_nt;
+  if (nt == 0 || nt > kRefineMax) return;      // (workgroup-uniform) no candidate: the first pass stands
+  // candidate tokens of those tiles; the others join the best non-candidate
+  for (int j = 0; j < nt; ++j) {
+    const int u = s_tile[j] * 256 + tid;
+    if (u >= a.V) continue;
+    const float l = tile_logit(a, row, u);
+    if (l >= thr) {
+      const int k = atomicAdd(&s_nc, 1);
+      if (k < kRefineMax) s_cand[k] = u;
+    } else if (l > ncm || (l == ncm && u < nci)) {
+      ncm = l;
+      nci = u;
+    }
+  }
+  max_arg_block256(ncm, nci);                 // (its barriers also order s_cand / s_nc)
+  const int nc = s_nc;
+  if (nc > kRefineMax) return;                // (uniform) a probability total past 1 by rounding: keep the first pass
+  if (tid == 0) {                             // ascending token order: a fixed summation order
+    for (int j = 1; j < nc; ++j) {
+      const int v = s_cand[j];
+      int k = j - 1;
+      while (k >= 0 && s_cand[k] > v) {
+        s_cand[k + 1] = s_cand[k];
+        --k;
+      }
+      s_cand[k + 1] = v;
+    }
+  }
+  __syncthreads();
+  // one wavefront per candidate: sum_k W[u, k] hi[k] and sum_k W[u, k] lo[k]
+  const int w = tid >> 6, lane = tid & 63, K = a.rf_K;
+  for (int j = w; j < nc; j += 4) {
+    const int u = s_cand[j];
+    float sh = 0.f, sl = 0.f;
+    for (int k = lane * 8; k < K; k += 512) {
+      const uint4 wv = *reinterpret_cast<const uint4 *>(a.rf_w + blocked_chunk(u, k, K));
+      const uint4 hv = *reinterpret_cast<const uint4 *>(a.rf_hi + blocked_chunk(row, k, K));
+      const uint4 lv = *reinterpret_cast<const uint4 *>(a.rf_lo + int64_t(row) * K + k);
+      sh += dot8h(wv, hv);
+      sl += dot8h(wv, lv);
+    }
+    sh = wave_sum(sh);
+    sl = wave_sum(sl);
+    if (lane == 0) {
+      s_old[j] = sh;
+      s_new[j] = sh + sl;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float so = 0.f, sn = 0.f, bm = ncm;
+    int bi = nci;
+    for (int j = 0; j < nc; ++j) {
+      const int u = s_cand[j];
+      const float l = s_new[j];
+      so += __expf(s_old[j] - lse);
+      sn += __expf(l - lse);
+      if (l > bm || (l == bm && u < bi)) {
+        bm = l;
+        bi = u;
+      }
+      if (a.p16)
+        a.p16[int64_t(row) * a.V + u] = f2h(__expf(l - a.t_max[rt + (u >> 8)]));
+      else
+        a.logits[int64_t(row) * a.V + u] = l;
+    }
+    lse += logf(fmaxf(1.f - so, 0.f) + sn);
+    r.m = bm;
+    r.i = bi;
+  }
+}
+
 __device__ __forceinline__ void row_combine_block(const VocabArgs &a, int i) {
-  const MaxSumArg r = row_stats_block(a, i);
+  MaxSumArg r = row_stats_block(a, i);
+  float lse = r.m + logf(r.s);
+  if (a.rf_w) refine_row(a, i, r, lse);      // tiled LM head: thread 0's values corrected
   if (threadIdx.x == 0) {
     a.row_max[i] = r.m;
-    a.row_lse[i] = r.m + logf(r.s);
+    a.row_lse[i] = lse;
     a.argmax[i] = r.i;
   }
   const int t = a.row_draft[i];

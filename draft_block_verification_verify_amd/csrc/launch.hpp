@@ -10,8 +10,16 @@ namespace sv {
 
 // Formats of the projections' small (activation) operand: ACT_SPLIT = fp16
 // hi plane + fp16 lo plane (hi + lo = value to ~22 bits), ACT_F16, ACT_F32,
-// ACT_F16_BLOCKED = fp16 in the blocked layout below.
-enum ActMode : int { ACT_SPLIT = 0, ACT_F16 = 1, ACT_F32 = 2, ACT_F16_BLOCKED = 3, ACT_FP8_BLOCKED = 4 };
+// ACT_F16_BLOCKED = fp16 in the blocked layout below, ACT_SPLIT_BLOCKED = the
+// hi and lo planes, each in the blocked layout (W_o above 64 rows).
+enum ActMode : int {
+  ACT_SPLIT = 0,
+  ACT_F16 = 1,
+  ACT_F32 = 2,
+  ACT_F16_BLOCKED = 3,
+  ACT_FP8_BLOCKED = 4,
+  ACT_SPLIT_BLOCKED = 5
+};
 
 // FP8 (OCP e4m3) operands of the FP8 LM head: each row of W and of the
 // activations is stored as e4m3 codes of value / 2^e, 2^e the smallest
@@ -30,7 +38,7 @@ constexpr int64_t blocked_elems(int64_t rows, int64_t K) { return (rows + 255) /
 
 struct AttnArgs {
   const uint16_t *kv_k, *kv_v;     // [T, Hkv, D] bf16, keys already rotated
-  const uint16_t *k_rot, *v_rows;  // [n, Hkv, D] bf16, row keys rotated
+  const uint16_t *k_rot, *v_rows;  // [n, Hkv, D] bf16, row keys rotated (hi plane)
   const uint16_t *q_rot;           // [n, Hq, D] bf16 hi plane of the rotated queries
   int64_t q_lo_off;                // elements from the hi plane to the lo plane
   const AttnItem *items;
@@ -50,6 +58,16 @@ struct MergeArgs {
   int mode;                        // ACT_SPLIT: fp16 hi plane at out, lo at out + lo_off; ACT_F16; ACT_F16_BLOCKED
   int64_t lo_off;
   uint16_t *out;                   // [n, Hq*D]
+  // exact weights of the keys rotated in this step (bf16 path): the row's
+  // ancestor-or-self bits in its own tree, its tree and the trees' first
+  // rows, the rotated queries and keys (hi planes, lo planes at q_lo_off /
+  // k_lo_off), the row values, the score scale in log2 units.  row_anc null:
+  // off.
+  const uint64_t *row_anc;
+  const int32_t *row_tree_real, *tree_start;
+  const uint16_t *q_rot, *k_rot, *v_rows;
+  int64_t q_lo_off, k_lo_off;
+  float scale_log2;
 };
 
 struct AttnF32Args {
@@ -91,8 +109,6 @@ struct GemmArgs {
 };
 
 // ---- attention ----
-void launch_rope_bf16(const uint16_t *q, const uint16_t *k, uint16_t *qo, uint16_t *ko, const int32_t *row_pos,
-                      int n, int Hq, int Hkv, int D, double base, int64_t q_lo_off, hipStream_t s);
 void launch_rope_f32(const float *q, const float *k, float *qo, float *ko, const int32_t *row_pos, int n, int Hq,
                      int Hkv, int D, double base, hipStream_t s);
 void launch_attn_mfma(const AttnArgs &a, int n_runs, int D, int max_qblocks, hipStream_t s);
@@ -107,7 +123,10 @@ int lm_tile_width(int rows, int N, int n_cu);
 int gemm_splits(int rows, int N, int K, int n_cu, int *k_split);
 // `blocked`: the tiled launch reads W and act in the blocked layout (always
 // for stats, the LM head)
-void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s, bool blocked = false);
+// `lo` (with `blocked`, not the LM head): act is an fp16 hi plane at g.act and
+// a lo plane at g.act_lo, both blocked; two MFMAs per product.
+void launch_gemm_bf16(const GemmArgs &g, bool stats, int splits, hipStream_t s, bool blocked = false,
+                      bool lo = false);
 void launch_gemm_f32(const float *act, int rows, const float *W, int N, int K, float *out, hipStream_t s);
 void launch_stats_from_logits(const float *logits, int rows, int V, int tile, float *t_max, float *t_sum,
                               int32_t *t_arg, int n_tiles, hipStream_t s);
@@ -140,9 +159,9 @@ struct VocabArgs {
   const int32_t *draft_ids;
   const void *drafter;          // [n_draft, V] bf16 or f32
   int drafter_bf16;
-  const float *logits;          // [n, V] fp32
+  float *logits;                // [n, V] fp32 (the refinement rewrites some entries)
   // [n, V] fp16 exp(l - t_max) per 256-token tile (null: read `logits`)
-  const uint16_t *p16;
+  uint16_t *p16;
   const float *t_max, *t_sum;
   const int32_t *t_arg;
   int n_tiles;
@@ -154,6 +173,13 @@ struct VocabArgs {
   // outputs
   int32_t *argmax, *accept_len, *bonus, *last_row;
   float *row_max, *row_lse, *overlap, *survival, *surv_sum;
+  // Logit refinement of the tiled LM head (plain fp16 activations): the
+  // row statistics recompute every token with probability >= 1/64 from the
+  // fp16 hi + lo activation pair.  rf_w: LM-head weights (blocked fp16),
+  // rf_hi: the rows' blocked fp16 activations, rf_lo: their row-major fp16
+  // residuals, rf_K: hidden width.  rf_w null: off.
+  const uint16_t *rf_w, *rf_hi, *rf_lo;
+  int rf_K;
 };
 // T = 1 stochastic verification of chains (see sv_mode in spec_verify.h).
 struct SampleArgs {
@@ -190,7 +216,7 @@ struct RopeArgs {
   const int32_t *row_pos;
   int Hq, Hkv, D;
   double base;
-  int64_t q_lo_off;
+  int64_t q_lo_off, k_lo_off;      // lo planes of the rotated queries and keys
   int n, ry;
 };
 void launch_rope_drafter_bf16(const RopeArgs &r, const VocabArgs &a, hipStream_t s);

@@ -10,13 +10,19 @@
 
 Both runs of a comparison take the same projection path when their row
 counts are on the same side of 64, so their results differ only by fp32
-summation order in the attention merge: logits are held to 2e-4 of
-max(|l|, rms of the row), overlaps and survival to 1e-5, and every greedy
-token, accept length, bonus and last row exactly where the first run's
-top-2 gap exceeds 1e-3.  A 448-row batch against its 7-row branches changes
-path (fp16 activations above 64 rows, an fp16 hi + lo pair below), and is
-held to the parity tolerances instead (logits 2e-2 of max(|l|, rms),
-overlaps 2e-3, decisions exact where the gap exceeds 1e-2).
+summation order in the attention merge.  Up to 64 rows (every activation an
+fp16 hi + lo pair) logits are held to 2e-4 of max(|l|, rms of the row),
+overlaps and survival to 1e-5, and every greedy token, accept length, bonus
+and last row exactly where the first run's top-2 gap exceeds 1e-3.  Above
+64 rows the LM head multiplies plain fp16 activations: an element within
+that summation-order difference of an fp16 rounding boundary can round to
+the neighbouring value in one run, which moves a logit by up to |w| times
+one fp16 step of the element (about 1e-3 of the row's rms at these weight
+scales); logits are then held to 3e-3, overlaps and survival to 5e-4,
+decisions exact where the gap exceeds 1e-2.  A 448-row batch against its
+7-row branches changes path, and is held to the parity tolerances (logits
+2e-2 of max(|l|, rms), overlaps 2e-3, decisions exact where the gap exceeds
+1e-2).
 """
 import dataclasses
 
@@ -30,6 +36,7 @@ from tests.test_gpu_parity import MINIS, _record, _say
 pytestmark = pytest.mark.gpu
 
 SAME_PATH = {"logit": 2e-4, "ov": 1e-5, "gap": 1e-3}
+SAME_TILED = {"logit": 3e-3, "ov": 5e-4, "gap": 1e-2}
 CROSS_PATH = {"logit": 2e-2, "ov": 2e-3, "gap": 1e-2}
 
 
@@ -163,5 +170,5 @@ def test_tree_permutation(name, n_trees):
     rep = {}
     trs, trs_b = _tree_rows(inp.st), _tree_rows(pinp.st)
     compare_runs(a, b, idx, np.arange(len(idx)), [(int(t), k, trs[t], trs_b[k][0]) for k, t in enumerate(perm)],
-                 SAME_PATH, rep)
+                 SAME_PATH if inp.st.n_rows <= 64 else SAME_TILED, rep)
     _record(f"{name}/tree-permutation", rep)
