@@ -32,6 +32,7 @@ FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 # the first tens of milliseconds of load below its working clocks: before the
 # warmup steps, the step runs untimed for at least this long.
 SETTLE_S = 0.5
+FLUSH_BYTES = 512 << 20        # written before each timed step (2x the 256 MB last-level cache)
 COUNTERS = os.path.join(ROOT, "profiles", "lm_head_counters.json")
 GEMM_SRC = [os.path.join(ROOT, "draft_block_verification_verify_amd", "csrc", f)
             for f in ("k_gemm.hip", "k_dma.hpp", "k_common.hpp")]
@@ -64,23 +65,18 @@ def counters_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(inp, min_seconds: float = 10.0, fp8: bool = False) -> dict:
-    """The fp64 oracle, as it stands, on whole sequences (trees) of the same
-    workload, one after another until at least `min_seconds` of CPU work
-    (`fp8`: with the FP8 LM head)."""
-    from oracle import verify_oracle as O
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
-        threads = 1
-    rng = np.random.default_rng(99)
-    d = dict(O.inp_dict(inp))
-    d["draft_ids"] = rng.integers(0, inp.cfg.vocab, inp.st.n_rows).astype(np.int32)
-    roots = np.nonzero(inp.st.parent < 0)[0].tolist() + [inp.st.n_rows]
-    cfg = O.cfg_dict(inp.cfg)
-    if fp8:
-        cfg["weight_format"] = "fp8"
+        return 1
+
+
+def _oracle_sample(inp, cfg, d, roots, min_seconds: float):
+    """The oracle on whole trees one after another until `min_seconds` of
+    CPU work: (rows, trees, seconds)."""
+    from oracle import verify_oracle as O
     rows, done, dt = 0, 0, 0.0
     t0 = time.perf_counter()
     while done < inp.st.n_roots and dt < min_seconds:
@@ -88,10 +84,55 @@ def cpu_baseline(inp, min_seconds: float = 10.0, fp8: bool = False) -> dict:
         rows += int(roots[done + 1] - roots[done])
         done += 1
         dt = time.perf_counter() - t0
+    return rows, done, dt
+
+
+def cpu_baseline(inp, min_seconds: float = 6.0, fp8: bool = False, one_thread: bool = False) -> dict:
+    """The fp64 oracle, as it stands, on the GPU machine's host: whole trees of
+    the same workload one after another until at least `min_seconds` of CPU
+    work (the sample), repeated for a median of 3 unless a run takes more than
+    30 s; `one_thread` adds the same sample with BLAS limited to one thread.
+    `fp8`: with the FP8 LM head."""
+    from oracle import verify_oracle as O
+    threads = _blas_threads()
+    rng = np.random.default_rng(99)
+    d = dict(O.inp_dict(inp))
+    d["draft_ids"] = rng.integers(0, inp.cfg.vocab, inp.st.n_rows).astype(np.int32)
+    roots = np.nonzero(inp.st.parent < 0)[0].tolist() + [inp.st.n_rows]
+    cfg = O.cfg_dict(inp.cfg)
+    if fp8:
+        cfg["weight_format"] = "fp8"
+    rows, done, dt = _oracle_sample(inp, cfg, d, roots, min_seconds)
+    rates = [rows / dt]
+    while len(rates) < 3 and dt <= 30.0:
+        r2, _, dt2 = _fixed_sample(inp, cfg, d, roots, done)
+        rates.append(r2 / dt2)
     kv = int(np.asarray(inp.st.root_kv_len)[:done].sum())
-    return {"value": rows / dt, "unit": "rows/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"trees 0..{done - 1} of {inp.st.n_roots} ({rows} rows, {kv} prefix tokens in all, "
-                      f"full vocabulary), {dt:.1f} s"}
+    out = {"value": float(np.median(rates)), "unit": "rows/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"trees 0..{done - 1} of {inp.st.n_roots} ({rows} rows, {kv} prefix tokens in all, "
+                     f"full vocabulary), about {dt:.1f} s per run, median of {len(rates)} run(s)",
+           "runs_rows_per_s": [float(x) for x in rates],
+           "os_cpu_count": os.cpu_count(),
+           "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+           "blas_threads": int(threads)}
+    if one_thread:
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                r1, _, dt1 = _fixed_sample(inp, cfg, d, roots, done)
+            out["one_thread"] = {"value": r1 / dt1, "unit": "rows/s", "cores": 1, "seconds": dt1}
+        except Exception as e:          # threadpoolctl missing: say so
+            out["one_thread"] = {"value": None, "error": str(e)}
+    return out
+
+
+def _fixed_sample(inp, cfg, d, roots, n_trees: int):
+    """The oracle on trees 0 .. n_trees - 1: (rows, trees, seconds)."""
+    from oracle import verify_oracle as O
+    t0 = time.perf_counter()
+    for t in range(n_trees):
+        O.verify(cfg, d, trees=[t])
+    return int(roots[n_trees] - roots[0]), n_trees, time.perf_counter() - t0
 
 
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 3) -> None:
@@ -353,6 +394,9 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5],
                     help="1 chain-tiny, 2 chain-8b, 3 block-27b-b16, 4 tree-specopd, 5 conc32-27b (default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", dest="other_configs", action="store_false",
+                    help="measure only --workload (by default the other four configurations follow, "
+                         "reported under other_configs)")
     ap.add_argument("--sample", action="store_true",
                     help="T = 1 stochastic verification (drafts drawn from the drafter, seeded uniforms)")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -374,10 +418,8 @@ def main() -> int:
         copy_calibration()
         return 0
 
-    from draft_block_verification_verify_amd import accounting as A
     from draft_block_verification_verify_amd import binding as B
     from draft_block_verification_verify_amd import workloads as W
-    from draft_block_verification_verify_amd.runner import DeviceCase
 
     B.lib()                                   # fails loudly without the HIP library
     cfg = W.CONFIGS[args.workload]
@@ -385,123 +427,228 @@ def main() -> int:
         return bench_rounds(args, cfg)
     if args.schedule:
         return bench_schedule(args, cfg)
-    log(f"[bench] generating {cfg.name} seed {args.seed}")
+    peaks = measured_peaks()
+    log(f"[bench] measured peaks: copy {peaks['copy_gbs']:.0f} GB/s, bf16 GEMM {peaks['gemm_bf16_tflops']:.0f} TFLOP/s")
+    head = measure(cfg, args.seed, args.steps, args.warmup, fp8=args.fp8, sample=args.sample, peaks=peaks,
+                   cpu=not args.no_cpu_baseline, stages=True)
+    res = {
+        "metric": METRIC,
+        "value": head["rows_per_s"],
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_p50"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": ("bf16, LM head e4m3" if args.fp8 else "bf16") if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; random-init weights of the stated shapes)",
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "timing": head["timing"],
+        "step": head["step"],
+        "measured_peaks": peaks,
+        "cpu_baseline": head.get("cpu_baseline"),
+    }
+    if args.other_configs and not (args.fp8 or args.sample):
+        # every other configuration in the same run, same protocol, fewer steps
+        others = {}
+        for wid in (1, 2, 3, 4):
+            if wid == args.workload:
+                continue
+            c = W.CONFIGS[wid]
+            o = measure(c, args.seed, max(5, args.steps // 2), 3, peaks=peaks, cpu=not args.no_cpu_baseline,
+                        one_thread=wid <= 3)
+            others[c.name] = {k: o[k] for k in ("rows_per_s", "ms_p50", "config", "roofline", "timing", "step",
+                                                "cpu_baseline") if k in o}
+        res["other_configs"] = others
+    print(json.dumps(res))
+    return 0
+
+
+def measured_peaks() -> dict:
+    """Achievable peaks measured on this GPU, beside the nominal ones: a
+    1 GiB device-to-device copy (bytes read + written per second, best of 5)
+    and a dense 8192^3 bf16 GEMM (torch.mm, best of 5)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(3)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    best = float("inf")
+    for _ in range(6):
+        ev[0].record()
+        dst.copy_(src)
+        ev[1].record()
+        torch.cuda.synchronize()
+        best = min(best, ev[0].elapsed_time(ev[1]))
+    copy_gbs = 2 * n / (best * 1e-3) / 1e9
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, dtype=torch.bfloat16, device="cuda:0")
+    b = torch.randn(m, m, dtype=torch.bfloat16, device="cuda:0")
+    for _ in range(3):
+        torch.mm(a, b)
+    best = float("inf")
+    for _ in range(5):
+        ev[0].record()
+        torch.mm(a, b)
+        ev[1].record()
+        torch.cuda.synchronize()
+        best = min(best, ev[0].elapsed_time(ev[1]))
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_gbs": copy_gbs, "gemm_bf16_tflops": 2 * m ** 3 / (best * 1e-3) / 1e12,
+            "copy": "1 GiB device-to-device copy, read + write bytes, best of 6",
+            "gemm": "torch.mm bf16 8192 x 8192 x 8192, best of 5 after 3"}
+
+
+class Flusher:
+    """Writes FLUSH_BYTES (twice the 256 MB last-level cache) on the current
+    stream before each timed step, outside the timed interval, so that the
+    weights and the KV cache come from HBM as in a step of a deep model."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+        self.i = 0
+
+    def __call__(self):
+        self.i += 1
+        self.buf.fill_(self.i & 0xFF)
+
+
+def timed_steps(step, steps: int, flush) -> np.ndarray:
+    """Per-step device times (ms) by two HIP events on the step's stream (the
+    current stream), a cache flush before each step outside its events."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        flush()
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in evs])
+
+
+def measure(cfg, seed, steps, warmup, *, fp8=False, sample=False, peaks=None, cpu=True, one_thread=False,
+            stages=False) -> dict:
+    """One workload: inputs resident in HBM, drafts planted, then the timed
+    steps (profiling off), the LM-head loop (its launch between two events),
+    and optionally the per-stage loop and the oracle on the host."""
+    import torch
+    from draft_block_verification_verify_amd import accounting as A
+    from draft_block_verification_verify_amd import binding as B
+    from draft_block_verification_verify_amd import workloads as W
+    from draft_block_verification_verify_amd.runner import DeviceCase
+
+    log(f"[bench] generating {cfg.name} seed {seed}")
     t0 = time.perf_counter()
-    inp = W.make_inputs(cfg, args.seed)
+    inp = W.make_inputs(cfg, seed)
     st = inp.st
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s: rows {st.n_rows}, trees {st.n_roots}, "
         f"kv tokens {st.kv_tokens}")
-    dc = DeviceCase(inp, with_logits=False, fp8=args.fp8)
+    dc = DeviceCase(inp, with_logits=False, fp8=fp8)
     torch.cuda.synchronize()
 
     # draft ids: trees use draws from the drafter; chains get a planted
     # accepted prefix k ~ U{0..gamma} on the target's greedy tokens (taken from
     # a first run of this same step)
     planted = None
-    if cfg.kind == "tree" or args.sample:
+    if cfg.kind == "tree" or sample:
         W.sample_tree_drafts(inp)
     else:
         dc.run()
-        g = dc.results()["argmax"]
-        planted = W.plant_chain_drafts(inp, g)
-    if args.sample:
+        planted = W.plant_chain_drafts(inp, dc.results()["argmax"])
+    if sample:
         dc.set_uniforms(W.make_uniforms(inp))
     dc.refresh()
+    flush = Flusher()
 
     settle(dc.run)
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
+    log(f"[bench] {cfg.name}: warmup {warmup}")
+    for _ in range(warmup):
+        flush()
         dc.run()
     torch.cuda.synchronize()
-    # timed region: K steps; the LM-head launch (the dominant kernel) is
-    # bracketed by two HIP events on the run's stream
-    B.spec_verify_profile(dc.ver.h, 2)
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
+    # the timed steps, profiling off
+    log(f"[bench] {cfg.name}: timing {steps} steps")
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        dc.run()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    lm_live = dict(B.spec_verify_stage_times(dc.ver.h)).get("lm_head", float("nan"))
-    B.spec_verify_profile(dc.ver.h, 0)
-    ms = (t1 - t0) * 1e3 / args.steps
-    # stage breakdown: the same K steps again with events around every stage
-    # (the events themselves add a few microseconds per stage)
-    B.spec_verify_profile(dc.ver.h, 1)
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for _ in range(args.steps):
-        dc.run()
-    torch.cuda.synchronize()
-    ms_staged = (time.perf_counter() - t2) * 1e3 / args.steps
-    stages = dict(B.spec_verify_stage_times(dc.ver.h))
-    B.spec_verify_profile(dc.ver.h, 0)
+    step_ms = timed_steps(dc.run, steps, flush)
+    wall = time.perf_counter() - t0
     out = dc.results()
-    if planted is not None:
-        ok = bool((out["accept_len"] == planted + 1).all())
-    else:
-        ok = None
+    ok = bool((out["accept_len"] == planted + 1).all()) if planted is not None else None
+    # the LM-head launch between two events, same protocol
+    B.spec_verify_profile(dc.ver.h, 2)
+    lm_step_ms = timed_steps(dc.run, steps, flush)
+    lm_ms = dict(B.spec_verify_stage_times(dc.ver.h)).get("lm_head", float("nan"))
+    B.spec_verify_profile(dc.ver.h, 0)
+    stage_ms = {}
+    if stages:
+        # events around every stage (they add a few microseconds each)
+        B.spec_verify_profile(dc.ver.h, 1)
+        timed_steps(dc.run, steps, flush)
+        stage_ms = dict(B.spec_verify_stage_times(dc.ver.h))
+        B.spec_verify_profile(dc.ver.h, 0)
+    dc.close()
 
     n = st.n_rows
-    sb, sf = A.step_bytes(cfg, st, fp8=args.fp8), A.step_flops(cfg, st)
-    mfma_peak = FP8_PEAK_TFLOPS if args.fp8 else BF16_PEAK_TFLOPS
-    lm_ms = lm_live
-    lm_bytes = sb["lm_head"]
-    lm_flops = sf["lm_head"]
-    ai = lm_flops / lm_bytes
+    p10, p50, p90 = (float(x) for x in np.percentile(step_ms, [10, 50, 90]))
+    sb, sf = A.step_bytes(cfg, st, fp8=fp8), A.step_flops(cfg, st)
+    mfma_peak = FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
+    lm_bytes, lm_flops = sb["lm_head"], sf["lm_head"]
     ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if ai < ridge:
+    meas_bw = peaks["copy_gbs"] if peaks else None
+    meas_mfma = None if (fp8 or not peaks) else peaks["gemm_bf16_tflops"]
+    if lm_flops / lm_bytes < ridge:
         achieved = lm_bytes / (lm_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS}
+                "frac": achieved / HBM_PEAK_GBS,
+                "measured_peak": meas_bw, "frac_of_measured": achieved / meas_bw if meas_bw else None}
     else:
         achieved = lm_flops / (lm_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": mfma_peak, "unit": "TFLOP/s",
-                "frac": achieved / mfma_peak}
-    roof["traffic"] = None if args.fp8 else counters_traffic(cfg.name)
-    roof["kernel"] = "lm_head"
-    roof["kernel_ms"] = lm_ms
-    roof["algorithmic_bytes"] = lm_bytes
-    roof["algorithmic_flops"] = lm_flops
-    roof["mfma_frac"] = lm_flops / (lm_ms * 1e-3) / 1e12 / mfma_peak
-
-    step_s = ms * 1e-3
+                "frac": achieved / mfma_peak,
+                "measured_peak": meas_mfma, "frac_of_measured": achieved / meas_mfma if meas_mfma else None}
+    roof["traffic"] = None if fp8 else counters_traffic(cfg.name)
+    roof.update(kernel="lm_head", kernel_ms=lm_ms, algorithmic_bytes=lm_bytes, algorithmic_flops=lm_flops,
+                mfma_frac=lm_flops / (lm_ms * 1e-3) / 1e12 / mfma_peak,
+                hbm_frac=lm_bytes / (lm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    step_s = p50 * 1e-3
     res = {
-        "metric": METRIC,
-        "value": n / step_s,
-        "unit": "rows/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": ("bf16, LM head e4m3" if args.fp8 else "bf16") if cfg.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded; random-init weights of the stated shapes)",
+        "rows_per_s": n / step_s,
+        "ms_p50": p50,
         "config": {"workload": cfg.name, "rows": n, "trees": st.n_roots, "kv_tokens": int(st.kv_tokens),
                    "heads_q_kv": [cfg.n_q_heads, cfg.n_kv_heads], "head_dim": cfg.head_dim,
-                   "hidden": cfg.hidden, "vocab": cfg.vocab, "gamma": cfg.gamma, "seed": args.seed,
-                   "acceptance": "T=1 sampling" if args.sample else "greedy",
-                   "lm_head_format": "fp8 e4m3 (W8A8)" if args.fp8 else "native"},
+                   "hidden": cfg.hidden, "vocab": cfg.vocab, "gamma": cfg.gamma, "seed": seed,
+                   "dtype": cfg.dtype, "acceptance": "T=1 sampling" if sample else "greedy",
+                   "lm_head_format": "fp8 e4m3 (W8A8)" if fp8 else "native"},
         "roofline": roof,
+        "timing": {"ms_p10": p10, "ms_p50": p50, "ms_p90": p90, "ms_mean": float(step_ms.mean()),
+                   "steps": int(steps), "flush_bytes_before_each_step": FLUSH_BYTES,
+                   "events": "two HIP events on the run's stream around each step, profiling off",
+                   "wall_s_timed_loop": wall,
+                   "lm_head_loop_step_ms_p50": float(np.median(lm_step_ms))},
         "step": {"algorithmic_bytes": sb["total"], "algorithmic_flops": sf["total"],
-                 "device_ms_staged": stages.get("step"), "ms_per_step_staged": ms_staged,
-                 "lm_head_ms_staged": stages.get("lm_head"),
                  "hbm_frac_of_step": sb["total"] / step_s / 1e9 / HBM_PEAK_GBS,
-                 "stages_ms": {k: v for k, v in stages.items() if k != "step"},
+                 "hbm_frac_of_step_measured_peak": (sb["total"] / step_s / 1e9 / meas_bw) if meas_bw else None,
+                 "stages_ms": {k: v for k, v in stage_ms.items() if k != "step"},
+                 "device_ms_staged": stage_ms.get("step"),
                  "planted_accept_ok": ok,
                  "accept_len_mean": float(out["accept_len"].mean())},
     }
-    if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle on one sequence)")
-        res["cpu_baseline"] = cpu_baseline(inp, fp8=args.fp8)
+    if cpu:
+        log(f"[bench] {cfg.name}: cpu baseline (the oracle on whole sequences)")
+        res["cpu_baseline"] = cpu_baseline(inp, fp8=fp8, one_thread=one_thread)
     else:
         res["cpu_baseline"] = None
-    dc.close()
-    print(json.dumps(res))
-    return 0
+    del dc, inp, flush
+    torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":
