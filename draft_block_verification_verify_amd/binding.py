@@ -68,6 +68,8 @@ SYMBOLS = {
     "spec_verify_schedule": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
                                        C.c_void_p, C.c_int32, C.c_void_p, C.POINTER(C.c_double),
                                        C.POINTER(C.c_double)]),
+    "spec_verify_run_static": (C.c_int, [C.POINTER(SvConfig), C.c_void_p, C.c_void_p, C.POINTER(SvInputs),
+                                         C.POINTER(SvOutputs), C.c_void_p]),
     "spec_verify_destroy": (C.c_int, [C.c_void_p]),
     "spec_verify_last_error": (C.c_char_p, []),
     "spec_verify_profile": (C.c_int, [C.c_void_p, C.c_int32]),
@@ -133,6 +135,13 @@ def spec_verify_schedule(n_cand, cand_parent, cand_conf, curve_rows, curve_ms, m
                                       int(cr.shape[0]), cr.ctypes.data, cm.ctypes.data, int(max_rows),
                                       sel.ctypes.data, C.byref(tok), C.byref(ms)))
     return sel[:int(n_cand.sum())], tok.value, ms.value
+
+
+def spec_verify_run_static(cfg: SvConfig, w_o_ptr: int, w_lm_ptr: int, inputs: SvInputs, outputs: SvOutputs,
+                           stream: int | None = None) -> None:
+    """The handle-free, allocation-free step of an fp32 model (see spec_verify.h)."""
+    _check(lib().spec_verify_run_static(C.byref(cfg), C.c_void_p(w_o_ptr), C.c_void_p(w_lm_ptr), C.byref(inputs),
+                                        C.byref(outputs), C.c_void_p(stream or 0)))
 
 
 def spec_verify_destroy(h) -> None:

@@ -8,6 +8,7 @@
 #include <climits>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -313,6 +314,72 @@ sv_status check_run(const sv::Dims &dm, const sv_inputs *in, const sv_outputs *o
 
 }  // namespace
 
+
+// ----------------------------------------------------------------------------
+// spec_verify_run_static: a verify step of an fp32 model without a handle and
+// without any allocation.  Every per-run buffer lives in `scratch`, one
+// file-scope device array (each device the library runs on holds its own
+// copy, at its own address, until the process ends); its device address is
+// taken once per device with hipGetSymbolAddress, and only that address is
+// ever given to kernels or copies.  The plan reaches the device as kernel
+// arguments, kStaticChunkWords words per launch, so no host or pinned staging
+// buffer has to outlive the call.
+// ----------------------------------------------------------------------------
+
+namespace {
+
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+constexpr int kStaticMaxDevices = 64;
+constexpr int kStaticChunkWords = 880;   // 3520 bytes of plan per launch (kernel arguments well under 4 KB)
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kStaticMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+struct PlanChunk {
+  uint32_t first, words;
+  uint32_t w[kStaticChunkWords];
+};
+
+__global__ __launch_bounds__(256) void plan_chunk_kernel(PlanChunk c, uint32_t *dst) {
+  for (uint32_t i = threadIdx.x; i < c.words; i += 256) dst[c.first + i] = c.w[i];
+}
+
+// The device address of `scratch` on device `dev` (the current device).
+sv_status static_scratch(int dev, unsigned char **out) {
+  if (dev < 0 || dev >= kStaticMaxDevices) return fail(SV_ERR_UNSUPPORTED, "device index beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return hip_fail("hipGetSymbolAddress(scratch)", e);
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<unsigned char *>(g_scratch_ptr[dev]);
+  return SV_OK;
+}
+
+// Carves `scratch` into the run's buffers, 256-byte aligned, in order.
+struct Carver {
+  unsigned char *base;
+  size_t used = 0;
+  template <class T>
+  T *take(size_t bytes) {
+    T *p = reinterpret_cast<T *>(base + used);
+    used += (std::max<size_t>(bytes, 1) + 255) / 256 * 256;
+    return p;
+  }
+};
+
+}  // namespace
 
 extern "C" {
 
@@ -870,6 +937,114 @@ sv_status spec_verify_commit(sv_handle *h, const sv_inputs *in, const sv_outputs
   if (e != hipSuccess) return hip_fail("kernel launch", e);
   e = hipEventRecord(h->done, stream);
   if (e != hipSuccess) return hip_fail("hipEventRecord", e);
+  return SV_OK;
+}
+
+sv_status spec_verify_run_static(const sv_config *cfg, const void *w_o, const void *w_lm, const sv_inputs *in,
+                                 const sv_outputs *out, void *stream_v) {
+  g_err.clear();
+  if (!cfg || !in || !out) return fail(SV_ERR_INVALID_ARG, "cfg, inputs and outputs must be non-null");
+  if (!w_o || !w_lm) return fail(SV_ERR_INVALID_ARG, "w_o and w_lm must be non-null device pointers");
+  const sv::Dims dm{cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, cfg->hidden,        cfg->vocab,
+                    cfg->dtype,     cfg->max_rows,   cfg->max_roots, cfg->max_tree_rows, cfg->max_pos,
+                    cfg->weight_format};
+  std::string err;
+  const int pc = sv::check_dims(dm, &err);
+  if (pc != sv::P_OK) return fail(sv_status(pc), err);
+  if (dm.dtype != SV_F32 || dm.weight_format != SV_WEIGHTS_NATIVE)
+    return fail(SV_ERR_UNSUPPORTED, "spec_verify_run_static takes fp32 models (weights used as given)");
+  if (!(cfg->rope_base > 1.0f) || !std::isfinite(cfg->rope_base))
+    return fail(SV_ERR_INVALID_ARG, "rope_base must be a finite value > 1");
+  if (!(cfg->norm_eps >= 0.0f) || !std::isfinite(cfg->norm_eps))
+    return fail(SV_ERR_INVALID_ARG, "norm_eps must be finite and >= 0");
+  if ((reinterpret_cast<uintptr_t>(w_o) | reinterpret_cast<uintptr_t>(w_lm)) % 16 != 0)
+    return fail(SV_ERR_INVALID_ARG, "w_o and w_lm must be 16-byte aligned");
+  const int64_t V = dm.vocab, H = dm.hidden, D = dm.d, Hq = dm.Hq, Hkv = dm.Hkv;
+  const int n_dch = int(ceil_div(V, kDChunk)), n_och = int(ceil_div(V, kOChunk)), n_tiles = int(ceil_div(V, 256));
+  sv::Plan plan;
+  sv::MetaLayout lay{};
+  {
+    const sv_status vs = check_run(dm, in, out, sv::slot_capacity(dm), 1, n_och, &plan, &lay);
+    if (vs != SV_OK) return vs;
+  }
+  const int64_t n = plan.n, nd = plan.n_draft, R = plan.R;
+  // the run's buffers, in the order they are carved from `scratch`
+  const size_t need_meta = (lay.total + 255) / 256 * 256;
+  const size_t f = 4;
+  const size_t sizes[] = {need_meta,
+                          size_t(n * Hq * D) * f,               // rotated queries
+                          size_t(n * Hkv * D) * f,              // rotated row keys
+                          size_t(n * Hq * D) * f,               // attention output
+                          size_t(n * H) * f,                    // W_o output
+                          size_t(n * H) * f,                    // normalised rows
+                          out->logits ? 0 : size_t(n * V) * f,  // logits
+                          size_t(n * n_tiles) * f,              // tile max
+                          size_t(n * n_tiles) * f,              // tile sum
+                          size_t(n * n_tiles) * f,              // tile argmax
+                          size_t(nd * n_dch) * 8,               // drafter chunk records
+                          size_t(nd) * f,                       // drafter logsumexp
+                          size_t(nd * n_och) * f,               // overlap chunk sums
+                          size_t(R) * f,                        // rejected child (T = 1)
+                          size_t(R * n_och) * f};               // bonus chunk sums (T = 1)
+  size_t total = 0;
+  for (size_t b : sizes) total += (std::max<size_t>(b, 1) + 255) / 256 * 256;
+  if (total > kStaticScratchBytes)
+    return fail(SV_ERR_CAPACITY, "this run needs " + std::to_string(total) + " bytes of scratch; " +
+                                     "spec_verify_run_static has " + std::to_string(kStaticScratchBytes));
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail("hipGetDeviceProperties", e);
+  if (std::strstr(prop.gcnArchName, "gfx950") == nullptr)
+    return fail(SV_ERR_UNSUPPORTED, std::string("device ") + std::to_string(dev) + " is " + prop.gcnArchName +
+                                        "; this library is built for gfx950 (MI355X) only");
+  unsigned char *base = nullptr;
+  {
+    const sv_status ss = static_scratch(dev, &base);
+    if (ss != SV_OK) return ss;
+  }
+  Carver cv{base};
+  char *m = cv.take<char>(sizes[0]);
+  F32Bufs fb{};
+  fb.q_rot = cv.take<float>(sizes[1]);
+  fb.k_rot = cv.take<float>(sizes[2]);
+  fb.o_act = cv.take<float>(sizes[3]);
+  fb.h_part = cv.take<float>(sizes[4]);
+  fb.hn = cv.take<float>(sizes[5]);
+  float *logits = out->logits ? out->logits : cv.take<float>(sizes[6]);
+  fb.t_max = cv.take<float>(sizes[7]);
+  fb.t_sum = cv.take<float>(sizes[8]);
+  fb.t_arg = cv.take<int32_t>(sizes[9]);
+  float2 *dpart = cv.take<float2>(sizes[10]);
+  float *lse_q = cv.take<float>(sizes[11]);
+  float *opart = cv.take<float>(sizes[12]);
+  int32_t *rej_child = cv.take<int32_t>(sizes[13]);
+  float *rpart = cv.take<float>(sizes[14]);
+
+  // the plan: packed on the host, sent as kernel arguments
+  const hipStream_t stream = static_cast<hipStream_t>(stream_v);
+  std::vector<uint32_t> words((lay.total + 3) / 4, 0u);
+  sv::MetaLayout lay2{};
+  sv::pack_plan(plan, dm.Hkv, words.data(), &lay2);
+  PlanChunk chunk;
+  for (size_t first = 0; first < words.size(); first += kStaticChunkWords) {
+    chunk.first = uint32_t(first);
+    chunk.words = uint32_t(std::min<size_t>(kStaticChunkWords, words.size() - first));
+    std::memcpy(chunk.w, words.data() + first, chunk.words * 4);
+    hipLaunchKernelGGL(plan_chunk_kernel, dim3(1), dim3(256), 0, stream, chunk, reinterpret_cast<uint32_t *>(m));
+  }
+  sv::VocabArgs va = vocab_args(plan, m, lay, int(V), false, in, out,
+                                VocabBufs{logits, nullptr, fb.t_max, fb.t_sum, fb.t_arg, n_tiles, dpart, n_dch, lse_q,
+                                          opart, n_och});
+  auto none = [](const char *) {};
+  auto none_end = []() {};
+  enqueue_f32(dm, *cfg, m, lay, fb, w_o, w_lm, in, va, stream, none, none_end);
+  enqueue_tail(va, in, m, lay, rej_child, rpart, stream, none, none_end);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail("kernel launch", e);
   return SV_OK;
 }
 

@@ -234,6 +234,28 @@ sv_status spec_verify_schedule(int32_t n_req, const int32_t *n_cand, const int32
                                const float *curve_ms, int32_t max_rows, int32_t *selected,
                                double *expected_tokens, double *step_ms);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): one verify
+ * step of an fp32 model (cfg->dtype SV_F32, native weights) without a handle.
+ * w_o and w_lm are DEVICE [hidden, Hq*d] and [vocab, hidden] fp32, used as
+ * given; cfg, in and out mean what they mean for spec_verify_create and
+ * spec_verify_run, and every check of those calls happens before anything is
+ * enqueued.  The call allocates no device, pinned or managed memory: every
+ * per-run buffer (metadata, rotated rows, attention output, hidden rows,
+ * logits when out->logits is NULL, tile and chunk records) lives in one
+ * 8 MiB array of the library, which every device it runs on holds until the
+ * process ends; a run that needs more fails with SV_ERR_CAPACITY (the logits
+ * take rows x vocab x 4 bytes unless the caller passes a logits buffer).  The
+ * step's metadata travels as kernel arguments, so host arrays may be reused
+ * as soon as the call returns; host-side planning uses ordinary heap memory
+ * of a few KB.  All calls on one device share that device's array, which
+ * keeps the last call's contents: calls that overlap on one device race, so
+ * the caller orders them (one stream, or events).  Enqueues on `stream`
+ * (hipStream_t; NULL = default) and never waits on the host.  Fails with
+ * SV_ERR_UNSUPPORTED for other dtypes, weight formats or devices. */
+sv_status spec_verify_run_static(const sv_config *cfg, const void *w_o, const void *w_lm, const sv_inputs *in,
+                                 const sv_outputs *out, void *stream);
+
 /* Wait for the handle's last enqueued step, then free everything it owns.
  * NULL is accepted. */
 sv_status spec_verify_destroy(sv_handle *h);

@@ -311,3 +311,31 @@ def test_plan_capacities(plan_lib):
     dims[7] = 1          # max_roots
     st, err, *_ = plan(plan_lib, dims, [-1, -1], range(2), [0, 0], [1, 1], 1)
     assert st == B.SV_ERR_CAPACITY and "max_roots" in err
+
+
+def test_run_static_rejects_before_device(libsv):
+    # the allocation-free entry point: configuration, dtype and argument
+    # errors come back before any device call (no GPU needed here)
+    inp = B.SvInputs()
+    out = B.SvOutputs()
+    f = libsv.spec_verify_run_static
+    assert f(None, C.c_void_p(16), C.c_void_p(16), C.byref(inp), C.byref(out), None) == B.SV_ERR_INVALID_ARG
+    assert f(C.byref(good_cfg()), None, C.c_void_p(16), C.byref(inp), C.byref(out), None) == B.SV_ERR_INVALID_ARG
+    assert f(C.byref(good_cfg(dtype=B.SV_BF16)), C.c_void_p(16), C.c_void_p(16), C.byref(inp), C.byref(out),
+             None) == B.SV_ERR_UNSUPPORTED
+    assert "fp32" in B.spec_verify_last_error()
+    assert f(C.byref(good_cfg(head_dim=96)), C.c_void_p(16), C.c_void_p(16), C.byref(inp), C.byref(out),
+             None) == B.SV_ERR_UNSUPPORTED
+    # a valid tree whose rows are not given: refused by the argument checks
+    parent = np.array([-1, 0], np.int32)
+    pos = np.array([3, 4], np.int32)
+    off = np.array([0], np.int64)
+    ln = np.array([3], np.int32)
+    inp = B.SvInputs(2, 1, parent.ctypes.data_as(C.POINTER(C.c_int32)), pos.ctypes.data_as(C.POINTER(C.c_int32)),
+                     off.ctypes.data_as(C.POINTER(C.c_int64)), ln.ctypes.data_as(C.POINTER(C.c_int32)), 3,
+                     16, 16, 0, 0, 0, 0, 0, 0, 0, 0)
+    assert f(C.byref(good_cfg()), C.c_void_p(16), C.c_void_p(16), C.byref(inp), C.byref(out),
+             None) == B.SV_ERR_INVALID_ARG
+    # misaligned weights
+    assert f(C.byref(good_cfg()), C.c_void_p(20), C.c_void_p(16), C.byref(inp), C.byref(out),
+             None) == B.SV_ERR_INVALID_ARG
