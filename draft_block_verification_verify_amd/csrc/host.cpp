@@ -156,6 +156,8 @@ sv::VocabArgs vocab_args(const sv::Plan &plan, const char *m, const sv::MetaLayo
   va.draft_row = reinterpret_cast<const int32_t *>(m + lay.draft_row);
   va.tree_start = reinterpret_cast<const int32_t *>(m + lay.tree_start);
   va.tree_rows = reinterpret_cast<const int32_t *>(m + lay.tree_rows);
+  va.row_tree = reinterpret_cast<const int32_t *>(m + lay.row_tree);
+  va.tree_done = reinterpret_cast<int32_t *>(const_cast<char *>(m) + lay.tree_done);
   va.draft_ids = in->draft_ids;
   va.drafter = in->drafter_logits;
   va.drafter_bf16 = bf16 ? 1 : 0;
@@ -245,8 +247,9 @@ void enqueue_tail(const sv::VocabArgs &va, const sv_inputs *in, const char *m, c
                   int32_t *rej_child, float *rpart, hipStream_t stream, Begin &&begin, End &&end) {
   if (va.n <= 64) {
     // few rows: few tile records per row, so the overlap workgroups merge
-    // their own logsumexps and the two passes share one launch
-    begin("combine_overlap");
+    // their own logsumexps, the two passes share one launch, and the
+    // workgroup that completes a tree runs its acceptance walk
+    begin("combine_overlap_accept");
     sv::launch_combine_overlap(va, stream);
     end();
   } else {
@@ -256,10 +259,10 @@ void enqueue_tail(const sv::VocabArgs &va, const sv_inputs *in, const char *m, c
     begin("overlap");
     sv::launch_overlap_partial(va, stream);
     end();
+    begin("accept");
+    sv::launch_accept(va, stream);
+    end();
   }
-  begin("accept");
-  sv::launch_accept(va, stream);
-  end();
   if (in->mode == SV_MODE_SAMPLE) {
     sv::SampleArgs sa{};
     sa.row_child = reinterpret_cast<const int32_t *>(m + lay.row_child);
@@ -724,7 +727,10 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     ra.q_lo_off = q_lo;
     ra.k_lo_off = k_lo;
     ra.n = n;
-    ra.ry = int(ceil_div(int64_t(Hq + Hkv) * (D / 2), 256));
+    // workgroups per row: about 512 in all (each builds its row's table once),
+    // at most one per 256 (head, pair) items
+    ra.ry = int(std::max<int64_t>(1, std::min<int64_t>(ceil_div(int64_t(Hq + Hkv) * (D / 2), 256),
+                                                       ceil_div(512, int64_t(n)))));
     begin("rope_drafter_stats");
     sv::launch_rope_drafter_bf16(ra, va, stream);
     end();

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(const T *__restrict__ q,
                                                         T *__restrict__ q_out, T *__restrict__ k_out,
                                                         const int32_t *__restrict__ row_pos, int Hq,
                                                         int Hkv, int D, double base) {
-  rope_rows_block<T>(q, k, q_out, k_out, row_pos, Hq, Hkv, D, base, 0, 0, blockIdx.x, blockIdx.y);
+  rope_rows_block<T>(q, k, q_out, k_out, row_pos, Hq, Hkv, D, base, 0, 0, blockIdx.x, blockIdx.y, gridDim.y);
 }
 
 // ----------------------------------------------------------------------------
@@ -170,9 +170,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_mfma_kernel(AttnArgs a) {
     const i32x4 rsv = make_rsrc(pre ? pv : rv, pre ? pre_bytes : row_bytes);
     const uint32_t sbase = lds0 + uint32_t((s % STG) * 2 * TILEB) + uint32_t(w * 1024);
 #pragma unroll
-    for (int i = 0; i < HPER; ++i) dma16(rsk, sbase + uint32_t(NW * i * 1024), vbase + voff_lane[i], 0);
+    for (int i = 0; i < HPER; ++i) dma16<kNtStream>(rsk, sbase + uint32_t(NW * i * 1024), vbase + voff_lane[i], 0);
 #pragma unroll
-    for (int i = 0; i < HPER; ++i) dma16(rsv, sbase + uint32_t(TILEB + NW * i * 1024), vbase + voff_lane[i], 0);
+    for (int i = 0; i < HPER; ++i) dma16<kNtStream>(rsv, sbase + uint32_t(TILEB + NW * i * 1024), vbase + voff_lane[i], 0);
   };
 
   // ---- compute side: the current item's query fragments (B operand of

@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     const uint32_t base = lds0 + (s % kSkST) * SST;
     const int soff = (ks + s * 64) * 2;
 #pragma unroll
-    for (int i = 0; i < WI; ++i) dma16(rw, base + (w * WI + i) * 1024, woff[i], BLOCKED ? (ks / 32 + 2 * s) * 16384 : soff);
+    for (int i = 0; i < WI; ++i) dma16<kNtStream>(rw, base + (w * WI + i) * 1024, woff[i], BLOCKED ? (ks / 32 + 2 * s) * 16384 : soff);
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       const int ia = w * AI + i;
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
     const uint32_t base = lds0 + (s % ST) * SST;
     const int soff = BLOCKED ? (ks / 32 + s) * 16384 : (ks + s * 32) * 2;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(sr.rw, base + (w * 32 + i * 16) * 64, off[i], soff);
+    for (int i = 0; i < 2; ++i) dma16<kNtStream>(sr.rw, base + (w * 32 + i * 16) * 64, off[i], soff);
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16(sr.ra, base + kTBN * 64 + (w * 32 + i * 16) * 64, off[i], soff);
     if constexpr (LO) {
@@ -582,7 +582,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
     const uint32_t base = lds0 + (s % kTST) * kTSST;
     const int soff = s * 16384;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(sr.rw, base + (w * 32 + i * 16) * 64, off[i], soff);
+    for (int i = 0; i < 2; ++i) dma16<kNtStream>(sr.rw, base + (w * 32 + i * 16) * 64, off[i], soff);
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16(sr.ra, base + kTBN * 64 + (w * 32 + i * 16) * 64, sr.ao[i], soff);
   };

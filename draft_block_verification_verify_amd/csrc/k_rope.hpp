@@ -29,44 +29,57 @@ __device__ __forceinline__ void st_q(uint16_t *p, int64_t lo_off, double v) {
 }
 __device__ __forceinline__ void st_q(float *p, int64_t, double v) { *p = float(v); }
 
-// One thread per (row, head, pair): workgroup (i, by) of 256 threads takes
-// pairs by * 256 + thread of row i.  Each workgroup first builds the row's sine/cosine table (d/2 <= 128
-// entries), so every thread then does one load pair, one rotation and one
-// store pair, with no chain of dependent memory accesses.
+// Workgroup (i, by) of ry workgroups of row i takes the row's (head, pair)
+// items by * 256 + thread, then every ry * 256 further.  Each workgroup first
+// builds the row's sine/cosine table (d/2 <= 128 entries) once, then rotates
+// its items four at a time, every load of the four issued before the
+// arithmetic.
 template <typename T>
 __device__ __forceinline__ void rope_rows_block(const T *__restrict__ q, const T *__restrict__ k,
                                                 T *__restrict__ q_out, T *__restrict__ k_out,
                                                 const int32_t *__restrict__ row_pos, int Hq, int Hkv, int D,
-                                                double base, int64_t q_lo_off, int64_t k_lo_off, int i, int by) {
+                                                double base, int64_t q_lo_off, int64_t k_lo_off, int i, int by,
+                                                int ry) {
   __shared__ double cs[128], sn[128];   // cos, sin of pos * theta_k, k < D/2 <= 128
   const int half = D / 2;
-  const int heads = Hq + Hkv;
-  const int p = by * blockDim.x + threadIdx.x;
-  const bool active = p < heads * half;
-  const int hh = active ? p / half : 0, kk = p % half;
-  // issue this thread's loads before the table's arithmetic
-  const T *src = hh < Hq ? q + (int64_t(i) * Hq + hh) * D : k + (int64_t(i) * Hkv + (hh - Hq)) * D;
-  double a = 0.0, b = 0.0;
-  if (active) {
-    a = ld(src + kk);
-    b = ld(src + kk + half);
-  }
+  const int items = (Hq + Hkv) * half;
   const double pos = double(row_pos[i]);
   if (threadIdx.x < half) {
     const double theta = pow(base, -2.0 * double(threadIdx.x) / double(D));
     sincos(pos * theta, &sn[threadIdx.x], &cs[threadIdx.x]);
   }
   __syncthreads();
-  if (!active) return;
-  const double c = cs[kk], s = sn[kk];
-  if (hh < Hq) {
-    T *dst = q_out + (int64_t(i) * Hq + hh) * D;
-    st_q(dst + kk, q_lo_off, a * c - b * s);
-    st_q(dst + kk + half, q_lo_off, b * c + a * s);
-  } else {
-    T *dst = k_out + (int64_t(i) * Hkv + (hh - Hq)) * D;
-    st_q(dst + kk, k_lo_off, a * c - b * s);
-    st_q(dst + kk + half, k_lo_off, b * c + a * s);
+  const int stride = ry * blockDim.x;
+  for (int p0 = by * blockDim.x + threadIdx.x; p0 < items; p0 += 4 * stride) {
+    double a[4], b[4];
+    const T *src[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = p0 + u * stride;
+      const int hh = p < items ? p / half : 0, kk = p % half;
+      src[u] = hh < Hq ? q + (int64_t(i) * Hq + hh) * D : k + (int64_t(i) * Hkv + (hh - Hq)) * D;
+      a[u] = b[u] = 0.0;
+      if (p < items) {
+        a[u] = ld(src[u] + kk);
+        b[u] = ld(src[u] + kk + half);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = p0 + u * stride;
+      if (p >= items) continue;
+      const int hh = p / half, kk = p % half;
+      const double c = cs[kk], sv_ = sn[kk];
+      if (hh < Hq) {
+        T *dst = q_out + (int64_t(i) * Hq + hh) * D;
+        st_q(dst + kk, q_lo_off, a[u] * c - b[u] * sv_);
+        st_q(dst + kk + half, q_lo_off, b[u] * c + a[u] * sv_);
+      } else {
+        T *dst = k_out + (int64_t(i) * Hkv + (hh - Hq)) * D;
+        st_q(dst + kk, k_lo_off, a[u] * c - b[u] * sv_);
+        st_q(dst + kk + half, k_lo_off, b[u] * c + a[u] * sv_);
+      }
+    }
   }
 }
 

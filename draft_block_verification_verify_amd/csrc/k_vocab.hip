@@ -145,8 +145,7 @@ __global__ __launch_bounds__(256) void rope_drafter_kernel(RopeArgs r, VocabArgs
   const int nr = r.n * r.ry;
   if (b < nr) {
     rope_rows_block<uint16_t>(r.q, r.k, r.q_out, r.k_out, r.row_pos, r.Hq, r.Hkv, r.D, r.base, r.q_lo_off, r.k_lo_off,
-                              b / r.ry,
-                              b % r.ry);
+                              b / r.ry, b % r.ry, r.ry);
   } else {
     const int d = b - nr;
     drafter_partial_block(a, d % a.n_dch, d / a.n_dch);
@@ -486,26 +485,10 @@ __global__ __launch_bounds__(256) void overlap_partial_kernel(VocabArgs a) {
   overlap_block(a, blockIdx.x, t, j, a.row_lse[j], a.lse_q[t]);
 }
 
-// Small batches: the row statistics and the overlap sums in one launch.
-// Workgroups [0, n) combine row b; the rest take overlap chunks, each
-// merging its parent's and its drafter row's records itself with the same
-// code and order as the combining workgroups (so with the same values).
-__global__ __launch_bounds__(256) void combine_overlap_kernel(VocabArgs a) {
-  const int b = blockIdx.x;
-  if (b < a.n) {
-    row_combine_block(a, b);
-    return;
-  }
-  const int d = b - a.n, c = d % a.n_och, t = d / a.n_och;
-  const int j = a.row_parent[a.draft_row[t]];
-  const MaxSumArg r = row_stats_block(a, j);
-  const MaxSum q = drafter_stats_block(a, t);
-  overlap_block(a, c, t, j, r.m + logf(r.s), q.m + logf(q.s));
-}
-
-// One wavefront per tree (at most 64 rows).
-__global__ __launch_bounds__(64) void accept_kernel(VocabArgs a) {
-  const int r = blockIdx.x, lane = threadIdx.x;
+// Overlaps, survival products and the greedy walk of tree r, by a whole
+// workgroup of at least 64 threads (thread k < T takes the tree's row k).
+__device__ __forceinline__ void accept_tree(const VocabArgs &a, int r) {
+  const int lane = threadIdx.x;
   const int s0 = a.tree_start[r], T = a.tree_rows[r];
   __shared__ float ov[kMaxTreeRows];
   __shared__ int par[kMaxTreeRows], arg[kMaxTreeRows], did[kMaxTreeRows];
@@ -563,6 +546,46 @@ __global__ __launch_bounds__(64) void accept_kernel(VocabArgs a) {
     a.last_row[r] = s0 + cur;
   }
 }
+
+// Small batches: the row statistics and the overlap sums in one launch.
+// Workgroups [0, n) combine row b; the rest take overlap chunks, each
+// merging its parent's and its drafter row's records itself with the same
+// code and order as the combining workgroups (so with the same values).
+//
+// A tree is complete when its T combine workgroups and the n_och overlap
+// workgroups of each of its T - 1 draft rows are done; each counts itself in
+// the tree's counter (after a device-scope release of its results), and the
+// one that brings the count to T + (T - 1) n_och runs the tree's acceptance
+// walk after a device-scope acquire.  No workgroup waits on another.
+__global__ __launch_bounds__(256) void combine_overlap_kernel(VocabArgs a) {
+  const int b = blockIdx.x;
+  int tree;
+  if (b < a.n) {
+    row_combine_block(a, b);
+    tree = a.row_tree[b];
+  } else {
+    const int d = b - a.n, c = d % a.n_och, t = d / a.n_och;
+    const int j = a.row_parent[a.draft_row[t]];
+    const MaxSumArg r = row_stats_block(a, j);
+    const MaxSum q = drafter_stats_block(a, t);
+    overlap_block(a, c, t, j, r.m + logf(r.s), q.m + logf(q.s));
+    tree = a.row_tree[a.draft_row[t]];
+  }
+  __shared__ int last;
+  __syncthreads();   // every thread's stores issued and visible in the workgroup
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const int T = a.tree_rows[tree];
+    const int old = atomicAdd(a.tree_done + tree, 1);
+    last = old == T + (T - 1) * a.n_och - 1;
+    if (last) __threadfence();
+  }
+  __syncthreads();
+  if (last) accept_tree(a, tree);
+}
+
+// One workgroup per tree (at most 64 rows).
+__global__ __launch_bounds__(64) void accept_kernel(VocabArgs a) { accept_tree(a, blockIdx.x); }
 
 // ----------------------------------------------------------------------------
 // T = 1 stochastic verification of chains.  One thread walks each chain (at

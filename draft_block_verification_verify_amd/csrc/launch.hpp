@@ -156,6 +156,8 @@ void launch_bf16_to_f16_blocked(const uint16_t *src, uint16_t *dst, int rows, in
 struct VocabArgs {
   int n, n_draft, R, V;
   const int32_t *row_parent, *row_draft, *draft_row, *tree_start, *tree_rows;
+  const int32_t *row_tree;      // [n] tree of each row
+  int32_t *tree_done;           // [R] completion counters (zero at the start of a run)
   const int32_t *draft_ids;
   const void *drafter;          // [n_draft, V] bf16 or f32
   int drafter_bf16;

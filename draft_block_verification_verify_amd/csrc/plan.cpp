@@ -121,6 +121,7 @@ MetaLayout meta_layout(int n, int R, int n_draft, int n_items, int n_runs, int n
   L.tree_rows = take(4 * size_t(R));
   L.tree_kv_len = take(4 * size_t(R));
   L.tree_kv_off = take(8 * size_t(R));
+  L.tree_done = take(4 * size_t(R));
   L.items = take(sizeof(AttnItem) * size_t(std::max(n_items, 1)));
   L.runs = take(sizeof(AttnRun) * size_t(std::max(n_runs, 1)));
   L.groups = take(sizeof(AttnGroup) * size_t(std::max(n_groups, 1)));
@@ -425,6 +426,7 @@ void pack_plan(const Plan &p, int Hkv, void *dst, MetaLayout *lay) {
   put(L.tree_rows, p.tree_rows.data(), 4 * size_t(p.R));
   put(L.tree_kv_len, p.tree_kv_len.data(), 4 * size_t(p.R));
   put(L.tree_kv_off, p.tree_kv_off.data(), 8 * size_t(p.R));
+  std::memset(b + L.tree_done, 0, 4 * size_t(p.R));
   put(L.items, p.items.data(), sizeof(AttnItem) * p.items.size());
   put(L.runs, p.runs.data(), sizeof(AttnRun) * p.runs.size());
   put(L.groups, p.groups.data(), sizeof(AttnGroup) * size_t(n_groups));

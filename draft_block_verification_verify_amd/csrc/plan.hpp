@@ -139,6 +139,7 @@ struct MetaLayout {
   size_t row_tree, row_local, row_pos, row_parent, row_draft, row_anc, row_child, draft_row;
   size_t row_pack, row_plocal, row_klen, row_panc;
   size_t tree_start, tree_rows, tree_kv_len, tree_kv_off;
+  size_t tree_done;   // per-tree completion counters, zero in every upload
   size_t items, runs, groups;
   size_t total;
 };
