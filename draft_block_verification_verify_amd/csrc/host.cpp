@@ -247,11 +247,17 @@ void enqueue_tail(const sv::VocabArgs &va, const sv_inputs *in, const char *m, c
                   int32_t *rej_child, float *rpart, hipStream_t stream, Begin &&begin, End &&end) {
   if (va.n <= 64) {
     // few rows: few tile records per row, so the overlap workgroups merge
-    // their own logsumexps, the two passes share one launch, and the
-    // workgroup that completes a tree runs its acceptance walk
-    begin("combine_overlap_accept");
+    // their own logsumexps and the two passes share one launch; in small
+    // launches the workgroup that completes a tree runs its acceptance walk
+    const bool fused = sv::combine_overlap_accepts(va);
+    begin(fused ? "combine_overlap_accept" : "combine_overlap");
     sv::launch_combine_overlap(va, stream);
     end();
+    if (!fused) {
+      begin("accept");
+      sv::launch_accept(va, stream);
+      end();
+    }
   } else {
     begin("row_combine");
     sv::launch_row_combine(va, stream);

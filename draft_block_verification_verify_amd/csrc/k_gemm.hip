@@ -312,6 +312,18 @@ constexpr size_t kTiledLdsLo = size_t(kTSTLo) * kTSSTLo;
 template <bool STATS, bool BLOCKED, bool LO = false>
 __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
   static_assert(!LO || (BLOCKED && !STATS), "the hi + lo activation pair is for the blocked W_o launch");
+  // PP (the LM head): waves 4-7 run half a K step behind waves 0-3 (one
+  // barrier later, the same code), so one group's fragment reads overlap the
+  // other group's MFMAs on each SIMD instead of every wave reading, then
+  // every wave multiplying.  The lagging group waits for its share of one
+  // stage more than the leading group before each barrier, and each group
+  // drains its fragment reads before its mid-step barrier, so every read
+  // follows every wave's copy of that stage and every refill follows every
+  // wave's reads of the slot (tests/test_lm_head_protocol.py checks a model
+  // of all waves' barrier sequences for 3-5 stages and 1-17 steps).  Same-box A/B, 256 rows over
+  // 248320 x 5120 weights: 707 -> 671 us; 448 rows over 151936 x 4096:
+  // 671 -> 641 us.
+  constexpr bool PP = STATS;
   // DMA instructions per wave per stage: 2 weight + 2 activation (+ 2 lo)
   constexpr int PER = LO ? 6 : 4;
   constexpr int ST = LO ? kTSTLo : kTST;        // ring stages
@@ -320,6 +332,9 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r32 = lane & 31, kg = lane >> 5;
   const int wn = w & 1, wt = w >> 1;
+  // wave-uniform (a scalar value), so that the barriers it selects sit
+  // under scalar branches
+  const bool lag = __builtin_amdgcn_readfirstlane(w) >= 4;
   const int n_ttiles = (g.rows + kTBT - 1) / kTBT;
   const int n_ntiles = (g.N + kTBN - 1) / kTBN;
   const int n_tiles_all = ((n_ntiles + 7) / 8) * 8 * n_ttiles;
@@ -363,8 +378,14 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
   auto issue = [&](const Src &sr, int s) {
     const uint32_t base = lds0 + (s % ST) * SST;
     const int soff = BLOCKED ? (ks / 32 + s) * 16384 : (ks + s * 32) * 2;
+    // weights: the non-temporal hint when no other row tile reads them again
+    if (n_ttiles == 1) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16<kNtStream>(sr.rw, base + (w * 32 + i * 16) * 64, off[i], soff);
+      for (int i = 0; i < 2; ++i) dma16<kNtStream>(sr.rw, base + (w * 32 + i * 16) * 64, off[i], soff);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) dma16(sr.rw, base + (w * 32 + i * 16) * 64, off[i], soff);
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16(sr.ra, base + kTBN * 64 + (w * 32 + i * 16) * 64, off[i], soff);
     if constexpr (LO) {
@@ -400,8 +421,22 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[v][t][j] = 0.f;
 
+    if (PP && lag) {
+      // half a step behind: this barrier meets the leading group's first
+      // one, after which it reads stage 0, so this group's share of stage 0
+      // must have landed
+      const int younger0 = min(ST - 2, nk - 1);
+      if (younger0 >= 2)
+        wait_and_barrier<2 * PER>();
+      else if (younger0 == 1)
+        wait_and_barrier<PER>();
+      else
+        wait_and_barrier<0>();
+    }
     for (int s = 0; s < nk; ++s) {
-      const int younger = min(ST - 2, nk - 1 - s);
+      // the lagging group waits for its share of stage s + 1 as well: the
+      // leading group reads that stage after the next barrier
+      const int younger = PP && lag ? max(0, min(ST - 3, nk - 2 - s)) : min(ST - 2, nk - 1 - s);
       if (younger >= 2)
         wait_and_barrier<2 * PER>();
       else if (younger == 1)
@@ -426,6 +461,14 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
           if constexpr (LO) bl[j][t] = lds16(base + (kTBN + kTBT) * 64 + R * 64 + ((q ^ ((R >> 1) & 3)) << 4));
         }
       }
+      if constexpr (PP) {
+        // this group's reads are done (so the slot may be refilled after the
+        // other group's next barrier); its MFMAs now run while the other
+        // group reads
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -436,6 +479,7 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
             if constexpr (LO) acc[v][t] = mfma32h(af[j][v], bl[j][t], acc[v][t]);
           }
     }
+    if (PP && !lag) asm volatile("s_barrier" ::: "memory");   // the lagging group's first barrier
 
     // epilogue of this tile (vector-memory waits count stores too, so the
     // next tile's loads are issued only after the stores)
@@ -581,8 +625,14 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
   auto issue = [&](const Src &sr, int s) {
     const uint32_t base = lds0 + (s % kTST) * kTSST;
     const int soff = s * 16384;
+    // weights: the non-temporal hint when no other row tile reads them again
+    if (n_ttiles == 1) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16<kNtStream>(sr.rw, base + (w * 32 + i * 16) * 64, off[i], soff);
+      for (int i = 0; i < 2; ++i) dma16<kNtStream>(sr.rw, base + (w * 32 + i * 16) * 64, off[i], soff);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) dma16(sr.rw, base + (w * 32 + i * 16) * 64, off[i], soff);
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16(sr.ra, base + kTBN * 64 + (w * 32 + i * 16) * 64, sr.ao[i], soff);
   };

@@ -57,9 +57,20 @@ __device__ __forceinline__ float sum_block256(float v) {
 }
 
 // 8 consecutive drafter logits as floats (bf16 or fp32 source)
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16 bytes with the non-temporal hint: the drafter logits and the LM head's
+// fp16 probabilities are streamed by each pass once (measured under a 512 MB
+// write flush before each step: the drafter-statistics pass of 224 rows x
+// 248320 bf16 logits 51 -> 36 us, the overlap pass 48 -> 42 us)
+__device__ __forceinline__ uint4 ld16s(const void *p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ void load8(const void *base, int bf16, int64_t idx, float (&x)[8]) {
   if (bf16) {
-    const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + idx);
+    const uint4 u = ld16s(static_cast<const uint16_t *>(base) + idx);
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int t = 0; t < 8; ++t) x[t] = __uint_as_float((t & 1) ? (w[t >> 1] & 0xFFFF0000u) : (w[t >> 1] << 16));
@@ -406,9 +417,8 @@ __device__ __forceinline__ void overlap_block(const VocabArgs &a, int c, int t, 
       for (int g = 0; g < NG; ++g) {
         const int u = lo + tid * 8 + g * 2048;
         const bool in = u < hi;
-        hq[g] = in ? *reinterpret_cast<const uint4 *>(pp + u) : make_uint4(0, 0, 0, 0);
-        hb[g] = in ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.drafter) + qrow + u)
-                   : make_uint4(0, 0, 0, 0);
+        hq[g] = in ? ld16s(pp + u) : make_uint4(0, 0, 0, 0);
+        hb[g] = in ? ld16s(static_cast<const uint16_t *>(a.drafter) + qrow + u) : make_uint4(0, 0, 0, 0);
         sc[g] = in ? tm[u >> 8] : -INFINITY;
       }
 #pragma unroll
@@ -552,11 +562,18 @@ __device__ __forceinline__ void accept_tree(const VocabArgs &a, int r) {
 // merging its parent's and its drafter row's records itself with the same
 // code and order as the combining workgroups (so with the same values).
 //
-// A tree is complete when its T combine workgroups and the n_och overlap
-// workgroups of each of its T - 1 draft rows are done; each counts itself in
-// the tree's counter (after a device-scope release of its results), and the
-// one that brings the count to T + (T - 1) n_och runs the tree's acceptance
-// walk after a device-scope acquire.  No workgroup waits on another.
+// ACCEPT: a tree is complete when its T combine workgroups and the n_och
+// overlap workgroups of each of its T - 1 draft rows are done; each counts
+// itself in the tree's counter (after a device-scope release of its
+// results), and the one that brings the count to T + (T - 1) n_och runs the
+// tree's acceptance walk after a device-scope acquire.  No workgroup waits
+// on another.  A device-scope release writes back the XCD's L2, which costs
+// about a microsecond per workgroup: the host takes this form only for
+// launches of at most kFusedAcceptMaxBlocks workgroups (8 rows over 151936
+// tokens: 141 workgroups, 20 -> 16 us with acceptance included; 17 rows over
+// 248320 tokens: 513 workgroups, 23 -> 71 us, so there the walk keeps its
+// own launch).
+template <bool ACCEPT>
 __global__ __launch_bounds__(256) void combine_overlap_kernel(VocabArgs a) {
   const int b = blockIdx.x;
   int tree;
@@ -571,6 +588,7 @@ __global__ __launch_bounds__(256) void combine_overlap_kernel(VocabArgs a) {
     overlap_block(a, c, t, j, r.m + logf(r.s), q.m + logf(q.s));
     tree = a.row_tree[a.draft_row[t]];
   }
+  if constexpr (!ACCEPT) return;
   __shared__ int last;
   __syncthreads();   // every thread's stores issued and visible in the workgroup
   if (threadIdx.x == 0) {
@@ -862,8 +880,13 @@ void launch_drafter_partial(const VocabArgs &a, hipStream_t s) {
 void launch_row_combine(const VocabArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(row_combine_kernel, dim3(a.n), dim3(256), 0, s, a);
 }
+bool combine_overlap_accepts(const VocabArgs &a) { return a.n + a.n_och * a.n_draft <= kFusedAcceptMaxBlocks; }
+
 void launch_combine_overlap(const VocabArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(combine_overlap_kernel, dim3(a.n + a.n_och * a.n_draft), dim3(256), 0, s, a);
+  if (combine_overlap_accepts(a))
+    hipLaunchKernelGGL(combine_overlap_kernel<true>, dim3(a.n + a.n_och * a.n_draft), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(combine_overlap_kernel<false>, dim3(a.n + a.n_och * a.n_draft), dim3(256), 0, s, a);
 }
 void launch_overlap_partial(const VocabArgs &a, hipStream_t s) {
   if (a.n_draft == 0) return;

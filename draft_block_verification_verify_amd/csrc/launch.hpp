@@ -225,6 +225,10 @@ void launch_rope_drafter_bf16(const RopeArgs &r, const VocabArgs &a, hipStream_t
 // row_combine and overlap_partial in one launch (small batches: each
 // overlap workgroup recomputes its two logsumexps from the tile records)
 void launch_combine_overlap(const VocabArgs &a, hipStream_t s);
+// Largest combine_overlap launch that also runs the acceptance walks, and
+// whether this one does (otherwise launch_accept follows it).
+constexpr int kFusedAcceptMaxBlocks = 256;
+bool combine_overlap_accepts(const VocabArgs &a);
 void launch_row_combine(const VocabArgs &a, hipStream_t s);
 void launch_overlap_partial(const VocabArgs &a, hipStream_t s);
 void launch_accept(const VocabArgs &a, hipStream_t s);
