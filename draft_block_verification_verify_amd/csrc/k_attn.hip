@@ -536,7 +536,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a, int n_pair
     // same layout lo_off elements on
     const int k = h * D + c * E, R = i & 255, q = (k >> 3) & 3;
     const int64_t b = (int64_t(i >> 8) * ((a.Hq * D) >> 5) + (k >> 5)) * 8192;
-    uint16_t *dst = a.out + b + R * 32 + ((q ^ ((R >> 1) & 3)) << 3) + (k & 7);
+    uint16_t *dst = a.out + b + R * 32 + (blk_slot(q, R) << 3) + (k & 7);
 #pragma unroll
     for (int e = 0; e < E; ++e) dst[e] = hi[e];
     if (a.mode == ACT_SPLIT_BLOCKED) {

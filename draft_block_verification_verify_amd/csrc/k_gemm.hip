@@ -224,7 +224,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
       for (int v = 0; v < WV; ++v) {
         const int R = w * WV * 32 + v * 32 + r32;
         // blocked: chunk q of the 128-B step is chunk q & 3 of block q >> 2
-        af[v] = BLOCKED ? lds16(base + (q >> 2) * HB + R * 64 + (((q & 3) ^ ((R >> 1) & 3)) << 4))
+        af[v] = BLOCKED ? lds16(base + (q >> 2) * HB + R * 64 + (blk_slot(q & 3, R) << 4))
                         : lds16(base + R * 128 + ((q ^ (R & 7)) << 4));
       }
 #pragma unroll
@@ -288,8 +288,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 // 256 (N) x 256 (rows).  8 wavefronts as 2 x 4, each 128 (N) x 64 (rows) =
 // 4 x 2 fp16 32x32x16 MFMA blocks.  K steps of 32 (64 B per row) land in a
 // 4-stage LDS ring by DMA (weights 256 rows, then activations 256 rows; 16-B
-// chunk c of row R at slot c ^ ((R >> 1) & 3), so that any 8 consecutive
-// rows of one chunk fall in 8 distinct bank groups), three steps ahead of the
+// chunk c of row R at slot blk_slot(c, R), so that any 16 consecutive rows
+// of one chunk fall in 16 distinct bank groups), three steps ahead of the
 // MFMAs.  BLOCKED (the LM head): both operands are stored in that same stage
 // image, block after block, so each DMA instruction reads 1 KB of consecutive
 // bytes; row-strided 64-byte pieces stream markedly slower from HBM and L2
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int R = w * 32 + i * 16 + (lane >> 2);
-    off[i] = BLOCKED ? (w * 32 + i * 16) * 64 + lane * 16 : R * Kb + ((c4 ^ ((R >> 1) & 3)) << 4);
+    off[i] = BLOCKED ? (w * 32 + i * 16) * 64 + lane * 16 : R * Kb + (blk_slot(c4, R) << 4);
   }
   // tile i -> (weight tile, row tile); i and i+8 share the weight tile
   auto tile_of = [&](int i, int &n_tile, int &t_tile) {
@@ -452,13 +452,13 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int R = wn * 128 + v * 32 + r32;
-          af[j][v] = lds16(base + R * 64 + ((q ^ ((R >> 1) & 3)) << 4));
+          af[j][v] = lds16(base + R * 64 + (blk_slot(q, R) << 4));
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int R = wt * 64 + t * 32 + r32;
-          bf[j][t] = lds16(base + kTBN * 64 + R * 64 + ((q ^ ((R >> 1) & 3)) << 4));
-          if constexpr (LO) bl[j][t] = lds16(base + (kTBN + kTBT) * 64 + R * 64 + ((q ^ ((R >> 1) & 3)) << 4));
+          bf[j][t] = lds16(base + kTBN * 64 + R * 64 + (blk_slot(q, R) << 4));
+          if constexpr (LO) bl[j][t] = lds16(base + (kTBN + kTBT) * 64 + R * 64 + (blk_slot(q, R) << 4));
         }
       }
       if constexpr (PP) {
@@ -681,12 +681,12 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
       i32x8 af[4], bf[2];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int R = wn * 128 + v * 32 + r32, sw = (R >> 1) & 3;
+        const int R = wn * 128 + v * 32 + r32, sw = blk_slot(0, R);
         af[v] = cat8(lds16(base + R * 64 + (((2 * kg) ^ sw) << 4)), lds16(base + R * 64 + (((2 * kg + 1) ^ sw) << 4)));
       }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int R = wt * 64 + t * 32 + r32, sw = (R >> 1) & 3;
+        const int R = wt * 64 + t * 32 + r32, sw = blk_slot(0, R);
         bf[t] = cat8(lds16(base + kTBN * 64 + R * 64 + (((2 * kg) ^ sw) << 4)),
                      lds16(base + kTBN * 64 + R * 64 + (((2 * kg + 1) ^ sw) << 4)));
       }
@@ -973,7 +973,7 @@ __device__ __forceinline__ uint4 e4m3_pack16(const float (&v)[16]) {
 // byte offset of (row, 16-value chunk c16 of the row) in the e4m3 blocked layout
 __device__ __forceinline__ int64_t fp8_blocked_off(int64_t row, int c16, int K) {
   const int R = int(row & 255), kb = c16 >> 2, q = c16 & 3;
-  return ((row >> 8) * (K >> 6) + kb) * 16384 + R * 64 + ((q ^ ((R >> 1) & 3)) << 4);
+  return ((row >> 8) * (K >> 6) + kb) * 16384 + R * 64 + (blk_slot(q, R) << 4);
 }
 
 // Counts weights that are not finite into *bad (such a row cannot be
@@ -1088,7 +1088,7 @@ __global__ __launch_bounds__(1024) void norm_kernel(const float *part, int split
       split_h(y, hi, lo);
       const int R = row & 255, q = (c >> 3) & 3;
       const int64_t b = (int64_t(row >> 8) * (hidden >> 5) + (c >> 5)) * 8192;
-      static_cast<uint16_t *>(out)[b + R * 32 + ((q ^ ((R >> 1) & 3)) << 3) + (c & 7)] = hi;
+      static_cast<uint16_t *>(out)[b + R * 32 + (blk_slot(q, R) << 3) + (c & 7)] = hi;
       static_cast<uint16_t *>(out)[lo_off + idx] = lo;
     } else {
       static_cast<float *>(out)[idx] = y;
@@ -1135,7 +1135,7 @@ __global__ __launch_bounds__(256) void bf16_to_f16_blocked_kernel(const uint16_t
     const int64_t blk = i >> 10;
     const int R = int(i >> 2) & 255, p = int(i & 3);
     const int64_t row = (blk / kbs) * 256 + R;
-    const int kb = int(blk % kbs), q = p ^ ((R >> 1) & 3);
+    const int kb = int(blk % kbs), q = blk_slot(p, R);
     uint4 v = {0u, 0u, 0u, 0u};
     if (row < rows) {
       const uint4 b = *reinterpret_cast<const uint4 *>(src + row * K + kb * 32 + q * 8);

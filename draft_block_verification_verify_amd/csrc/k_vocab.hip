@@ -232,7 +232,7 @@ __device__ __forceinline__ float tile_logit(const VocabArgs &a, int row, int u) 
 // blocked fp16 layout of the tiled LM head
 __device__ __forceinline__ int64_t blocked_chunk(int64_t r, int k, int K) {
   const int R = int(r & 255), q = (k >> 3) & 3;
-  return ((r >> 8) * (K >> 5) + (k >> 5)) * 8192 + R * 32 + ((q ^ ((R >> 1) & 3)) << 3);
+  return ((r >> 8) * (K >> 5) + (k >> 5)) * 8192 + R * 32 + (blk_slot(q, R) << 3);
 }
 
 __device__ __forceinline__ float dot8h(uint4 x, uint4 y) {

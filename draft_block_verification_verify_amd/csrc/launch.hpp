@@ -25,16 +25,22 @@ enum ActMode : int {
 // activations is stored as e4m3 codes of value / 2^e, 2^e the smallest
 // power of two with max |row| <= 448 * 2^e, in a blocked layout like the fp16
 // one with K steps of 64 (64 bytes per row): blocks [rows / 256][K / 64] of
-// 256 x 64 bytes, 16-byte chunk q of row R at byte R * 64 + ((q ^ ((R >> 1) &
-// 3)) << 4).  The scales 2^e are kept per row as floats.
+// 256 x 64 bytes, 16-byte chunk q of row R at byte R * 64 + (blk_slot(q, R)
+// << 4).  The scales 2^e are kept per row as floats.
 
 // Blocked fp16 layout of a [M, K] operand of the tiled LM-head launch: rows
 // padded to a multiple of 256; blocks [M / 256][K / 32], each 256 rows x 64
 // bytes (one K step) = 16 KB.  Inside a block, row R's 16-byte chunk q
-// (elements 8q .. 8q+7 of the K step) sits at byte R * 64 + ((q ^ ((R >> 1)
-// & 3)) << 4): the image of one ring stage in LDS, so that every DMA
-// instruction reads 1 KB of consecutive bytes.
+// (elements 8q .. 8q+7 of the K step) sits at byte R * 64 + (blk_slot(q, R)
+// << 4): the image of one ring stage in LDS, so that every DMA instruction
+// reads 1 KB of consecutive bytes.
 constexpr int64_t blocked_elems(int64_t rows, int64_t K) { return (rows + 255) / 256 * 256 * K; }
+
+// Slot of 16-byte chunk q (0..3) of row R in a 64-byte row of a blocked
+// stage.  Sixteen consecutive rows put one chunk in sixteen distinct
+// 16-byte bank groups of a 256-byte LDS line, so a 16-byte fragment read of
+// 32 consecutive rows (one MFMA operand) runs without bank conflicts.
+__host__ __device__ constexpr int blk_slot(int q, int R) { return q ^ ((R >> 2) & 3); }
 
 struct AttnArgs {
   const uint16_t *kv_k, *kv_v;     // [T, Hkv, D] bf16, keys already rotated
