@@ -70,6 +70,9 @@ SYMBOLS = {
                                        C.POINTER(C.c_double)]),
     "spec_verify_run_static": (C.c_int, [C.POINTER(SvConfig), C.c_void_p, C.c_void_p, C.POINTER(SvInputs),
                                          C.POINTER(SvOutputs), C.c_void_p]),
+    "spec_verify_weight_bytes": (C.c_int, [C.POINTER(SvConfig), C.POINTER(C.c_size_t)]),
+    "spec_verify_prepare_weights": (C.c_int, [C.POINTER(SvConfig), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "spec_verify_create_prepared": (C.c_int, [C.POINTER(SvConfig), C.c_void_p, C.POINTER(C.c_void_p)]),
     "spec_verify_destroy": (C.c_int, [C.c_void_p]),
     "spec_verify_last_error": (C.c_char_p, []),
     "spec_verify_profile": (C.c_int, [C.c_void_p, C.c_int32]),
@@ -107,6 +110,24 @@ def _check(st: int):
 def spec_verify_create(cfg: SvConfig, w_o_ptr: int, w_lm_ptr: int) -> C.c_void_p:
     h = C.c_void_p()
     _check(lib().spec_verify_create(C.byref(cfg), C.c_void_p(w_o_ptr), C.c_void_p(w_lm_ptr), C.byref(h)))
+    return h
+
+
+def spec_verify_weight_bytes(cfg: SvConfig) -> int:
+    n = C.c_size_t(0)
+    _check(lib().spec_verify_weight_bytes(C.byref(cfg), C.byref(n)))
+    return int(n.value)
+
+
+def spec_verify_prepare_weights(cfg: SvConfig, w_o_ptr: int, w_lm_ptr: int, dst_ptr: int,
+                                stream: int | None = None) -> None:
+    _check(lib().spec_verify_prepare_weights(C.byref(cfg), C.c_void_p(w_o_ptr), C.c_void_p(w_lm_ptr),
+                                             C.c_void_p(dst_ptr), C.c_void_p(stream or 0)))
+
+
+def spec_verify_create_prepared(cfg: SvConfig, prepared_ptr: int) -> C.c_void_p:
+    h = C.c_void_p()
+    _check(lib().spec_verify_create_prepared(C.byref(cfg), C.c_void_p(prepared_ptr), C.byref(h)))
     return h
 
 
@@ -185,11 +206,15 @@ class Verifier:
 
     `cfg` is an SvConfig; `w_o`, `w_lm` are contiguous device tensors."""
 
-    def __init__(self, cfg: SvConfig, w_o, w_lm):
+    def __init__(self, cfg: SvConfig, w_o, w_lm, prepared=None):
         import torch  # noqa: F401  (device memory)
         self.cfg = cfg
-        self._w = (w_o, w_lm)
-        self.h = spec_verify_create(cfg, _ptr(w_o), _ptr(w_lm))
+        self._w = (w_o, w_lm, prepared)
+        if prepared is not None:
+            # weights converted by spec_verify_prepare_weights, borrowed
+            self.h = spec_verify_create_prepared(cfg, _ptr(prepared))
+        else:
+            self.h = spec_verify_create(cfg, _ptr(w_o), _ptr(w_lm))
 
     def close(self):
         if self.h is not None:

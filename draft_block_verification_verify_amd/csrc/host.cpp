@@ -394,11 +394,52 @@ extern "C" {
 
 const char *spec_verify_last_error(void) { return g_err.c_str(); }
 
-sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *w_lm, sv_handle **out) {
+}  // extern "C"
+
+namespace {
+
+// Byte offsets of the parts of a prepared-weights buffer (spec_verify_weight_bytes).
+struct PreparedLayout {
+  size_t o16, o_blk, lm_blk, bad, total;
+};
+
+PreparedLayout prepared_layout(const sv::Dims &dm) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  const int64_t H = dm.hidden, K = int64_t(dm.Hq) * dm.d, V = dm.vocab;
+  PreparedLayout L{};
+  size_t o = 0;
+  L.o16 = o;
+  o = al(o + size_t(H * K * 2));
+  L.o_blk = o;
+  o = al(o + size_t(sv::blocked_elems(H, K) * 2));
+  L.lm_blk = o;
+  o = al(o + size_t(sv::blocked_elems(V, H) * 2));
+  L.bad = o;
+  L.total = o + 256;
+  return L;
+}
+
+// The checks every prepared-weights call shares: dimensions, and a bf16
+// model whose weights the library converts to fp16 (not FP8).
+sv_status check_prepared_cfg(const sv_config *cfg, sv::Dims *dm) {
+  if (!cfg) return fail(SV_ERR_INVALID_ARG, "cfg must be non-null");
+  *dm = sv::Dims{cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, cfg->hidden,        cfg->vocab,
+                 cfg->dtype,     cfg->max_rows,   cfg->max_roots, cfg->max_tree_rows, cfg->max_pos,
+                 cfg->weight_format};
+  std::string err;
+  const int pc = sv::check_dims(*dm, &err);
+  if (pc != sv::P_OK) return fail(sv_status(pc), err);
+  if (dm->dtype != SV_BF16 || dm->weight_format != SV_WEIGHTS_NATIVE)
+    return fail(SV_ERR_UNSUPPORTED, "prepared weights are for bf16 models with the native (fp16) weight format");
+  return SV_OK;
+}
+
+sv_status create_impl(const sv_config *cfg, const void *w_o, const void *w_lm, const unsigned char *prepared,
+                      sv_handle **out) {
   g_err.clear();
   if (!cfg || !out) return fail(SV_ERR_INVALID_ARG, "cfg and out must be non-null");
   *out = nullptr;
-  if (!w_o || !w_lm) return fail(SV_ERR_INVALID_ARG, "w_o and w_lm must be non-null device pointers");
+  if (!prepared && (!w_o || !w_lm)) return fail(SV_ERR_INVALID_ARG, "w_o and w_lm must be non-null device pointers");
   sv::Dims dm{cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, cfg->hidden, cfg->vocab, cfg->dtype,
               cfg->max_rows,  cfg->max_roots,  cfg->max_tree_rows, cfg->max_pos, cfg->weight_format};
   std::string err;
@@ -473,7 +514,24 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
   A(&h->opart, size_t(R * h->n_och * 4));
   A(&h->rej_child, size_t(dm.max_roots) * 4);
   A(&h->rpart, size_t(dm.max_roots) * h->n_och * 4);
-  if (dm.dtype == SV_BF16) {
+  if (dm.dtype == SV_BF16 && prepared) {
+    // borrowed fp16 weights (spec_verify_prepare_weights): nothing to copy
+    const PreparedLayout L = prepared_layout(dm);
+    h->w_o = prepared + L.o16;
+    h->w_o_blk = reinterpret_cast<const uint16_t *>(prepared + L.o_blk);
+    h->w_lm = prepared + L.lm_blk;
+    if (st == SV_OK) {
+      // padding rows of the blocked activations are read by the LM head:
+      // start them at zero
+      e = hipMemsetAsync(h->hn, 0, std::max<size_t>(size_t(R * H * 4), size_t((sv::blocked_elems(R, H) + R * H) * 2)),
+                         nullptr);
+      if (e == hipSuccess) e = hipDeviceSynchronize();
+      if (e != hipSuccess) {
+        release(h);
+        return hip_fail("hipMemsetAsync", e);
+      }
+    }
+  } else if (dm.dtype == SV_BF16) {
     // the projections run on fp16 MFMA: keep fp16 copies of the weights
     // (W_o row-major, W_lm in the blocked layout)
     uint16_t *wo16 = nullptr, *wlm16 = nullptr, *wo_blk = nullptr;
@@ -549,6 +607,70 @@ sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *
   }
   *out = h;
   return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sv_status spec_verify_create(const sv_config *cfg, const void *w_o, const void *w_lm, sv_handle **out) {
+  return create_impl(cfg, w_o, w_lm, nullptr, out);
+}
+
+sv_status spec_verify_weight_bytes(const sv_config *cfg, size_t *bytes) {
+  g_err.clear();
+  if (!bytes) return fail(SV_ERR_INVALID_ARG, "bytes must be non-null");
+  *bytes = 0;
+  sv::Dims dm{};
+  const sv_status st = check_prepared_cfg(cfg, &dm);
+  if (st != SV_OK) return st;
+  *bytes = prepared_layout(dm).total;
+  return SV_OK;
+}
+
+sv_status spec_verify_prepare_weights(const sv_config *cfg, const void *w_o, const void *w_lm, void *dst,
+                                      void *stream_v) {
+  g_err.clear();
+  sv::Dims dm{};
+  const sv_status st = check_prepared_cfg(cfg, &dm);
+  if (st != SV_OK) return st;
+  if (!w_o || !w_lm || !dst) return fail(SV_ERR_INVALID_ARG, "w_o, w_lm and dst must be non-null device pointers");
+  if (reinterpret_cast<uintptr_t>(dst) % 256 != 0) return fail(SV_ERR_INVALID_ARG, "dst must be 256-byte aligned");
+  const PreparedLayout L = prepared_layout(dm);
+  const hipStream_t stream = static_cast<hipStream_t>(stream_v);
+  unsigned char *d = static_cast<unsigned char *>(dst);
+  int32_t *bad = reinterpret_cast<int32_t *>(d + L.bad);
+  const int64_t H = dm.hidden, K = int64_t(dm.Hq) * dm.d;
+  hipError_t e = hipMemsetAsync(bad, 0, 4, stream);
+  if (e != hipSuccess) return hip_fail("hipMemsetAsync", e);
+  sv::launch_bf16_to_f16(static_cast<const uint16_t *>(w_o), reinterpret_cast<uint16_t *>(d + L.o16), H * K, bad,
+                         stream);
+  sv::launch_bf16_to_f16_blocked(static_cast<const uint16_t *>(w_o), reinterpret_cast<uint16_t *>(d + L.o_blk),
+                                 int(H), int(K), bad, stream);
+  sv::launch_bf16_to_f16_blocked(static_cast<const uint16_t *>(w_lm), reinterpret_cast<uint16_t *>(d + L.lm_blk),
+                                 int(dm.vocab), int(H), bad, stream);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail("weight conversion", e);
+  int32_t n_bad = 0;
+  e = hipMemcpyAsync(&n_bad, bad, 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail("weight conversion", e);
+  if (n_bad != 0)
+    return fail(SV_ERR_UNSUPPORTED,
+                std::to_string(n_bad) + " weight values exceed the fp16 range (|w| > 65504) or are not finite");
+  return SV_OK;
+}
+
+sv_status spec_verify_create_prepared(const sv_config *cfg, const void *prepared, sv_handle **out) {
+  g_err.clear();
+  if (out) *out = nullptr;
+  sv::Dims dm{};
+  const sv_status st = check_prepared_cfg(cfg, &dm);
+  if (st != SV_OK) return st;
+  if (!prepared) return fail(SV_ERR_INVALID_ARG, "prepared must be a non-null device pointer");
+  if (reinterpret_cast<uintptr_t>(prepared) % 256 != 0)
+    return fail(SV_ERR_INVALID_ARG, "prepared must be 256-byte aligned");
+  return create_impl(cfg, nullptr, nullptr, static_cast<const unsigned char *>(prepared), out);
 }
 
 sv_status spec_verify_destroy(sv_handle *h) {

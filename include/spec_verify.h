@@ -256,6 +256,36 @@ sv_status spec_verify_schedule(int32_t n_req, const int32_t *n_cand, const int32
 sv_status spec_verify_run_static(const sv_config *cfg, const void *w_o, const void *w_lm, const sv_inputs *in,
                                  const sv_outputs *out, void *stream);
 
+/* Prepared weights, for callers that convert a bf16 model's weights once and
+ * share them between handles (a bf16 handle made by spec_verify_create keeps
+ * its own fp16 copies: about 2.5 GB for a 248320 x 5120 LM head).  The three
+ * calls below are for cfg->dtype SV_BF16 with weight_format
+ * SV_WEIGHTS_NATIVE; any other cfg fails with SV_ERR_UNSUPPORTED.
+ *
+ * spec_verify_weight_bytes: HOST only, no GPU work.  *bytes receives the size
+ * of one device buffer that holds W_o as fp16 row-major, W_o and W_lm in
+ * the blocked fp16 layout of the tiled launches, and a 256-byte check word.
+ * The size depends on hidden, n_q_heads * head_dim and vocab only, not on the
+ * capacities, so one buffer serves handles of any capacities.
+ *
+ * spec_verify_prepare_weights: converts the bf16 weights w_o and w_lm
+ * (DEVICE, as for spec_verify_create) into dst (DEVICE, caller-owned,
+ * spec_verify_weight_bytes bytes, 256-byte aligned) on `stream`, then WAITS
+ * for the conversion.  The conversion rounds to nearest even, exactly as
+ * spec_verify_create's does.  Fails with SV_ERR_UNSUPPORTED when a weight is
+ * not finite or exceeds 65504 in magnitude; dst is then unusable.
+ *
+ * spec_verify_create_prepared: as spec_verify_create, but the handle borrows
+ * `prepared` (a buffer filled by spec_verify_prepare_weights for a cfg with
+ * the same hidden, n_q_heads, head_dim and vocab) instead of copying the
+ * weights.  The caller keeps it alive and unchanged until the handle is
+ * destroyed; the library never frees it.  Results are identical to those of
+ * a handle made by spec_verify_create from the same bf16 weights. */
+sv_status spec_verify_weight_bytes(const sv_config *cfg, size_t *bytes);
+sv_status spec_verify_prepare_weights(const sv_config *cfg, const void *w_o, const void *w_lm, void *dst,
+                                      void *stream);
+sv_status spec_verify_create_prepared(const sv_config *cfg, const void *prepared, sv_handle **out);
+
 /* Wait for the handle's last enqueued step, then free everything it owns.
  * NULL is accepted. */
 sv_status spec_verify_destroy(sv_handle *h);

@@ -339,3 +339,37 @@ def test_run_static_rejects_before_device(libsv):
     # misaligned weights
     assert f(C.byref(good_cfg()), C.c_void_p(20), C.c_void_p(16), C.byref(inp), C.byref(out),
              None) == B.SV_ERR_INVALID_ARG
+
+
+def test_prepared_weight_bytes_and_refusals(libsv):
+    # host-only: the prepared-weights buffer's size is fixed by hidden,
+    # n_q_heads * head_dim and vocab (three 256-byte aligned parts and a
+    # 256-byte check word), not by the capacities; other dtypes and the FP8
+    # format are refused, and every call checks its arguments before any
+    # device work
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    def blocked(rows, k):
+        return (rows + 255) // 256 * 256 * k
+
+    cfg = good_cfg(dtype=B.SV_BF16)
+    h, k, v = cfg.hidden, cfg.n_q_heads * cfg.head_dim, cfg.vocab
+    want = al(h * k * 2) + al(blocked(h, k) * 2) + al(blocked(v, h) * 2) + 256
+    assert B.spec_verify_weight_bytes(cfg) == want
+    assert B.spec_verify_weight_bytes(good_cfg(dtype=B.SV_BF16, max_rows=7, max_roots=1)) == want
+    n = C.c_size_t(7)
+    assert libsv.spec_verify_weight_bytes(C.byref(good_cfg()), C.byref(n)) == B.SV_ERR_UNSUPPORTED and n.value == 0
+    assert libsv.spec_verify_weight_bytes(C.byref(good_cfg(dtype=B.SV_BF16, weight_format=B.SV_WEIGHTS_FP8)),
+                                          C.byref(n)) == B.SV_ERR_UNSUPPORTED
+    assert libsv.spec_verify_weight_bytes(None, C.byref(n)) == B.SV_ERR_INVALID_ARG
+    assert libsv.spec_verify_weight_bytes(C.byref(cfg), None) == B.SV_ERR_INVALID_ARG
+    prep = libsv.spec_verify_prepare_weights
+    assert prep(C.byref(cfg), None, C.c_void_p(256), C.c_void_p(256), None) == B.SV_ERR_INVALID_ARG
+    assert prep(C.byref(cfg), C.c_void_p(256), C.c_void_p(256), C.c_void_p(272), None) == B.SV_ERR_INVALID_ARG
+    assert prep(C.byref(good_cfg()), C.c_void_p(256), C.c_void_p(256), C.c_void_p(256), None) == B.SV_ERR_UNSUPPORTED
+    hp = C.c_void_p(1)
+    create = libsv.spec_verify_create_prepared
+    assert create(C.byref(cfg), None, C.byref(hp)) == B.SV_ERR_INVALID_ARG and hp.value is None
+    assert create(C.byref(cfg), C.c_void_p(272), C.byref(hp)) == B.SV_ERR_INVALID_ARG
+    assert create(C.byref(good_cfg()), C.c_void_p(256), C.byref(hp)) == B.SV_ERR_UNSUPPORTED
