@@ -582,9 +582,15 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
   constexpr bool STATS = true;
   constexpr int PER = 4;     // DMA instructions per wave per stage (2 weight + 2 activation)
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // w wave-uniform (a scalar value), so that wave-indexed choices are scalar branches
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, kg = lane >> 5;
   const int wn = w & 1, wt = w >> 1;
+  // the ping-pong K loop for full tiles only: with most waves idle on
+  // padding rows (SPARSE), its second barrier per step costs more than it
+  // overlaps (8 rows: 164 -> 332 us)
+  constexpr bool PP = !SPARSE;
+  const bool lag = PP && w >= 4;   // the lagging group of the ping-pong loop
   const int n_ttiles = (g.rows + kTBT - 1) / kTBT;
   const int n_ntiles = (g.N + kTBN - 1) / kTBN;
   const int n_tiles_all = ((n_ntiles + 7) / 8) * 8 * n_ttiles;
@@ -666,8 +672,19 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[v][t][j] = 0.f;
 
+    // the ping-pong K loop of the fp16 LM head (gemm_tiled_kernel, PP):
+    // waves 4-7 one barrier behind waves 0-3, the same barrier sequence
+    if (lag) {
+      const int younger0 = min(kTST - 2, nk - 1);
+      if (younger0 >= 2)
+        wait_and_barrier<2 * PER>();
+      else if (younger0 == 1)
+        wait_and_barrier<PER>();
+      else
+        wait_and_barrier<0>();
+    }
     for (int s = 0; s < nk; ++s) {
-      const int younger = min(kTST - 2, nk - 1 - s);
+      const int younger = lag ? max(0, min(kTST - 3, nk - 2 - s)) : min(kTST - 2, nk - 1 - s);
       if (younger >= 2)
         wait_and_barrier<2 * PER>();
       else if (younger == 1)
@@ -676,20 +693,27 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
         wait_and_barrier<0>();
       if (s + kTST - 1 < nk) issue(cur, s + kTST - 1);
       const uint8_t *base = smem + (s % kTST) * kTSST;
-      if (!live_t0) continue;   // this wave's 64 rows are all padding: DMA and barriers only
       // 32 bytes of the lane's row per operand: chunks 2 kg and 2 kg + 1
       i32x8 af[4], bf[2];
+      if (live_t0) {   // else: this wave's 64 rows are all padding (copies and barriers only)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int R = wn * 128 + v * 32 + r32, sw = blk_slot(0, R);
-        af[v] = cat8(lds16(base + R * 64 + (((2 * kg) ^ sw) << 4)), lds16(base + R * 64 + (((2 * kg + 1) ^ sw) << 4)));
-      }
+        for (int v = 0; v < 4; ++v) {
+          const int R = wn * 128 + v * 32 + r32, sw = blk_slot(0, R);
+          af[v] = cat8(lds16(base + R * 64 + (((2 * kg) ^ sw) << 4)), lds16(base + R * 64 + (((2 * kg + 1) ^ sw) << 4)));
+        }
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int R = wt * 64 + t * 32 + r32, sw = blk_slot(0, R);
-        bf[t] = cat8(lds16(base + kTBN * 64 + R * 64 + (((2 * kg) ^ sw) << 4)),
-                     lds16(base + kTBN * 64 + R * 64 + (((2 * kg + 1) ^ sw) << 4)));
+        for (int t = 0; t < 2; ++t) {
+          const int R = wt * 64 + t * 32 + r32, sw = blk_slot(0, R);
+          bf[t] = cat8(lds16(base + kTBN * 64 + R * 64 + (((2 * kg) ^ sw) << 4)),
+                       lds16(base + kTBN * 64 + R * 64 + (((2 * kg + 1) ^ sw) << 4)));
+        }
       }
+      if constexpr (PP) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (!live_t0) continue;
       if (live_t1) {
 #pragma unroll
         for (int v = 0; v < 4; ++v)
@@ -700,6 +724,8 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
         for (int v = 0; v < 4; ++v) acc[v][0] = mfma32_fp8(af[v], bf[0], acc[v][0]);
       }
     }
+
+    if (PP && !lag) asm volatile("s_barrier" ::: "memory");   // the lagging group's first barrier
 
     // epilogue of this tile (vector-memory waits count stores too, so the
     // next tile's loads are issued only after the stores)
