@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
   constexpr int AI = 2 * TB * 32 / 8 / 4;    // activation DMA instructions per wave per stage
   constexpr int PER = WI + AI;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, kg = lane >> 5;
   const int n0 = blockIdx.x * NR;
   const int ks = blockIdx.y * g.k_split;
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
   constexpr int ST = LO ? kTSTLo : kTST;        // ring stages
   constexpr int SST = LO ? kTSSTLo : kTSST;     // bytes per stage
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, kg = lane >> 5;
   const int wn = w & 1, wt = w >> 1;
   // wave-uniform (a scalar value), so that the barriers it selects sit
