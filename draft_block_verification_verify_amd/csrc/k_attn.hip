@@ -123,7 +123,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_mfma_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // [stage][K tile | V tile]
 
   const auto &run = as_const(a.runs)[blockIdx.x];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, kg = lane >> 4;
   const int G = a.G, Hkv = a.Hkv, Hq = a.Hq;
   const int nt = run.tiles;                                  // the run's tiles, item after item
@@ -433,7 +433,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a, int n_pair
   typedef float fvec __attribute__((ext_vector_type(E)));
   __shared__ float wl[4][kMaxSplits];
   __shared__ fvec red[WPP > 1 ? WPP : 1][64];
-  const int w = threadIdx.x >> 6, c = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), c = threadIdx.x & 63;
   const int pair = WPP > 1 ? int(blockIdx.x) : int(blockIdx.x) * 4 + w;
   if (WPP == 1 && pair >= n_pairs) return;    // no workgroup-wide synchronisation with one wave per pair
   const int i = pair / a.Hq, h = pair % a.Hq;
