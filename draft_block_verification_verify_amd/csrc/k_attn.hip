@@ -483,7 +483,6 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a, int n_pair
   if constexpr (WPP > 1) {
     red[w][c] = val;
     __syncthreads();
-    if (w != 0) return;
     val = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
   }
   // The keys rotated in this step (the row's ancestors and itself) reached
@@ -500,9 +499,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a, int n_pair
     for (int e = 0; e < E; ++e) qv[e] = bf2f(a.q_rot[qoff + e]) + bf2f(a.q_rot[a.q_lo_off + qoff + e]);
     const int ts = as_const(a.tree_start)[as_const(a.row_tree_real)[i]];
     uint64_t bits = a.row_anc[i];
-    while (bits) {
+    // WPP > 1: wavefront w takes the keys w, w + WPP, ... (in bit order) and
+    // its sums are added in wavefront order below; the LDS records of the
+    // merge above are no longer read, so they take these sums
+    fvec dv = fvec(0.f);
+    float dl = 0.f;
+    for (int k = 0; bits; ++k) {
       const int j = __builtin_ctzll(bits);
       bits &= bits - 1;
+      if (WPP > 1 && k % WPP != w) continue;
       const int64_t koff = (int64_t(ts + j) * a.Hkv + g) * D + c * E;
       float st = 0.f, sx = 0.f;
 #pragma unroll
@@ -514,10 +519,24 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a, int n_pair
       st = wave_sum(st);
       sx = wave_sum(sx);
       const float dp = exp2f(sx * a.scale_log2 - M) - exp2f(st * a.scale_log2 - M);
-      Lx += dp;
+      dl += dp;
 #pragma unroll
-      for (int e = 0; e < E; ++e) val[e] = fmaf(dp, bf2f(a.v_rows[koff + e]), val[e]);
+      for (int e = 0; e < E; ++e) dv[e] = fmaf(dp, bf2f(a.v_rows[koff + e]), dv[e]);
     }
+    if constexpr (WPP > 1) {
+      __shared__ float dls[WPP];
+      __syncthreads();   // every wavefront has read the merge records
+      red[w][c] = dv;
+      if (c == 0) dls[w] = dl;
+      __syncthreads();
+      if (w != 0) return;
+      dv = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
+      dl = (dls[0] + dls[1]) + (dls[2] + dls[3]);
+    }
+    Lx += dl;
+    val += dv;
+  } else if constexpr (WPP > 1) {
+    if (w != 0) return;
   }
   val = val / Lx;
 
