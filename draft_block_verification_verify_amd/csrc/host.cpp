@@ -27,7 +27,7 @@ sv_status fail(sv_status st, std::string msg) {
 }
 
 constexpr int kRing = 4;          // pinned metadata staging slots
-constexpr int kDChunk = 8192;     // vocabulary chunk of the drafter-stats pass
+constexpr int kDChunk = 2048;     // vocabulary chunk of the drafter-stats pass (one record per wavefront)
 constexpr int kOChunk = 8192;     // vocabulary chunk of the overlap pass and of the T = 1 draw
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

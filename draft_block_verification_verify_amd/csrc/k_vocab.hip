@@ -88,23 +88,24 @@ __device__ __forceinline__ float load1(const void *base, int bf16, int64_t idx) 
 
 // ----------------------------------------------------------------------------
 
-constexpr int kDrafterChunk = 8192;   // the host's drafter-stats chunk (vocabulary values per workgroup)
+constexpr int kDrafterChunk = 2048;   // the host's drafter-stats chunk: vocabulary values per wavefront record
 
-// (max, sum exp) of chunk c of drafter row t, by one 256-thread workgroup
-__device__ __forceinline__ void drafter_partial_block(const VocabArgs &a, int c, int t) {
-  const int tid = threadIdx.x;
+// (max, sum exp) of chunk c of drafter row t, by one wavefront: its own
+// record, so that no workgroup-wide reduction or barrier sits between the
+// loads and the store (a workgroup's four wavefronts take four chunks)
+__device__ __forceinline__ void drafter_partial_wave(const VocabArgs &a, int c, int t) {
+  const int lane = threadIdx.x & 63;
   const int lo = c * a.dchunk, hi = min(a.V, lo + a.dchunk);
   const int64_t row = int64_t(t) * a.V;
-  const bool vec = (a.V % 8) == 0;
   float m = -INFINITY, s = 0.f;
-  if (vec && a.dchunk == kDrafterChunk) {
-    // the thread's kDrafterChunk / 2048 groups of 8, all loaded before use
-    // (one pass over HBM); values past the vocabulary read as -inf
-    constexpr int NG = kDrafterChunk / 2048;
+  if ((a.V % 8) == 0 && a.dchunk == kDrafterChunk) {
+    // the lane's four groups of 8, all loaded before use (one pass over HBM);
+    // values past the vocabulary read as -inf
+    constexpr int NG = kDrafterChunk / 512;
     float x[NG][8];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const int u = lo + tid * 8 + g * 2048;
+      const int u = lo + lane * 8 + g * 512;
       if (u < hi) {
         load8(a.drafter, a.drafter_bf16, row + u, x[g]);
       } else {
@@ -116,31 +117,27 @@ __device__ __forceinline__ void drafter_partial_block(const VocabArgs &a, int c,
     for (int g = 0; g < NG; ++g)
 #pragma unroll
       for (int e = 0; e < 8; ++e) m = fmaxf(m, x[g][e]);
+    m = wave_max(m);
+    if (m != -INFINITY) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
+      for (int g = 0; g < NG; ++g)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += __expf(x[g][e] - m);   // exp(-inf) = 0
-  } else if (vec) {
-    // pass 1: max; pass 2: sum exp (the chunk is re-read from L2)
-    for (int u = lo + tid * 8; u < hi; u += 256 * 8) {
-      float x[8];
-      load8(a.drafter, a.drafter_bf16, row + u, x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) m = fmaxf(m, x[e]);
-    }
-    for (int u = lo + tid * 8; u < hi; u += 256 * 8) {
-      float x[8];
-      load8(a.drafter, a.drafter_bf16, row + u, x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s += __expf(x[e] - m);
+        for (int e = 0; e < 8; ++e) s += __expf(x[g][e] - m);   // exp(-inf) = 0
     }
   } else {
-    for (int u = lo + tid; u < hi; u += 256) m = fmaxf(m, load1(a.drafter, a.drafter_bf16, row + u));
-    for (int u = lo + tid; u < hi; u += 256) s += __expf(load1(a.drafter, a.drafter_bf16, row + u) - m);
+    for (int u = lo + lane; u < hi; u += 64) m = fmaxf(m, load1(a.drafter, a.drafter_bf16, row + u));
+    m = wave_max(m);
+    if (m != -INFINITY)
+      for (int u = lo + lane; u < hi; u += 64) s += __expf(load1(a.drafter, a.drafter_bf16, row + u) - m);
   }
-  if (m == -INFINITY) s = 0.f;
-  const MaxSum r = ms_block256(MaxSum{m, s});
-  if (tid == 0) a.dpart[int64_t(t) * a.n_dch + c] = make_float2(r.m, r.s);
+  s = wave_sum(s);
+  if (lane == 0) a.dpart[int64_t(t) * a.n_dch + c] = make_float2(m, s);
+}
+
+// chunks 4 cg .. 4 cg + 3 of drafter row t, one per wavefront
+__device__ __forceinline__ void drafter_partial_block(const VocabArgs &a, int cg, int t) {
+  const int c = cg * 4 + int(threadIdx.x >> 6);
+  if (c < a.n_dch) drafter_partial_wave(a, c, t);
 }
 
 __global__ __launch_bounds__(256) void drafter_partial_kernel(VocabArgs a) {
@@ -158,8 +155,8 @@ __global__ __launch_bounds__(256) void rope_drafter_kernel(RopeArgs r, VocabArgs
     rope_rows_block<uint16_t>(r.q, r.k, r.q_out, r.k_out, r.row_pos, r.Hq, r.Hkv, r.D, r.base, r.q_lo_off, r.k_lo_off,
                               b / r.ry, b % r.ry, r.ry);
   } else {
-    const int d = b - nr;
-    drafter_partial_block(a, d % a.n_dch, d / a.n_dch);
+    const int d = b - nr, ncg = (a.n_dch + 3) / 4;
+    drafter_partial_block(a, d % ncg, d / ncg);
   }
 }
 
@@ -869,13 +866,13 @@ void launch_sample(const VocabArgs &a, const SampleArgs &sa, hipStream_t s) {
 }
 
 void launch_rope_drafter_bf16(const RopeArgs &r, const VocabArgs &a, hipStream_t s) {
-  const int blocks = r.n * r.ry + a.n_dch * a.n_draft;
+  const int blocks = r.n * r.ry + (a.n_dch + 3) / 4 * a.n_draft;
   hipLaunchKernelGGL(rope_drafter_kernel, dim3(blocks), dim3(256), 0, s, r, a);
 }
 
 void launch_drafter_partial(const VocabArgs &a, hipStream_t s) {
   if (a.n_draft == 0) return;
-  hipLaunchKernelGGL(drafter_partial_kernel, dim3(a.n_dch, a.n_draft), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(drafter_partial_kernel, dim3((a.n_dch + 3) / 4, a.n_draft), dim3(256), 0, s, a);
 }
 void launch_row_combine(const VocabArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(row_combine_kernel, dim3(a.n), dim3(256), 0, s, a);
