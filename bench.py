@@ -35,7 +35,7 @@ SETTLE_S = 0.5
 FLUSH_BYTES = 512 << 20        # written before each timed step (2x the 256 MB last-level cache)
 COUNTERS = os.path.join(ROOT, "profiles", "lm_head_counters.json")
 GEMM_SRC = [os.path.join(ROOT, "draft_block_verification_verify_amd", "csrc", f)
-            for f in ("k_gemm.hip", "k_dma.hpp", "k_common.hpp")]
+            for f in ("k_gemm.hip", "k_dma.hpp", "k_common.hpp", "launch.hpp")]   # launch.hpp: the blocked layout
 
 
 def log(*a):

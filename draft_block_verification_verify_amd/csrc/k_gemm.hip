@@ -528,7 +528,43 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
           const int row = wt * 64 + t * 32 + r32;
           m[t] = fmaxf(red[0][row].m, red[1][row].m);
         }
-        store_tile_p16<4, 2>(g, acc, nb, tb, m, lane);
+        // The tile's fp16 probabilities go through the idle ring (256 rows x
+        // 512 B = its 128 KB): each lane writes its 8-byte pieces, 16-byte
+        // chunk c of row r at slot c ^ (r & 31) so that a store instruction's
+        // 32 rows take distinct banks, then 32 consecutive threads store
+        // each row as 16-byte pieces of one 512-byte run (row-strided 8-byte
+        // stores straight from the accumulators took about 17 us longer per
+        // 256 x 248320 launch, 13 us per 448 x 151936).
+        static_assert(kTST * kTSST == kTBT * kTBN * 2, "the fp16 tile fills the ring");
+        // the lane's chunk c = 16 wn + 4 v + q of row rl (rl & 31 = r32) sits
+        // at slot (16 wn ^ r32) ^ (4 v + q); xs is kept opaque so that the
+        // sixteen slot addresses are formed here rather than hoisted out of
+        // the tile loop (and spilled)
+        int xs = (16 * wn) ^ r32;
+        asm volatile("" : "+v"(xs));
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          uint8_t *rowp = smem + (wt * 64 + t * 32 + r32) * 512 + kg * 8;
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              uint32_t hh[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) hh[e] = f2h(__expf(acc[v][t][4 * q + e] - m[t]));
+              *reinterpret_cast<uint2 *>(rowp + ((xs ^ (4 * v + q)) << 4)) =
+                  make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll 4
+        for (int i = tid; i < kTBT * 32; i += 512) {
+          const int rl = i >> 5, c = i & 31;
+          const int tok = t0 + rl, col = n0 + c * 8;
+          if (tok < g.rows && col < g.N)
+            *reinterpret_cast<uint4 *>(g.p16 + int64_t(tok) * g.ldo + col) =
+                *reinterpret_cast<const uint4 *>(smem + rl * 512 + ((c ^ (rl & 31)) << 4));
+        }
       } else {
         store_tile<4, 2>(go, acc, nb, tb, lane);
       }
@@ -536,6 +572,10 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
       store_tile<4, 2>(go, acc, nb, tb, lane);
     }
 
+    // the staged probabilities are read before the next tile's copies refill the ring
+    if constexpr (STATS) {
+      if (g.p16) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
     int next = tile + gridDim.x;
     while (next < n_tiles_all && !valid(next)) next += gridDim.x;
     const bool more = next < n_tiles_all;
