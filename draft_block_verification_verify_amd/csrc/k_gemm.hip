@@ -99,10 +99,13 @@ __device__ __forceinline__ void store_tile_p16(const GemmArgs &g, const f32x16 (
 
 // Per-lane (max, sumexp, argmax) over the lane's N values of token block t,
 // merged with the partner lane (l ^ 32) holding the other N rows.  CHECK
-// masks columns n >= N (only the last tile of a launch needs it).
-template <int NV, int NT, bool CHECK = true>
-__device__ __forceinline__ MaxSumArg lane_stats(const GemmArgs &g, const f32x16 (&acc)[NV][NT], const int (&nb)[NV],
-                                                int t, int lane) {
+// masks columns n >= N (only the last tile of a launch needs it).  KEEP:
+// each value is replaced by its exp(x - m), m the lane's own maximum
+// (returned in *m_lane), so that the caller can rescale it instead of taking
+// the exponential again; the sums are the same either way.
+template <int NV, int NT, bool CHECK = true, bool KEEP = false>
+__device__ __forceinline__ MaxSumArg lane_stats(const GemmArgs &g, f32x16 (&acc)[NV][NT], const int (&nb)[NV],
+                                                int t, int lane, float *m_lane = nullptr) {
   const int kg = lane >> 5;
   float m = -INFINITY;
   int arg = 0x7fffffff;
@@ -119,7 +122,21 @@ __device__ __forceinline__ MaxSumArg lane_stats(const GemmArgs &g, const f32x16 
       }
     }
   float s = 0.f;
-  if (m != -INFINITY) {
+  if constexpr (KEEP) {
+    // branch-free (a lane whose columns are all masked has every x = -inf,
+    // so every exp is 0, as is its sum)
+    const float mm = m == -INFINITY ? 0.f : m;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int n = nb[v] + 8 * (j >> 2) + 4 * kg + (j & 3);
+        const float e = __expf(acc[v][t][j] - mm);
+        if (!CHECK || n < g.N) s += e;
+        acc[v][t][j] = e;
+      }
+    *m_lane = m;
+  } else if (m != -INFINITY) {
 #pragma unroll
     for (int v = 0; v < NV; ++v)
 #pragma unroll
@@ -506,9 +523,14 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
             for (int j = 0; j < 16; ++j)
               if (nb[v] + 8 * (j >> 2) + 4 * kg + (j & 3) >= g.N) acc[v][t][j] = -INFINITY;
       }
+      // fp32 logits (when asked for) leave first: the statistics below
+      // replace each accumulator by exp(x - the lane's maximum), which the
+      // fp16 probabilities rescale
+      if (!g.p16) store_tile<4, 2>(go, acc, nb, tb, lane);
+      float ml[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const MaxSumArg r = lane_stats<4, 2, false>(g, acc, nb, t, lane);
+        const MaxSumArg r = lane_stats<4, 2, false, true>(g, acc, nb, t, lane, &ml[t]);
         if (kg == 0) red[wn][wt * 64 + t * 32 + r32] = r;
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -520,13 +542,15 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
         g.t_arg[o] = r.i;
       }
       if (g.p16) {
-        // tile maximum of each of the lane's two tokens (the value the merge
-        // above writes to t_max)
-        float m[2];
+        // exp(x - M), M the tile maximum of the token (the value the merge
+        // above writes to t_max), as exp(x - m) exp(m - M) with m the lane's
+        // maximum (a lane whose columns are all past N stores none of them)
+        float sc[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int row = wt * 64 + t * 32 + r32;
-          m[t] = fmaxf(red[0][row].m, red[1][row].m);
+          const float M = fmaxf(red[0][row].m, red[1][row].m);
+          sc[t] = ml[t] == -INFINITY ? 0.f : __expf(ml[t] - M);
         }
         // The tile's fp16 probabilities go through the idle ring (256 rows x
         // 512 B = its 128 KB): each lane writes its 8-byte pieces, 16-byte
@@ -551,7 +575,7 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
             for (int q = 0; q < 4; ++q) {
               uint32_t hh[4];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) hh[e] = f2h(__expf(acc[v][t][4 * q + e] - m[t]));
+              for (int e = 0; e < 4; ++e) hh[e] = f2h(acc[v][t][4 * q + e] * sc[t]);
               *reinterpret_cast<uint2 *>(rowp + ((xs ^ (4 * v + q)) << 4)) =
                   make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
             }
@@ -565,8 +589,6 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
             *reinterpret_cast<uint4 *>(g.p16 + int64_t(tok) * g.ldo + col) =
                 *reinterpret_cast<const uint4 *>(smem + rl * 512 + ((c ^ (rl & 31)) << 4));
         }
-      } else {
-        store_tile<4, 2>(go, acc, nb, tb, lane);
       }
     } else {
       store_tile<4, 2>(go, acc, nb, tb, lane);
