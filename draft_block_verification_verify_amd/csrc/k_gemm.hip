@@ -109,29 +109,53 @@ __device__ __forceinline__ MaxSumArg lane_stats(const GemmArgs &g, f32x16 (&acc)
   const int kg = lane >> 5;
   float m = -INFINITY;
   int arg = 0x7fffffff;
-#pragma unroll
-  for (int v = 0; v < NV; ++v)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int n = nb[v] + 8 * (j >> 2) + 4 * kg + (j & 3);
-      const float x = acc[v][t][j];
-      // columns grow with (v, j): a strict > keeps the lowest index on ties
-      if ((!CHECK || n < g.N) && x > m) {
-        m = x;
-        arg = n;
-      }
-    }
-  float s = 0.f;
-  if constexpr (KEEP) {
-    // branch-free (a lane whose columns are all masked has every x = -inf,
-    // so every exp is 0, as is its sum)
-    const float mm = m == -INFINITY ? 0.f : m;
+  if constexpr (CHECK) {
 #pragma unroll
     for (int v = 0; v < NV; ++v)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int n = nb[v] + 8 * (j >> 2) + 4 * kg + (j & 3);
-        const float e = __expf(acc[v][t][j] - mm);
+        const float x = acc[v][t][j];
+        // columns grow with (v, j): a strict > keeps the lowest index on ties
+        if (n < g.N && x > m) {
+          m = x;
+          arg = n;
+        }
+      }
+  } else {
+    // the maximum, then the first (v, j) holding it (columns grow with
+    // (v, j), so that is the lowest column); the position is a constant
+    // per value and becomes a column once
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) m = fmaxf(m, acc[v][t][j]);
+    int code = 16 * NV;
+#pragma unroll
+    for (int v = NV - 1; v >= 0; --v)
+#pragma unroll
+      for (int j = 15; j >= 0; --j) code = acc[v][t][j] == m ? 16 * v + j : code;
+    if (m != -INFINITY) {
+      int base = nb[0];
+#pragma unroll
+      for (int v = 1; v < NV; ++v) base = (code >> 4) == v ? nb[v] : base;
+      const int j = code & 15;
+      arg = base + 8 * (j >> 2) + 4 * kg + (j & 3);
+    }
+  }
+  float s = 0.f;
+  if constexpr (KEEP) {
+    // branch-free (a lane whose columns are all masked has every x = -inf,
+    // so every exp is 0, as is its sum); exp(x - m) as 2^(x log2 e - m log2 e)
+    // with one fused multiply-add
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float mL = (m == -INFINITY ? 0.f : m) * kLog2e;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int n = nb[v] + 8 * (j >> 2) + 4 * kg + (j & 3);
+        const float e = __builtin_amdgcn_exp2f(fmaf(acc[v][t][j], kLog2e, -mL));
         if (!CHECK || n < g.N) s += e;
         acc[v][t][j] = e;
       }
