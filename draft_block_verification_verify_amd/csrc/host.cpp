@@ -818,7 +818,7 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   // probabilities relative to the tile maximum in fp16 instead of fp32
   // logits: half the bytes for their readers (the overlap pass, and in T = 1
   // mode the accept tests and the bonus draw).
-  const bool use_p16 = bf16 && !fp8 && n > 64 && !out->logits && h->p16 != nullptr;
+  const bool use_p16 = bf16 && n > 64 && !out->logits && h->p16 != nullptr;
   sv::VocabArgs va = vocab_args(plan, m, lay, int(V), bf16, in, out,
                                 VocabBufs{logits, use_p16 ? h->p16 : nullptr, h->t_max, h->t_sum, h->t_arg,
                                           n_tiles, h->dpart, h->n_dch, h->lse_q, h->opart, h->n_och});

@@ -143,32 +143,22 @@ __device__ __forceinline__ MaxSumArg lane_stats(const GemmArgs &g, f32x16 (&acc)
       arg = base + 8 * (j >> 2) + 4 * kg + (j & 3);
     }
   }
+  // exp(x - m) as 2^(x log2 e - m log2 e), one fused multiply-add per value
+  // and the same form on every path; branch-free (a lane whose columns are
+  // all masked has every x = -inf, so every exp is 0, as is its sum)
+  constexpr float kLog2e = 1.4426950408889634f;
+  const float mL = (m == -INFINITY ? 0.f : m) * kLog2e;
   float s = 0.f;
-  if constexpr (KEEP) {
-    // branch-free (a lane whose columns are all masked has every x = -inf,
-    // so every exp is 0, as is its sum); exp(x - m) as 2^(x log2 e - m log2 e)
-    // with one fused multiply-add
-    constexpr float kLog2e = 1.4426950408889634f;
-    const float mL = (m == -INFINITY ? 0.f : m) * kLog2e;
 #pragma unroll
-    for (int v = 0; v < NV; ++v)
+  for (int v = 0; v < NV; ++v)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int n = nb[v] + 8 * (j >> 2) + 4 * kg + (j & 3);
-        const float e = __builtin_amdgcn_exp2f(fmaf(acc[v][t][j], kLog2e, -mL));
-        if (!CHECK || n < g.N) s += e;
-        acc[v][t][j] = e;
-      }
-    *m_lane = m;
-  } else if (m != -INFINITY) {
-#pragma unroll
-    for (int v = 0; v < NV; ++v)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int n = nb[v] + 8 * (j >> 2) + 4 * kg + (j & 3);
-        if (!CHECK || n < g.N) s += __expf(acc[v][t][j] - m);
-      }
-  }
+    for (int j = 0; j < 16; ++j) {
+      const int n = nb[v] + 8 * (j >> 2) + 4 * kg + (j & 3);
+      const float e = __builtin_amdgcn_exp2f(fmaf(acc[v][t][j], kLog2e, -mL));
+      if (!CHECK || n < g.N) s += e;
+      if constexpr (KEEP) acc[v][t][j] = e;
+    }
+  if constexpr (KEEP) *m_lane = m;
   MaxSumArg r{m, s, arg};
   return msa_shfl_xor(r, 32);
 }
@@ -842,8 +832,12 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
       }
     }
     if constexpr (STATS) {
-      // (max, sumexp, argmax) per row over this wave's 128 N, then across
-      // the two N halves through a small static LDS array
+      // the fp16 tiled kernel's epilogue, line for line: (max, sumexp,
+      // argmax) per row over this wave's 128 N, then across the two N halves
+      // through a small static LDS array, then fp32 logits or staged fp16
+      // probabilities.  (Kept inline in both kernels: as one shared
+      // function the compiler held more kernel arguments in scalar registers
+      // across the K loop and spilled them there.)
       __shared__ MaxSumArg red[2][kTBT];
       if (n0 + kTBN > g.N) {
         // last tile: columns past N (zero weights) must not take part
@@ -855,9 +849,14 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
             for (int j = 0; j < 16; ++j)
               if (nb[v] + 8 * (j >> 2) + 4 * kg + (j & 3) >= g.N) acc[v][t][j] = -INFINITY;
       }
+      // fp32 logits (when asked for) leave first: the statistics below
+      // replace each accumulator by exp(x - the lane's maximum), which the
+      // fp16 probabilities rescale
+      if (!g.p16) store_tile<4, 2>(go, acc, nb, tb, lane);
+      float ml[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const MaxSumArg r = lane_stats<4, 2, false>(g, acc, nb, t, lane);
+        const MaxSumArg r = lane_stats<4, 2, false, true>(g, acc, nb, t, lane, &ml[t]);
         if (kg == 0) red[wn][wt * 64 + t * 32 + r32] = r;
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -868,8 +867,58 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
         g.t_sum[o] = r.s;
         g.t_arg[o] = r.i;
       }
+      if (g.p16) {
+        // exp(x - M), M the tile maximum of the token (the value the merge
+        // above writes to t_max), as exp(x - m) exp(m - M) with m the lane's
+        // maximum (a lane whose columns are all past N stores none of them)
+        float sc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int row = wt * 64 + t * 32 + r32;
+          const float M = fmaxf(red[0][row].m, red[1][row].m);
+          sc[t] = ml[t] == -INFINITY ? 0.f : __expf(ml[t] - M);
+        }
+        // The tile's fp16 probabilities go through the idle ring (256 rows x
+        // 512 B = its 128 KB): each lane writes its 8-byte pieces, 16-byte
+        // chunk c of row r at slot c ^ (r & 31) so that a store instruction's
+        // 32 rows take distinct banks, then 32 consecutive threads store
+        // each row as 16-byte pieces of one 512-byte run (row-strided 8-byte
+        // stores straight from the accumulators took about 17 us longer per
+        // 256 x 248320 launch, 13 us per 448 x 151936).
+        static_assert(kTST * kTSST == kTBT * kTBN * 2, "the fp16 tile fills the ring");
+        // the lane's chunk c = 16 wn + 4 v + q of row rl (rl & 31 = r32) sits
+        // at slot (16 wn ^ r32) ^ (4 v + q); xs is kept opaque so that the
+        // sixteen slot addresses are formed here rather than hoisted out of
+        // the tile loop (and spilled)
+        int xs = (16 * wn) ^ r32;
+        asm volatile("" : "+v"(xs));
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          uint8_t *rowp = smem + (wt * 64 + t * 32 + r32) * 512 + kg * 8;
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              uint32_t hh[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) hh[e] = f2h(acc[v][t][4 * q + e] * sc[t]);
+              *reinterpret_cast<uint2 *>(rowp + ((xs ^ (4 * v + q)) << 4)) =
+                  make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll 4
+        for (int i = tid; i < kTBT * 32; i += 512) {
+          const int rl = i >> 5, c = i & 31;
+          const int tok = t0 + rl, col = n0 + c * 8;
+          if (tok < g.rows && col < g.N)
+            *reinterpret_cast<uint4 *>(g.p16 + int64_t(tok) * g.ldo + col) =
+                *reinterpret_cast<const uint4 *>(smem + rl * 512 + ((c ^ (rl & 31)) << 4));
+        }
+      }
     }
-    store_tile<4, 2>(go, acc, nb, tb, lane);
+    // the staged probabilities are read before the next tile's copies refill the ring
+    if (g.p16) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     int next = tile + gridDim.x;
     while (next < n_tiles_all && !valid(next)) next += gridDim.x;

@@ -38,6 +38,9 @@ FP8_MINIS = {
     # the tree shape with a hidden width above its 448 rows (the margin
     # planting needs no more rows than the hidden width)
     "c4m8": mini(4, hidden=1024, vocab=2048, stem=300, w_lm_std=0.04),
+    # 96 rows: above 64 (fp16 probabilities without a logits buffer) and
+    # below 128 (the kernel's variant that skips padding rows)
+    "c5h": mini(5, hidden=384, vocab=3000, n_seqs=12, min_len=3, max_len=200, w_lm_std=0.06),
 }
 
 
@@ -178,6 +181,30 @@ def _check_fp8(inp, cd, ref, gpu, rows, name, min_clear):
 def test_parity_fp8(name, seed):
     inp, cd, ref, gpu, rows = fp8_case(FP8_MINIS[name], seed)
     _check_fp8(inp, cd, ref, gpu, rows, f"{name}/fp8/seed{seed}", 0.9)
+
+
+@pytest.mark.parametrize("name", ["c5m", "c4m8", "c5h"])
+def test_parity_fp8_without_logits_buffer(name):
+    # No caller logits buffer: above 64 rows the FP8 LM head then keeps fp16
+    # tile-relative probabilities for the overlap pass instead of fp32 logits
+    # (the path the benchmark times); every output is held to the same rules.
+    inp, cd, ref, gpu, rows = fp8_case(FP8_MINIS[name], 0, with_logits=False)
+    assert gpu["logits"] is None
+    _check_fp8(inp, cd, ref, gpu, rows, f"{name}/fp8/no-logits", 0.9)
+
+
+@pytest.mark.parametrize("name", ["c5m", "c5h"])
+def test_fp8_logits_buffer_changes_no_decision(name):
+    # the same FP8 run with and without a logits buffer: the tile statistics
+    # come from the same code either way, so every decision and row
+    # statistic is identical; only the overlaps' inputs differ (fp32 logits
+    # or fp16 probabilities relative to each tile's maximum, 2^-11 relative)
+    inp, cd, ref, with_buf, rows = fp8_case(FP8_MINIS[name], 1)
+    without = _run(inp, with_logits=False)
+    for k in ("argmax", "accept_len", "bonus", "last_row", "row_max", "row_lse"):
+        np.testing.assert_array_equal(without[k], with_buf[k], err_msg=k)
+    np.testing.assert_allclose(without["overlap"], with_buf["overlap"], rtol=0, atol=2e-3)
+    np.testing.assert_allclose(without["survival"], with_buf["survival"], rtol=0, atol=2e-3)
 
 
 @pytest.mark.parametrize("name", ["c5m", "c4m8"])
