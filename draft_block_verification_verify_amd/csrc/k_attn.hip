@@ -104,8 +104,10 @@ __device__ __forceinline__ const __attribute__((address_space(4))) T *as_const(c
 }
 
 // STG: ring stages (tiles in flight = STG - 1); OCC: wavefronts per SIMD the
-// launch is built for (registers per wavefront <= 512 / OCC).
-template <int D, int NW, int STG, int OCC>
+// launch is built for (registers per wavefront <= 512 / OCC); NTP: partial o
+// records stored with the non-temporal hint (a template choice: as a runtime
+// branch the compiler merged the two stores and dropped the hint).
+template <int D, int NW, int STG, int OCC, bool NTP>
 __global__ __launch_bounds__(64 * NW, OCC) void attn_mfma_kernel(AttnArgs a) {
   using TL = AttnTile<D>;
   constexpr int KT = TL::KT, ROWB = TL::ROWB, TILEB = TL::TILEB, CH = TL::CH, RPI = TL::RPI;
@@ -411,8 +413,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void attn_mfma_kernel(AttnArgs a) {
           a.part_ml[2 * slot + 1] = l_all;
         }
         float *po = a.part_o + slot * D + 4 * kg;
+        if constexpr (NTP) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4 *>(po + db * 16) = o[db];
+          for (int db = 0; db < DB; ++db) __builtin_nontemporal_store(o[db], reinterpret_cast<f32x4 *>(po + db * 16));
+        } else {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4 *>(po + db * 16) = o[db];
+        }
       }
       if (s + 1 < nt) c_enter(c_item + 1);
     }
@@ -655,12 +662,20 @@ void launch_rope_f32(const float *q, const float *k, float *qo, float *ko, const
   hipLaunchKernelGGL(rope_rows_kernel<float>, grid, dim3(256), 0, s, q, k, qo, ko, row_pos, Hq, Hkv, D, base);
 }
 
+template <int D, int NW, int STG, int OCC, bool NTP>
+static void launch_attn_ddn(const AttnArgs &a, int n_runs, hipStream_t s) {
+  constexpr size_t lds = attn_lds_bytes<D, STG>();
+  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(attn_mfma_kernel<D, NW, STG, OCC, NTP>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  hipLaunchKernelGGL((attn_mfma_kernel<D, NW, STG, OCC, NTP>), dim3(n_runs), dim3(64 * NW), lds, s, a);
+}
+
 template <int D, int NW, int STG, int OCC>
 static void launch_attn_dd(const AttnArgs &a, int n_runs, hipStream_t s) {
-  constexpr size_t lds = attn_lds_bytes<D, STG>();
-  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(attn_mfma_kernel<D, NW, STG, OCC>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-  hipLaunchKernelGGL((attn_mfma_kernel<D, NW, STG, OCC>), dim3(n_runs), dim3(64 * NW), lds, s, a);
+  if (a.nt_part)
+    launch_attn_ddn<D, NW, STG, OCC, true>(a, n_runs, s);
+  else
+    launch_attn_ddn<D, NW, STG, OCC, false>(a, n_runs, s);
 }
 
 // Four wavefronts (up to 64 query vectors): a 2-stage ring (64 KB of LDS)

@@ -54,6 +54,7 @@ struct AttnArgs {
   float *part_o, *part_ml;         // [slots, D], [slots, 2]
   int Hq, Hkv, G;
   float scale_log2;                // log2(e) / sqrt(D)
+  int nt_part;                     // 1: o records stored with the non-temporal hint
 };
 
 struct MergeArgs {
