@@ -586,6 +586,56 @@ __device__ __forceinline__ void accept_tree(const VocabArgs &a, int r) {
   }
 }
 
+// The overlap chunk of the small-batch launch (fp32 logits, bf16 drafter
+// logits, a full chunk): its loads are issued before the row and drafter
+// statistics are merged, since they do not depend on them; the sum then
+// follows overlap_block's order exactly.
+struct OverlapChunk {
+  static constexpr int NG = kOverlapChunk / 2048;   // groups of 8 per thread
+  uint4 q[NG];                                      // drafter logits, bf16 packed
+  float4 l0[NG], l1[NG];                            // the parent's logits
+};
+
+__device__ __forceinline__ bool overlap_chunk_fast(const VocabArgs &a) {
+  return !a.p16 && (a.V % 8) == 0 && a.ochunk == kOverlapChunk && a.drafter_bf16;
+}
+
+__device__ __forceinline__ void overlap_chunk_load(const VocabArgs &a, int c, int t, int j, OverlapChunk &k) {
+  const int tid = threadIdx.x;
+  const float *lp = a.logits + int64_t(j) * a.V;
+  const int64_t qrow = int64_t(t) * a.V;
+  const int lo = c * a.ochunk, hi = min(a.V, lo + a.ochunk);
+#pragma unroll
+  for (int g = 0; g < OverlapChunk::NG; ++g) {
+    const int u = lo + tid * 8 + g * 2048;
+    if (u < hi) {
+      k.q[g] = ld16s(static_cast<const uint16_t *>(a.drafter) + qrow + u);
+      k.l0[g] = *reinterpret_cast<const float4 *>(lp + u);
+      k.l1[g] = *reinterpret_cast<const float4 *>(lp + u + 4);
+    }
+  }
+}
+
+__device__ __forceinline__ void overlap_chunk_sum(const VocabArgs &a, int c, int t, const OverlapChunk &k, float A,
+                                                  float B) {
+  const int tid = threadIdx.x;
+  const int lo = c * a.ochunk, hi = min(a.V, lo + a.ochunk);
+  float s = 0.f;
+#pragma unroll
+  for (int g = 0; g < OverlapChunk::NG; ++g) {
+    if (lo + tid * 8 + g * 2048 >= hi) continue;
+    const float l[8] = {k.l0[g].x, k.l0[g].y, k.l0[g].z, k.l0[g].w, k.l1[g].x, k.l1[g].y, k.l1[g].z, k.l1[g].w};
+    const uint32_t w[4] = {k.q[g].x, k.q[g].y, k.q[g].z, k.q[g].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float b = __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+      s += __expf(fminf(l[e] - A, b - B));
+    }
+  }
+  s = sum_block256(s);
+  if (tid == 0) a.opart[int64_t(t) * a.n_och + c] = s;
+}
+
 // Small batches: the row statistics and the overlap sums in one launch.
 // Workgroups [0, n) combine row b; the rest take overlap chunks, each
 // merging its parent's and its drafter row's records itself with the same
@@ -612,9 +662,17 @@ __global__ __launch_bounds__(256) void combine_overlap_kernel(VocabArgs a) {
   } else {
     const int d = b - a.n, c = d % a.n_och, t = d / a.n_och;
     const int j = a.row_parent[a.draft_row[t]];
-    const MaxSumArg r = row_stats_block(a, j);
-    const MaxSum q = drafter_stats_block(a, t);
-    overlap_block(a, c, t, j, r.m + logf(r.s), q.m + logf(q.s));
+    if (overlap_chunk_fast(a)) {
+      OverlapChunk k;
+      overlap_chunk_load(a, c, t, j, k);
+      const MaxSumArg r = row_stats_block(a, j);
+      const MaxSum q = drafter_stats_block(a, t);
+      overlap_chunk_sum(a, c, t, k, r.m + logf(r.s), q.m + logf(q.s));
+    } else {
+      const MaxSumArg r = row_stats_block(a, j);
+      const MaxSum q = drafter_stats_block(a, t);
+      overlap_block(a, c, t, j, r.m + logf(r.s), q.m + logf(q.s));
+    }
     tree = a.row_tree[a.draft_row[t]];
   }
   if constexpr (!ACCEPT) return;
