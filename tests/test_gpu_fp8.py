@@ -217,7 +217,9 @@ def test_parity_fp8_unplanted(name):
 
 
 @pytest.mark.slow
-def test_parity_fp8_full_size_sampled():
+@pytest.mark.parametrize("with_logits", [True, False])
+def test_parity_fp8_full_size_sampled(with_logits):
+    # without a logits buffer: the fp16 probability path the benchmark times
     from draft_block_verification_verify_amd.runner import DeviceCase
     cfg = W.CONFIGS[5]
     _say(f"[full fp8] generating {cfg.name}")
@@ -232,10 +234,11 @@ def test_parity_fp8_full_size_sampled():
     g = O.target_greedy(cd, O.inp_dict(inp), trees=trees)
     W.plant_chain_drafts(inp, np.where(g < 0, 0, g))
     ref = O.verify(cd, O.inp_dict(inp), trees=trees, keep_logits=True)
-    _say("[full fp8] gpu run")
-    dc = DeviceCase(inp, with_logits=True, fp8=True)
+    _say(f"[full fp8] gpu run, logits buffer {with_logits}")
+    dc = DeviceCase(inp, with_logits=with_logits, fp8=True)
     dc.run()
     gpu = dc.results()
     dc.close()
-    rep = _check_fp8(inp, cd, ref, gpu, [int(i) for i in ref["rows"]], f"{cfg.name}/fp8/full-sampled", 0.9)
+    name = f"{cfg.name}/fp8/full-sampled" + ("" if with_logits else "/no-logits")
+    rep = _check_fp8(inp, cd, ref, gpu, [int(i) for i in ref["rows"]], name, 0.9)
     _say(f"[full fp8] clear fraction {rep['clear_fraction']:.3f}")
