@@ -9,9 +9,9 @@ Tolerances (bf16 inputs, fp32 accumulation):
   * probabilities p = softmax(logits): 1e-3 absolute.  Without a logits
     buffer this is checked on the top token from the row statistics alone:
     p_max = exp(row_max - row_lse) moves by p_max * |d(row_max - row_lse)|,
-    held to 1e-3; row_lse itself is held to 1e-2 absolute (a common shift
-    of every logit moves lse but no probability, so lse gets the looser
-    bound);
+    held to 1e-3; row_lse itself is held to 1e-3 absolute (an lse error d
+    moves every p = exp(l - lse) by about p * d <= d, so this bounds what
+    lse alone can do to any probability by the probability tolerance);
   * overlaps and survival products: 2e-3 absolute.
 
 FP8 LM head (e4m3 W8A8): the activations are quantised from each side's own
@@ -23,7 +23,7 @@ differ by B[t, n] = a_t * sum over such elements k of step_k * |s_n q_w[n, k]|
 (fp8_bounds, from the oracle's own hidden state and weights); the logits are
 held to B plus 1e-3 * max(|ref|, rms) (fp32 accumulation), decisions are
 exact where the oracle's top-2 gap exceeds 2 max_n B[t, n] + 1e-2.  Since
-lse moves by at most max_n B[t, n], the log-sum-exp is held to 1e-2 + max B
+lse moves by at most max_n B[t, n], the log-sum-exp is held to 1e-3 + max B
 and each probability p_n to 1e-3 + p_n (exp(B[t, n] + max B) - 1) (the
 top token's likewise, from the row statistics).  A row whose largest value sits within 1e-2 of a
 scale boundary (448 * 2^e) may take the other power of two: it is held to
@@ -39,7 +39,7 @@ LOGIT_REL = 2e-2
 PROB_ABS = 1e-3
 OV_ABS = 2e-3
 EPS_H = 2e-3
-LSE_ABS = 1e-2
+LSE_ABS = 1e-3
 FP8_TOL = {}
 
 
