@@ -413,7 +413,7 @@ def test_repeat_runs_bit_identical_and_handle_reuse():
     dc2 = DeviceCase(small, with_logits=True, verifier=dc.ver, weights=(dc.w_o, dc.w_lm))
     dc2.run()
     c = dc2.results()
-    # 32 rows take the skinny projection path (256 took the tiled one): judge
+    # 32 rows take the skinny projection path (256 took the tiled one): check
     # the second run against the oracle
     ref = O.verify(O.cfg_dict(cfg), O.inp_dict(small), keep_logits=True)
     P.check_self_consistency(small.st.parent, small.draft_ids, c)
