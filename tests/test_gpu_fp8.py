@@ -41,6 +41,9 @@ FP8_MINIS = {
     # 96 rows: above 64 (fp16 probabilities without a logits buffer) and
     # below 128 (the kernel's variant that skips padding rows)
     "c5h": mini(5, hidden=384, vocab=3000, n_seqs=12, min_len=3, max_len=200, w_lm_std=0.06),
+    # 96 rows, a vocabulary that is not a multiple of 8: fp32 logits for the
+    # overlap pass even without a caller buffer
+    "c5v": MINIS["c5v"],
 }
 
 
@@ -183,7 +186,7 @@ def test_parity_fp8(name, seed):
     _check_fp8(inp, cd, ref, gpu, rows, f"{name}/fp8/seed{seed}", 0.9)
 
 
-@pytest.mark.parametrize("name", ["c5m", "c4m8", "c5h"])
+@pytest.mark.parametrize("name", ["c5m", "c4m8", "c5h", "c5v"])
 def test_parity_fp8_without_logits_buffer(name):
     # No caller logits buffer: above 64 rows the FP8 LM head then keeps fp16
     # tile-relative probabilities for the overlap pass instead of fp32 logits
