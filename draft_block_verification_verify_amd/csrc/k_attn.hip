@@ -466,8 +466,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a, int n_pair
       Li += ml.y * exp2f(ml.x - Mi);
     }
   }
-  const float M = wave_max(Mi);
-  const float L = wave_sum(Mi == -INFINITY ? 0.f : Li * exp2f(Mi - M));
+  const float M = wave_max_dpp(Mi);
+  const float L = wave_sum_dpp(Mi == -INFINITY ? 0.f : Li * exp2f(Mi - M));
   for (int t = c; t < cnt; t += 64) {         // the lane's own entries: no other lane writes them
     const float mt = wl[w][t];
     wl[w][t] = mt == -INFINITY ? 0.f : exp2f(mt - M);
@@ -523,8 +523,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a, int n_pair
         st = fmaf(kh, qv[e], st);
         sx = fmaf(kh + kl, qv[e], sx);
       }
-      st = wave_sum(st);
-      sx = wave_sum(sx);
+      st = wave_sum_dpp(st);
+      sx = wave_sum_dpp(sx);
       const float dp = exp2f(sx * a.scale_log2 - M) - exp2f(st * a.scale_log2 - M);
       dl += dp;
 #pragma unroll

@@ -122,6 +122,36 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Whole-wavefront sum and max on DPP moves instead of LDS permutes: xor 1
+// and xor 2 inside each quad, the half-row and row mirrors (8 and 16 lanes),
+// then the row broadcasts of lane 15 and lane 31 carry the partial results up
+// to lane 63, which every lane then reads.  The order of the adds differs
+// from the permute butterfly above.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_move(float v, float fill) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_move<0xB1>(v, 0.f);         // quad_perm [1,0,3,2]
+  v += dpp_move<0x4E>(v, 0.f);         // quad_perm [2,3,0,1]
+  v += dpp_move<0x141>(v, 0.f);        // row_half_mirror
+  v += dpp_move<0x140>(v, 0.f);        // row_mirror
+  v += dpp_move<0x142, 0xA>(v, 0.f);   // row_bcast15 into rows 1 and 3
+  v += dpp_move<0x143, 0xC>(v, 0.f);   // row_bcast31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_move<0xB1>(v, -INFINITY));
+  v = fmaxf(v, dpp_move<0x4E>(v, -INFINITY));
+  v = fmaxf(v, dpp_move<0x141>(v, -INFINITY));
+  v = fmaxf(v, dpp_move<0x140>(v, -INFINITY));
+  v = fmaxf(v, dpp_move<0x142, 0xA>(v, -INFINITY));
+  v = fmaxf(v, dpp_move<0x143, 0xC>(v, -INFINITY));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // Reductions over the four lanes l, l^16, l^32, l^48 (one per 16-lane row)
 // with the gfx950 row swaps: v_permlane16_swap exchanges the odd rows of its
 // first operand with the even rows of its second, v_permlane32_swap the upper
