@@ -110,23 +110,11 @@ __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), as_bf8(b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-// Whole-wavefront sum and max on DPP moves instead of LDS permutes: xor 1
-// and xor 2 inside each quad, the half-row and row mirrors (8 and 16 lanes),
-// then the row broadcasts of lane 15 and lane 31 carry the partial results up
-// to lane 63, which every lane then reads.  The order of the adds differs
-// from the permute butterfly above.
+// Whole-wavefront reductions on DPP moves (a permute butterfly of
+// __shfl_xor compiles to six LDS round trips): xor 1 and xor 2 inside each
+// quad, the half-row and row mirrors (8 and 16 lanes), then the row
+// broadcasts of lane 15 and lane 31 carry the partial results up to lane 63,
+// which every lane then reads.  Every lane of the wavefront must be active.
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ float dpp_move(float v, float fill) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
@@ -151,6 +139,9 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
   v = fmaxf(v, dpp_move<0x143, 0xC>(v, -INFINITY));
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+
+__device__ __forceinline__ float wave_max(float v) { return wave_max_dpp(v); }
+__device__ __forceinline__ float wave_sum(float v) { return wave_sum_dpp(v); }
 
 // Reductions over the four lanes l, l^16, l^32, l^48 (one per 16-lane row)
 // with the gfx950 row swaps: v_permlane16_swap exchanges the odd rows of its
@@ -192,6 +183,30 @@ __device__ __forceinline__ MaxSumArg msa_merge(MaxSumArg a, MaxSumArg b) {
   }
   r.i = (b.m > a.m || (b.m == a.m && b.i < a.i)) ? b.i : a.i;
   return r;
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ MaxSumArg msa_dpp_step(MaxSumArg a) {
+  const MaxSumArg e = msa_empty();
+  MaxSumArg b;
+  b.m = dpp_move<CTRL, ROW_MASK>(a.m, e.m);
+  b.s = dpp_move<CTRL, ROW_MASK>(a.s, e.s);
+  b.i = __builtin_amdgcn_update_dpp(e.i, a.i, CTRL, ROW_MASK, 0xF, false);
+  return msa_merge(a, b);
+}
+
+// (max, sum exp, argmax) over the wavefront (the DPP sequence of wave_sum);
+// every lane gets lane 63's result
+__device__ __forceinline__ MaxSumArg msa_wave(MaxSumArg r) {
+  r = msa_dpp_step<0xB1>(r);
+  r = msa_dpp_step<0x4E>(r);
+  r = msa_dpp_step<0x141>(r);
+  r = msa_dpp_step<0x140>(r);
+  r = msa_dpp_step<0x142, 0xA>(r);
+  r = msa_dpp_step<0x143, 0xC>(r);
+  return MaxSumArg{__int_as_float(__builtin_amdgcn_readlane(__float_as_int(r.m), 63)),
+                   __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r.s), 63)),
+                   __builtin_amdgcn_readlane(r.i, 63)};
 }
 
 __device__ __forceinline__ MaxSumArg msa_shfl_xor(MaxSumArg a, int mask) {

@@ -1090,8 +1090,7 @@ __global__ __launch_bounds__(256) void stats_from_logits_kernel(const float *log
   const float *lg = logits + int64_t(row) * V;
   MaxSumArg r = msa_empty();
   for (int u = c * tile + tid; u < min(V, (c + 1) * tile); u += 256) r = msa_merge(r, MaxSumArg{lg[u], 1.f, u});
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) r = msa_shfl_xor(r, o);
+  r = msa_wave(r);
   __shared__ MaxSumArg red[4];
   if ((tid & 63) == 0) red[tid >> 6] = r;
   __syncthreads();

@@ -34,12 +34,21 @@ __device__ __forceinline__ MaxSum ms_merge(MaxSum a, MaxSum b) {
   return {m, a.s * __expf(a.m - m) + b.s * __expf(b.m - m)};
 }
 
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ MaxSum ms_dpp_step(MaxSum a) {
+  return ms_merge(a, MaxSum{dpp_move<CTRL, ROW_MASK>(a.m, -INFINITY), dpp_move<CTRL, ROW_MASK>(a.s, 0.f)});
+}
+
 __device__ __forceinline__ MaxSum ms_block256(MaxSum r) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    MaxSum b{__shfl_xor(r.m, o), __shfl_xor(r.s, o)};
-    r = ms_merge(r, b);
-  }
+  // the wavefront's (max, sum exp) on DPP moves (the sequence of wave_sum)
+  r = ms_dpp_step<0xB1>(r);
+  r = ms_dpp_step<0x4E>(r);
+  r = ms_dpp_step<0x141>(r);
+  r = ms_dpp_step<0x140>(r);
+  r = ms_dpp_step<0x142, 0xA>(r);
+  r = ms_dpp_step<0x143, 0xC>(r);
+  r = MaxSum{__int_as_float(__builtin_amdgcn_readlane(__float_as_int(r.m), 63)),
+             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r.s), 63))};
   __shared__ MaxSum red[4];
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = r;
@@ -212,8 +221,7 @@ __device__ __forceinline__ MaxSumArg row_stats_block(const VocabArgs &a, int i) 
     for (int e = 0; e < 4; ++e)
       if (c0 + 256 * e < a.n_tiles) r = msa_merge(r, v[e]);
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) r = msa_shfl_xor(r, o);
+  r = msa_wave(r);
   __shared__ MaxSumArg red[4];
   __syncthreads();
   if ((tid & 63) == 0) red[tid >> 6] = r;
