@@ -317,7 +317,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 // ----------------------------------------------------------------------------
 // tiled launch (rows > 64), persistent: each workgroup walks output tiles of
 // 256 (N) x 256 (rows).  8 wavefronts as 2 x 4, each 128 (N) x 64 (rows) =
-// 4 x 2 fp16 32x32x16 MFMA blocks.  K steps of 32 (64 B per row) land in a
+// 4 x 2 fp16 32x32x16 MFMA blocks; wave (wn, wt) takes the 32-row blocks wt
+// and wt + 4, so the 64 padding rows of a 192-row tile (448 rows = 256 +
+// 192) are one block of each of four waves on four different SIMDs, which
+// skip its fragment reads and MFMAs (a K loop chosen per tile).  K steps of 32 (64 B per row) land in a
 // 4-stage LDS ring by DMA (weights 256 rows, then activations 256 rows; 16-B
 // chunk c of row R at slot blk_slot(c, R), so that any 16 consecutive rows
 // of one chunk fall in 16 distinct bank groups), three steps ahead of the
@@ -464,6 +467,10 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
       else
         wait_and_barrier<0>();
     }
+    // SK: this wave's second row block (rows wt * 32 + 128 ... + 31 of the
+    // tile) is all padding, so its fragment reads and MFMAs are skipped
+    auto kloop = [&](auto sk_tag) __attribute__((always_inline)) {
+    constexpr bool SK = decltype(sk_tag)::value;
     for (int s = 0; s < nk; ++s) {
       // the lagging group waits for its share of stage s + 1 as well: the
       // leading group reads that stage after the next barrier
@@ -487,7 +494,8 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const int R = wt * 64 + t * 32 + r32;
+          if (SK && t == 1) continue;
+          const int R = wt * 32 + t * 128 + r32;
           bf[j][t] = lds16(base + kTBN * 64 + R * 64 + (blk_slot(q, R) << 4));
           if constexpr (LO) bl[j][t] = lds16(base + (kTBN + kTBT) * 64 + R * 64 + (blk_slot(q, R) << 4));
         }
@@ -506,10 +514,16 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
         for (int v = 0; v < 4; ++v)
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
+            if (SK && t == 1) continue;
             acc[v][t] = mfma32h(af[j][v], bf[j][t], acc[v][t]);
             if constexpr (LO) acc[v][t] = mfma32h(af[j][v], bl[j][t], acc[v][t]);
           }
     }
+    };
+    if (t_tile * kTBT + (wt + 4) * 32 >= g.rows)
+      kloop(std::true_type{});
+    else
+      kloop(std::false_type{});
     if (PP && !lag) asm volatile("s_barrier" ::: "memory");   // the lagging group's first barrier
 
     // epilogue of this tile (vector-memory waits count stores too, so the
@@ -520,7 +534,7 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) nb[v] = n0 + wn * 128 + v * 32;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) tb[t] = t0 + wt * 64 + t * 32;
+    for (int t = 0; t < 2; ++t) tb[t] = t0 + wt * 32 + t * 128;
     GemmArgs go = g;
     go.out = g.out + int64_t(blockIdx.y) * g.split_stride;
     if constexpr (STATS) {
@@ -545,7 +559,7 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const MaxSumArg r = lane_stats<4, 2, false, true>(g, acc, nb, t, lane, &ml[t]);
-        if (kg == 0) red[wn][wt * 64 + t * 32 + r32] = r;
+        if (kg == 0) red[wn][wt * 32 + t * 128 + r32] = r;
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (tid < kTBT && t0 + tid < g.rows) {
@@ -562,7 +576,7 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
         float sc[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const int row = wt * 64 + t * 32 + r32;
+          const int row = wt * 32 + t * 128 + r32;
           const float M = fmaxf(red[0][row].m, red[1][row].m);
           sc[t] = ml[t] == -INFINITY ? 0.f : __expf(ml[t] - M);
         }
@@ -582,7 +596,7 @@ __global__ __launch_bounds__(512) void gemm_tiled_kernel(GemmArgs g) {
         asm volatile("" : "+v"(xs));
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          uint8_t *rowp = smem + (wt * 64 + t * 32 + r32) * 512 + kg * 8;
+          uint8_t *rowp = smem + (wt * 32 + t * 128 + r32) * 512 + kg * 8;
 #pragma unroll
           for (int v = 0; v < 4; ++v)
 #pragma unroll
