@@ -681,6 +681,11 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
   // overlaps (8 rows: 164 -> 332 us)
   constexpr bool PP = !SPARSE;
   const bool lag = PP && w >= 4;   // the lagging group of the ping-pong loop
+  // the wave's two 32-row blocks: 2 wt and 2 wt + 1 with few rows (SPARSE:
+  // waves whose blocks are all padding idle), else wt and wt + 4, as in the
+  // fp16 tiled kernel (the padding blocks of a 192-row tile then fall to one
+  // wave per SIMD)
+  auto rowblk = [&](int t) { return SPARSE ? 2 * wt + t : wt + 4 * t; };
   const int n_ttiles = (g.rows + kTBT - 1) / kTBT;
   const int n_ntiles = (g.N + kTBN - 1) / kTBN;
   const int n_tiles_all = ((n_ntiles + 7) / 8) * 8 * n_ttiles;
@@ -773,6 +778,11 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
       else
         wait_and_barrier<0>();
     }
+    // SK (full tiles only): this wave's second row block is all padding, so
+    // its fragment reads and MFMAs are skipped
+    auto kloop = [&](auto sk_tag) {
+    constexpr bool SK = decltype(sk_tag)::value;
+    const bool live1 = SPARSE ? live_t1 : !SK;
     for (int s = 0; s < nk; ++s) {
       const int younger = lag ? max(0, min(kTST - 3, nk - 2 - s)) : min(kTST - 2, nk - 1 - s);
       if (younger >= 2)
@@ -793,7 +803,8 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const int R = wt * 64 + t * 32 + r32, sw = blk_slot(0, R);
+          if (SK && t == 1) continue;
+          const int R = rowblk(t) * 32 + r32, sw = blk_slot(0, R);
           bf[t] = cat8(lds16(base + kTBN * 64 + R * 64 + (((2 * kg) ^ sw) << 4)),
                        lds16(base + kTBN * 64 + R * 64 + (((2 * kg + 1) ^ sw) << 4)));
         }
@@ -804,7 +815,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
       }
       if (!live_t0) continue;
-      if (live_t1) {
+      if (live1) {
 #pragma unroll
         for (int v = 0; v < 4; ++v)
 #pragma unroll
@@ -814,6 +825,13 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
         for (int v = 0; v < 4; ++v) acc[v][0] = mfma32_fp8(af[v], bf[0], acc[v][0]);
       }
     }
+    };
+    if constexpr (SPARSE)
+      kloop(std::false_type{});
+    else if (t_tile * kTBT + (wt + 4) * 32 >= g.rows)
+      kloop(std::true_type{});
+    else
+      kloop(std::false_type{});
 
     if (PP && !lag) asm volatile("s_barrier" ::: "memory");   // the lagging group's first barrier
 
@@ -825,7 +843,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) nb[v] = n0 + wn * 128 + v * 32;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) tb[t] = t0 + wt * 64 + t * 32;
+    for (int t = 0; t < 2; ++t) tb[t] = t0 + rowblk(t) * 32;
     GemmArgs go = g;
     // scales: logit = a_t s_n * (code products); padding rows have scale 1
     {
@@ -871,7 +889,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const MaxSumArg r = lane_stats<4, 2, false, true>(g, acc, nb, t, lane, &ml[t]);
-        if (kg == 0) red[wn][wt * 64 + t * 32 + r32] = r;
+        if (kg == 0) red[wn][rowblk(t) * 32 + r32] = r;
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (tid < kTBT && t0 + tid < g.rows) {
@@ -888,7 +906,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
         float sc[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const int row = wt * 64 + t * 32 + r32;
+          const int row = rowblk(t) * 32 + r32;
           const float M = fmaxf(red[0][row].m, red[1][row].m);
           sc[t] = ml[t] == -INFINITY ? 0.f : __expf(ml[t] - M);
         }
@@ -908,7 +926,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
         asm volatile("" : "+v"(xs));
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          uint8_t *rowp = smem + (wt * 64 + t * 32 + r32) * 512 + kg * 8;
+          uint8_t *rowp = smem + (rowblk(t) * 32 + r32) * 512 + kg * 8;
 #pragma unroll
           for (int v = 0; v < 4; ++v)
 #pragma unroll
