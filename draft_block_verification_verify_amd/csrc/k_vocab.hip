@@ -542,25 +542,37 @@ __device__ __forceinline__ void accept_tree(const VocabArgs &a, int r) {
   if (lane < T) {
     const int i = s0 + lane;
     const int p = a.row_parent[i];
+    const int d = a.row_draft[i];
+    const int am = a.argmax[i], di = a.draft_ids[i];
     float o = 1.f;
     if (p >= 0) {
-      // the chunk sums in chunk order; loads issued eight at a time ahead of
-      // the adds (a runtime-bounded loop of loads would wait on each one)
-      const float *op = a.opart + int64_t(a.row_draft[i]) * a.n_och;
+      // the chunk sums in chunk order; loads issued ahead of the adds (a
+      // runtime-bounded loop of loads would wait on each one): all at once
+      // for up to 32 chunks (vocabularies up to 262144), else eight at a time
+      const float *op = a.opart + int64_t(d) * a.n_och;
       o = 0.f;
-      for (int c0 = 0; c0 < a.n_och; c0 += 8) {
-        float x[8];
+      if (a.n_och <= 32) {
+        float x[32];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = c0 + e < a.n_och ? op[c0 + e] : 0.f;
+        for (int e = 0; e < 32; ++e) x[e] = e < a.n_och ? op[e] : 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (c0 + e < a.n_och) o += x[e];
+        for (int e = 0; e < 32; ++e)
+          if (e < a.n_och) o += x[e];
+      } else {
+        for (int c0 = 0; c0 < a.n_och; c0 += 8) {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = c0 + e < a.n_och ? op[c0 + e] : 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (c0 + e < a.n_och) o += x[e];
+        }
       }
     }
     ov[lane] = o;
     par[lane] = p < 0 ? -1 : p - s0;
-    arg[lane] = a.argmax[i];
-    did[lane] = a.draft_ids[i];
+    arg[lane] = am;
+    did[lane] = di;
     a.overlap[i] = o;
   }
   __syncthreads();
