@@ -44,6 +44,9 @@ FP8_MINIS = {
     # 96 rows, a vocabulary that is not a multiple of 8: fp32 logits for the
     # overlap pass even without a caller buffer
     "c5v": MINIS["c5v"],
+    # 144 rows: the dense kernel with a partly real row block and padding
+    # blocks skipped
+    "c5r": MINIS["c5r"],
 }
 
 

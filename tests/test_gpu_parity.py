@@ -63,6 +63,9 @@ MINIS = {
     # 96 rows with a vocabulary that is not a multiple of 8 (the tiled LM
     # head's ragged last tile; fp32 logits for the overlap pass)
     "c5v": mini(5, hidden=384, vocab=3001, n_seqs=12, min_len=0, max_len=100, w_lm_std=0.06),
+    # 144 rows: one row tile whose 32-row block 4 is partly real (rows 128-143)
+    # and whose blocks 5-7 are padding (the waves holding them skip them)
+    "c5r": mini(5, hidden=384, vocab=3000, n_seqs=18, min_len=0, max_len=120, w_lm_std=0.06),
 }
 
 
@@ -112,7 +115,7 @@ def test_parity_small(name, seed):
     _record(f"{name}/seed{seed}", rep)
 
 
-@pytest.mark.parametrize("name", ["c4m", "c5m", "c5t", "c5v", "c2m"])
+@pytest.mark.parametrize("name", ["c4m", "c5m", "c5t", "c5v", "c5r", "c2m"])
 @pytest.mark.parametrize("seed", [0, 1])
 def test_parity_without_logits_buffer(name, seed):
     # No caller logits buffer: above 64 rows the LM head then keeps fp16
