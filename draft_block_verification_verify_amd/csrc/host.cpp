@@ -882,9 +882,10 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
     aa.scale_log2 = float(1.4426950408889634 / std::sqrt(double(D)));
     // Partial o records with the non-temporal hint when the K/V tiles streamed
     // exceed the 256 MB last-level cache: the record stores then leave the
-    // KV stream alone (C5 shape: attention 230 -> 222 us, merge 21 -> 26 us,
-    // which reads them from HBM instead).  With less KV the merge's cached
-    // reads win (the 17-row, 8192-prefix chain: attention -1, merge +4 us).
+    // KV stream alone (32 chains over 1.28 GB of K/V tiles: attention
+    // 230 -> 222 us, merge 21 -> 26 us, which reads them from HBM instead).
+    // With less KV the merge's cached reads win (the 17-row, 8192-prefix
+    // chain: attention -1, merge +4 us).
     int64_t kv_tile_bytes = 0;
     for (const auto &it : plan.items) kv_tile_bytes += int64_t(it.k1 - it.k0) * D * 4;
     aa.nt_part = kv_tile_bytes > (int64_t(256) << 20) ? 1 : 0;

@@ -110,7 +110,7 @@ __device__ __forceinline__ void drafter_partial_wave(const VocabArgs &a, int c, 
   if ((a.V % 8) == 0 && a.dchunk == kDrafterChunk && a.drafter_bf16) {
     // the lane's four groups of 8 bf16 values, all loaded before use (one
     // pass over HBM) and kept packed, 4 registers per group, until each pass
-    // widens them (widened on load, the C5 pass of 224 rows x 248320 took
+    // widens them (widened on load, the pass over 224 rows x 248320 took
     // 33 -> 29 us); values past the vocabulary read as -inf
     constexpr int NG = kDrafterChunk / 512;
     uint32_t raw[NG][4];

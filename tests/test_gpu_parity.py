@@ -583,8 +583,9 @@ def _full_case(cfg_id, seed):
 @pytest.mark.parametrize("cfg_id,seed,with_logits", [
     (2, 0, True), (2, 1, True), (2, 2, True),
     (3, 0, True), (3, 1, True), (3, 2, True),
-    # C4 / C5 in the benchmark's launch configuration (no logits buffer: fp16
-    # tile probabilities), and once with fp32 logits compared element-wise
+    # the tree and 32-chain workloads in the benchmark's launch configuration
+    # (no logits buffer: fp16 tile probabilities), and once with fp32 logits
+    # compared element-wise
     (4, 0, False), (4, 0, True), (4, 1, False), (4, 2, False),
     (5, 0, False), (5, 0, True), (5, 1, False), (5, 2, False),
 ])
