@@ -64,7 +64,7 @@ struct sv_handle {
   void *q_rot = nullptr, *k_rot = nullptr, *o_act = nullptr, *hn = nullptr;
   float *part_o = nullptr, *part_ml = nullptr, *h_part = nullptr, *logits = nullptr;
   float *t_max = nullptr, *t_sum = nullptr, *lse_q = nullptr, *opart = nullptr;
-  uint16_t *p16 = nullptr;         // tiled LM head: fp16 tile-relative probabilities
+  uint16_t *p16 = nullptr;         // LM head: fp16 tile-relative probabilities
   int32_t *t_arg = nullptr;
   float2 *dpart = nullptr;
   int64_t slot_cap = 0;
@@ -505,7 +505,7 @@ sv_status create_impl(const sv_config *cfg, const void *w_o, const void *w_lm, c
   // plane, one blocked capacity further in both cases
   A(&h->hn, std::max<size_t>(size_t(R * H * 4), size_t((sv::blocked_elems(R, H) + R * H) * 2)));
   A(&h->logits, size_t(R * V * 4));
-  if (dm.dtype == SV_BF16 && R > 64 && V % 8 == 0) A(&h->p16, size_t(R * V * 2));
+  if (dm.dtype == SV_BF16 && V % 8 == 0) A(&h->p16, size_t(R * V * 2));
   A(&h->t_max, size_t(R * h->n_tiles_cap * 4));
   A(&h->t_sum, size_t(R * h->n_tiles_cap * 4));
   A(&h->t_arg, size_t(R * h->n_tiles_cap * 4));
@@ -814,11 +814,14 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   const int tile_w = bf16 && !fp8 ? sv::lm_tile_width(n, int(V), h->n_cu) : 256;
   const int n_tiles = int(ceil_div(V, tile_w));
 
-  // Without a caller logits buffer, the tiled LM head stores each tile's
+  // Without a caller logits buffer, the LM head stores each tile's
   // probabilities relative to the tile maximum in fp16 instead of fp32
   // logits: half the bytes for their readers (the overlap pass, and in T = 1
-  // mode the accept tests and the bonus draw).
-  const bool use_p16 = bf16 && n > 64 && !out->logits && h->p16 != nullptr;
+  // mode the accept tests and the bonus draw), and half the bytes written
+  // while the weights stream in.  The tiled launches (above 64 rows, fp16 or
+  // FP8) and the small-batch fp16 launch with 256-token tiles do this.
+  const bool use_p16 =
+      bf16 && !out->logits && h->p16 != nullptr && (n > 64 || (!fp8 && tile_w == 256));
   sv::VocabArgs va = vocab_args(plan, m, lay, int(V), bf16, in, out,
                                 VocabBufs{logits, use_p16 ? h->p16 : nullptr, h->t_max, h->t_sum, h->t_arg,
                                           n_tiles, h->dpart, h->n_dch, h->lse_q, h->opart, h->n_och});

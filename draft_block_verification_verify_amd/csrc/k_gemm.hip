@@ -291,14 +291,17 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
   for (int t = 0; t < TB; ++t) tb[t] = t * 32;
   GemmArgs go = g;
   go.out = g.out + int64_t(blockIdx.y) * g.split_stride;
-  store_tile<WV, TB>(go, acc, nb, tb, lane);
+  if (!STATS || !g.p16) store_tile<WV, TB>(go, acc, nb, tb, lane);
 
   if constexpr (STATS) {
     __syncthreads();
     MaxSumArg *red = reinterpret_cast<MaxSumArg *>(smem);   // [4][TB * 32]
+    // the statistics leave exp(x - m) in the accumulators, m the lane's
+    // maximum (the fp16 probabilities below rescale them)
+    float ml[TB];
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
-      const MaxSumArg r = lane_stats<WV, TB>(g, acc, nb, t, lane);
+      const MaxSumArg r = lane_stats<WV, TB, true, true>(g, acc, nb, t, lane, &ml[t]);
       if (kg == 0) red[w * TB * 32 + t * 32 + r32] = r;
     }
     __syncthreads();
@@ -310,6 +313,52 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
       g.t_max[o] = r.m;
       g.t_sum[o] = r.s;
       g.t_arg[o] = r.i;
+    }
+    if constexpr (NR == 256) {
+      if (g.p16) {
+        // fp16 probabilities relative to the tile maximum M of each token
+        // (the value the records above hold), exp(x - m) exp(m - M), in
+        // place of fp32 logits when no logits are asked for: half the bytes
+        // written while the weights stream in (17 rows over 248320 x 5120
+        // weights: writing half of the fp32 logits saved 23 us of 433).
+        // Staged through the ring after the records (chunk cc of token row
+        // rl at slot cc ^ (rl & 31)), then stored as one 512-byte run per
+        // row; g.N % 8 == 0 here.
+        static_assert(4096 + TB * 32 * NR * 2 <= kSkST * SST, "the fp16 tile fits the ring");
+        uint8_t *stg = smem + 4096;
+        float sc[TB];
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+          const int rl = t * 32 + r32;
+          float M = red[rl].m;
+#pragma unroll
+          for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, red[ww * TB * 32 + rl].m);
+          sc[t] = ml[t] == -INFINITY ? 0.f : __expf(ml[t] - M);
+        }
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+          const int rl = t * 32 + r32;
+#pragma unroll
+          for (int v = 0; v < WV; ++v)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int cc = (w * WV + v) * 4 + q;
+              uint32_t hh[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) hh[e] = f2h(acc[v][t][4 * q + e] * sc[t]);
+              *reinterpret_cast<uint2 *>(stg + rl * 512 + ((cc ^ (rl & 31)) << 4) + kg * 8) =
+                  make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
+            }
+        }
+        __syncthreads();
+        const int live = min(TB * 32, g.rows);
+        for (int i = tid; i < live * 32; i += 256) {
+          const int rl = i >> 5, c = i & 31, col = n0 + c * 8;
+          if (col < g.N)
+            *reinterpret_cast<uint4 *>(g.p16 + int64_t(rl) * g.ldo + col) =
+                *reinterpret_cast<const uint4 *>(stg + rl * 512 + ((c ^ (rl & 31)) << 4));
+        }
+      }
     }
   }
 }
