@@ -147,6 +147,7 @@ struct VocabBufs {
 sv::VocabArgs vocab_args(const sv::Plan &plan, const char *m, const sv::MetaLayout &lay, int V, bool bf16,
                          const sv_inputs *in, const sv_outputs *out, const VocabBufs &b) {
   sv::VocabArgs va{};
+  va.tile_shift = 8;
   va.n = plan.n;
   va.n_draft = plan.n_draft;
   va.R = plan.R;
@@ -819,12 +820,12 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   // logits: half the bytes for their readers (the overlap pass, and in T = 1
   // mode the accept tests and the bonus draw), and half the bytes written
   // while the weights stream in.  The tiled launches (above 64 rows, fp16 or
-  // FP8) and the small-batch fp16 launch with 256-token tiles do this.
-  const bool use_p16 =
-      bf16 && !out->logits && h->p16 != nullptr && (n > 64 || (!fp8 && tile_w == 256));
+  // FP8) and the small-batch fp16 launches do this.
+  const bool use_p16 = bf16 && !out->logits && h->p16 != nullptr && (n > 64 || !fp8);
   sv::VocabArgs va = vocab_args(plan, m, lay, int(V), bf16, in, out,
                                 VocabBufs{logits, use_p16 ? h->p16 : nullptr, h->t_max, h->t_sum, h->t_arg,
                                           n_tiles, h->dpart, h->n_dch, h->lse_q, h->opart, h->n_och});
+  va.tile_shift = tile_w == 128 ? 7 : 8;
 
   int k_split = 0;
   const int splits = bf16 ? sv::gemm_splits(n, int(H), int(Hq * D), h->n_cu, &k_split) : 1;

@@ -314,16 +314,16 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
       g.t_sum[o] = r.s;
       g.t_arg[o] = r.i;
     }
-    if constexpr (NR == 256) {
-      if (g.p16) {
+    if (g.p16) {
         // fp16 probabilities relative to the tile maximum M of each token
         // (the value the records above hold), exp(x - m) exp(m - M), in
         // place of fp32 logits when no logits are asked for: half the bytes
         // written while the weights stream in (17 rows over 248320 x 5120
         // weights: writing half of the fp32 logits saved 23 us of 433).
         // Staged through the ring after the records (chunk cc of token row
-        // rl at slot cc ^ (rl & 31)), then stored as one 512-byte run per
-        // row; g.N % 8 == 0 here.
+        // rl at slot cc ^ (rl & (CPR - 1))), then stored as one run of NR
+        // values per row; g.N % 8 == 0 here.
+        constexpr int CPR = NR / 8;   // 16-byte chunks per row
         static_assert(4096 + TB * 32 * NR * 2 <= kSkST * SST, "the fp16 tile fits the ring");
         uint8_t *stg = smem + 4096;
         float sc[TB];
@@ -346,19 +346,18 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
               uint32_t hh[4];
 #pragma unroll
               for (int e = 0; e < 4; ++e) hh[e] = f2h(acc[v][t][4 * q + e] * sc[t]);
-              *reinterpret_cast<uint2 *>(stg + rl * 512 + ((cc ^ (rl & 31)) << 4) + kg * 8) =
+              *reinterpret_cast<uint2 *>(stg + rl * (NR * 2) + ((cc ^ (rl & (CPR - 1))) << 4) + kg * 8) =
                   make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
             }
         }
         __syncthreads();
         const int live = min(TB * 32, g.rows);
-        for (int i = tid; i < live * 32; i += 256) {
-          const int rl = i >> 5, c = i & 31, col = n0 + c * 8;
+        for (int i = tid; i < live * CPR; i += 256) {
+          const int rl = i / CPR, c = i % CPR, col = n0 + c * 8;
           if (col < g.N)
             *reinterpret_cast<uint4 *>(g.p16 + int64_t(rl) * g.ldo + col) =
-                *reinterpret_cast<const uint4 *>(stg + rl * 512 + ((c ^ (rl & 31)) << 4));
+                *reinterpret_cast<const uint4 *>(stg + rl * (NR * 2) + ((c ^ (rl & (CPR - 1))) << 4));
         }
-      }
     }
   }
 }

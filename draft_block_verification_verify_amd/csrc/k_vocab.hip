@@ -256,11 +256,11 @@ __device__ __forceinline__ MaxSum drafter_stats_block(const VocabArgs &a, int t)
 constexpr int kRefineMax = 64;
 constexpr float kRefineLogTau = -4.1588830833596715f;   // log(1/64)
 
-// first-pass logit of token u of row `row` (tiles of 256 tokens)
+// first-pass logit of token u of row `row`
 __device__ __forceinline__ float tile_logit(const VocabArgs &a, int row, int u) {
   if (a.p16) {
     const float p = h2f(a.p16[int64_t(row) * a.V + u]);
-    return p > 0.f ? a.t_max[int64_t(row) * a.n_tiles + (u >> 8)] + logf(p) : -INFINITY;
+    return p > 0.f ? a.t_max[int64_t(row) * a.n_tiles + (u >> a.tile_shift)] + logf(p) : -INFINITY;
   }
   return a.logits[int64_t(row) * a.V + u];
 }
@@ -440,8 +440,8 @@ __device__ __forceinline__ void overlap_block(const VocabArgs &a, int c, int t, 
   const int lo = c * a.ochunk, hi = min(a.V, lo + a.ochunk);
   float s = 0.f;
   if (a.p16) {
-    // p_j(u) = p16(u) * exp(t_max - lse) within each 256-token tile of the
-    // LM head (the host takes this path only when V % 8 == 0)
+    // p_j(u) = p16(u) * exp(t_max - lse) within each tile of the LM head
+    // (2^tile_shift tokens; the host takes this path only when V % 8 == 0)
     const uint16_t *pp = a.p16 + int64_t(j) * a.V;
     const float *tm = a.t_max + int64_t(j) * a.n_tiles;
     constexpr int NG = kOverlapChunk / 2048;   // groups of 8 per thread in a full chunk
@@ -456,7 +456,7 @@ __device__ __forceinline__ void overlap_block(const VocabArgs &a, int c, int t, 
         const bool in = u < hi;
         hq[g] = in ? ld16s(pp + u) : make_uint4(0, 0, 0, 0);
         hb[g] = in ? ld16s(static_cast<const uint16_t *>(a.drafter) + qrow + u) : make_uint4(0, 0, 0, 0);
-        sc[g] = in ? tm[u >> 8] : -INFINITY;
+        sc[g] = in ? tm[u >> a.tile_shift] : -INFINITY;
       }
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
@@ -476,7 +476,7 @@ __device__ __forceinline__ void overlap_block(const VocabArgs &a, int c, int t, 
       float b[8];
       load8(a.drafter, a.drafter_bf16, qrow + u, b);
       const uint4 h = *reinterpret_cast<const uint4 *>(pp + u);
-      const float sc = __expf(tm[u >> 8] - A);
+      const float sc = __expf(tm[u >> a.tile_shift] - A);
       const uint32_t w[4] = {h.x, h.y, h.z, h.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -731,11 +731,12 @@ __device__ __forceinline__ float drafter_at(const VocabArgs &a, int draft, int u
   return load1(a.drafter, a.drafter_bf16, int64_t(draft) * a.V + u);
 }
 
-// target probability p_row(u): from the fp32 logits, or from the tiled LM
-// head's fp16 probabilities relative to their 256-token tile's maximum
+// target probability p_row(u): from the fp32 logits, or from the LM head's
+// fp16 probabilities relative to their tile's maximum
 __device__ __forceinline__ float p_at(const VocabArgs &a, int row, int u) {
   if (a.p16)
-    return h2f(a.p16[int64_t(row) * a.V + u]) * __expf(a.t_max[int64_t(row) * a.n_tiles + (u >> 8)] - a.row_lse[row]);
+    return h2f(a.p16[int64_t(row) * a.V + u]) *
+           __expf(a.t_max[int64_t(row) * a.n_tiles + (u >> a.tile_shift)] - a.row_lse[row]);
   return __expf(a.logits[int64_t(row) * a.V + u] - a.row_lse[row]);
 }
 
@@ -794,7 +795,7 @@ __device__ __forceinline__ void chunk_weights(const VocabArgs &a, const BonusRow
                                               float (&w)[kSampPer]) {
   float pr[kSampPer];   // p of the stop row
   if (b.pp) {
-    // token u = base + thread + 256 j lies in 256-token tile base / 256 + j
+    // token u = base + thread + 256 j lies in tile u >> tile_shift
     uint16_t h[kSampPer];
 #pragma unroll
     for (int j = 0; j < kSampPer; ++j) {
@@ -803,7 +804,7 @@ __device__ __forceinline__ void chunk_weights(const VocabArgs &a, const BonusRow
     }
 #pragma unroll
     for (int j = 0; j < kSampPer; ++j) {
-      const int tile = min((base >> 8) + j, a.n_tiles - 1);
+      const int tile = min((base + int(threadIdx.x) + 256 * j) >> a.tile_shift, a.n_tiles - 1);
       pr[j] = h2f(h[j]) * __expf(b.tm[tile] - b.lse_p);
     }
   } else {

@@ -169,11 +169,12 @@ struct VocabArgs {
   const void *drafter;          // [n_draft, V] bf16 or f32
   int drafter_bf16;
   float *logits;                // [n, V] fp32 (the refinement rewrites some entries)
-  // [n, V] fp16 exp(l - t_max) per 256-token tile (null: read `logits`)
+  // [n, V] fp16 exp(l - t_max) per LM-head tile (null: read `logits`)
   uint16_t *p16;
   const float *t_max, *t_sum;
   const int32_t *t_arg;
   int n_tiles;
+  int tile_shift;               // log2 of the LM head's tile width (8, or 7 for 128-token tiles)
   float2 *dpart;                // [n_draft, n_dch]
   int n_dch, dchunk;
   float *lse_q;                 // [n_draft]

@@ -69,6 +69,9 @@ MINIS = {
     # 17 rows over 240 vocabulary tiles: the small-batch launch with
     # 256-token tiles (fp16 probabilities when no logits buffer is given)
     "c3w": mini(3, hidden=384, vocab=61440, prefix=777, w_lm_std=0.05),
+    # 8 rows, 128-token tiles, a vocabulary that is a multiple of 8 (fp16
+    # probabilities per 128-token tile without a logits buffer)
+    "c2n": mini(2, hidden=512, vocab=3000, prefix=301, w_lm_std=0.06),
 }
 
 
@@ -118,7 +121,7 @@ def test_parity_small(name, seed):
     _record(f"{name}/seed{seed}", rep)
 
 
-@pytest.mark.parametrize("name", ["c4m", "c5m", "c5t", "c5v", "c5r", "c2m", "c5s", "c3w"])
+@pytest.mark.parametrize("name", ["c4m", "c5m", "c5t", "c5v", "c5r", "c2m", "c5s", "c3w", "c2n"])
 @pytest.mark.parametrize("seed", [0, 1])
 def test_parity_without_logits_buffer(name, seed):
     # No caller logits buffer: above 64 rows the LM head then keeps fp16
@@ -507,7 +510,7 @@ def test_parity_sample_mode(name, sigma):
 
 
 @pytest.mark.parametrize("name,sigma", [("c5m", 0.5), ("c4m", 0.3), ("c5t", 0.4), ("c5m", None), ("c5s", 0.5),
-                                        ("c3w", 0.4)])
+                                        ("c3w", 0.4), ("c2n", None)])
 def test_parity_sample_mode_without_logits_buffer(name, sigma):
     # above 64 rows without a caller logits buffer the accept tests and the
     # bonus draw read the LM head's fp16 tile-relative probabilities
@@ -585,7 +588,7 @@ def _full_case(cfg_id, seed):
 
 @pytest.mark.slow
 @pytest.mark.parametrize("cfg_id,seed,with_logits", [
-    (2, 0, True), (2, 1, True), (2, 2, True),
+    (2, 0, True), (2, 1, True), (2, 2, True), (2, 0, False),
     (3, 0, True), (3, 1, True), (3, 2, True), (3, 0, False),
     # the tree and 32-chain workloads in the benchmark's launch configuration
     # (no logits buffer: fp16 tile probabilities), and once with fp32 logits
