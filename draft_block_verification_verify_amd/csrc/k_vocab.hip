@@ -656,6 +656,58 @@ __device__ __forceinline__ void overlap_chunk_sum(const VocabArgs &a, int c, int
   if (tid == 0) a.opart[int64_t(t) * a.n_och + c] = s;
 }
 
+// The same for fp16 tile-relative probabilities (the p16 path of
+// overlap_block with a full chunk, the same order of adds): the
+// probabilities, the drafter logits and each group's tile maximum are loaded
+// before the row and drafter statistics are merged.
+struct OverlapChunkP16 {
+  static constexpr int NG = kOverlapChunk / 2048;   // groups of 8 per thread
+  uint4 p[NG], q[NG];                               // fp16 probabilities, bf16 drafter logits
+  float tm[NG];                                     // the maximum of each group's tile
+};
+
+__device__ __forceinline__ bool overlap_chunk_p16_fast(const VocabArgs &a) {
+  return a.p16 && (a.V % 8) == 0 && a.ochunk == kOverlapChunk && a.drafter_bf16;
+}
+
+__device__ __forceinline__ void overlap_chunk_p16_load(const VocabArgs &a, int c, int t, int j, OverlapChunkP16 &k) {
+  const int tid = threadIdx.x;
+  const uint16_t *pp = a.p16 + int64_t(j) * a.V;
+  const float *tm = a.t_max + int64_t(j) * a.n_tiles;
+  const int64_t qrow = int64_t(t) * a.V;
+  const int lo = c * a.ochunk, hi = min(a.V, lo + a.ochunk);
+#pragma unroll
+  for (int g = 0; g < OverlapChunkP16::NG; ++g) {
+    const int u = lo + tid * 8 + g * 2048;
+    const bool in = u < hi;
+    k.p[g] = in ? ld16s(pp + u) : make_uint4(0, 0, 0, 0);
+    k.q[g] = in ? ld16s(static_cast<const uint16_t *>(a.drafter) + qrow + u) : make_uint4(0, 0, 0, 0);
+    k.tm[g] = in ? tm[u >> a.tile_shift] : -INFINITY;
+  }
+}
+
+__device__ __forceinline__ void overlap_chunk_p16_sum(const VocabArgs &a, int c, int t, const OverlapChunkP16 &k,
+                                                      float A, float B) {
+  const int tid = threadIdx.x;
+  const int lo = c * a.ochunk, hi = min(a.V, lo + a.ochunk);
+  float s = 0.f;
+#pragma unroll
+  for (int g = 0; g < OverlapChunkP16::NG; ++g) {
+    if (lo + tid * 8 + g * 2048 >= hi) continue;
+    const float scale = __expf(k.tm[g] - A);
+    const uint32_t w[4] = {k.p[g].x, k.p[g].y, k.p[g].z, k.p[g].w};
+    const uint32_t d[4] = {k.q[g].x, k.q[g].y, k.q[g].z, k.q[g].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = h2f(uint16_t((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu))) * scale;
+      const float b = __uint_as_float((e & 1) ? (d[e >> 1] & 0xFFFF0000u) : (d[e >> 1] << 16));
+      s += fminf(p, __expf(b - B));
+    }
+  }
+  s = sum_block256(s);
+  if (tid == 0) a.opart[int64_t(t) * a.n_och + c] = s;
+}
+
 // Small batches: the row statistics and the overlap sums in one launch.
 // Workgroups [0, n) combine row b; the rest take overlap chunks, each
 // merging its parent's and its drafter row's records itself with the same
@@ -688,6 +740,12 @@ __global__ __launch_bounds__(256) void combine_overlap_kernel(VocabArgs a) {
       const MaxSumArg r = row_stats_block(a, j);
       const MaxSum q = drafter_stats_block(a, t);
       overlap_chunk_sum(a, c, t, k, r.m + logf(r.s), q.m + logf(q.s));
+    } else if (overlap_chunk_p16_fast(a)) {
+      OverlapChunkP16 k;
+      overlap_chunk_p16_load(a, c, t, j, k);
+      const MaxSumArg r = row_stats_block(a, j);
+      const MaxSum q = drafter_stats_block(a, t);
+      overlap_chunk_p16_sum(a, c, t, k, r.m + logf(r.s), q.m + logf(q.s));
     } else {
       const MaxSumArg r = row_stats_block(a, j);
       const MaxSum q = drafter_stats_block(a, t);
