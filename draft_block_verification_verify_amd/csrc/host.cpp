@@ -819,9 +819,8 @@ sv_status spec_verify_run(sv_handle *h, const sv_inputs *in, const sv_outputs *o
   // probabilities relative to the tile maximum in fp16 instead of fp32
   // logits: half the bytes for their readers (the overlap pass, and in T = 1
   // mode the accept tests and the bonus draw), and half the bytes written
-  // while the weights stream in.  The tiled launches (above 64 rows, fp16 or
-  // FP8) and the small-batch fp16 launches do this.
-  const bool use_p16 = bf16 && !out->logits && h->p16 != nullptr && (n > 64 || !fp8);
+  // while the weights stream in (every LM head launch, fp16 or FP8).
+  const bool use_p16 = bf16 && !out->logits && h->p16 != nullptr;
   sv::VocabArgs va = vocab_args(plan, m, lay, int(V), bf16, in, out,
                                 VocabBufs{logits, use_p16 ? h->p16 : nullptr, h->t_max, h->t_sum, h->t_arg,
                                           n_tiles, h->dpart, h->n_dch, h->lse_q, h->opart, h->n_och});

@@ -974,6 +974,8 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
         asm volatile("" : "+v"(xs));
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
+          // (few rows: 32-row blocks past the batch are neither staged nor stored)
+          if (SPARSE && rowblk(t) * 32 >= live_rows) continue;
           uint8_t *rowp = smem + (rowblk(t) * 32 + r32) * 512 + kg * 8;
 #pragma unroll
           for (int v = 0; v < 4; ++v)
@@ -987,8 +989,9 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(GemmArgs g) {
             }
         }
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const int nst = SPARSE ? min(kTBT, live_rows) * 32 : kTBT * 32;
 #pragma unroll 4
-        for (int i = tid; i < kTBT * 32; i += 512) {
+        for (int i = tid; i < nst; i += 512) {
           const int rl = i >> 5, c = i & 31;
           const int tok = t0 + rl, col = n0 + c * 8;
           if (tok < g.rows && col < g.N)

@@ -189,7 +189,7 @@ def test_parity_fp8(name, seed):
     _check_fp8(inp, cd, ref, gpu, rows, f"{name}/fp8/seed{seed}", 0.9)
 
 
-@pytest.mark.parametrize("name", ["c5m", "c4m8", "c5h", "c5v"])
+@pytest.mark.parametrize("name", ["c5m", "c4m8", "c5h", "c5v", "c5s", "c3m"])
 def test_parity_fp8_without_logits_buffer(name):
     # No caller logits buffer: above 64 rows the FP8 LM head then keeps fp16
     # tile-relative probabilities for the overlap pass instead of fp32 logits
